@@ -1,0 +1,54 @@
+"""Haar-random orthogonal rotation, float64 (oracle; test infrastructure only).
+
+KV Cache API page (ginkgoq.github.io/TurboQuant/api/kv), TurboQuantCompressorV2.__init__
+(also TurboQuantCompressorMSE.__init__, MSECompressor.__init__): a seeded CPU generator
+draws a d x d standard-normal matrix G; G is QR-factored; the rotation is Q with each
+column j multiplied by the sign of R[j, j], a zero sign counting as +1.
+
+Reading: the page factors in float32, which is orthogonal only to ~1e-6. The oracle
+keeps the page's float32 draw (the input) and factors it in float64, so the result is
+orthogonal to ~1e-15 and is the unique QR factor whose R has a positive diagonal.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def householder_qr(g):
+    """Plain Householder QR of a square matrix in float64: returns (Q, R) with G = Q R."""
+    r = np.array(g, dtype=np.float64, copy=True)
+    d = r.shape[0]
+    if r.shape != (d, d):
+        raise ValueError("householder_qr expects a square matrix")
+    q = np.eye(d)
+    for k in range(d - 1):
+        col = r[k:, k]
+        norm = np.sqrt(np.dot(col, col))
+        if norm == 0.0:
+            continue
+        alpha = -norm if col[0] >= 0 else norm
+        v = col.copy()
+        v[0] -= alpha
+        vn = np.sqrt(np.dot(v, v))
+        if vn == 0.0:
+            continue
+        v /= vn
+        # reflect the trailing rows of R and accumulate Q = H_0 H_1 ... H_k
+        r[k:, :] -= 2.0 * np.outer(v, v @ r[k:, :])
+        q[:, k:] -= 2.0 * np.outer(q[:, k:] @ v, v)
+    return q, r
+
+
+def haar_rotation(gaussian):
+    """Rotation Pi from a Gaussian draw: Q * sign(diag R) column-wise (sign 0 -> +1)."""
+    q, r = householder_qr(gaussian)
+    s = np.sign(np.diag(r))
+    s[s == 0] = 1.0
+    return q * s[None, :]
+
+
+def haar_rotations(gaussians):
+    """Stack version: [n, d, d] draws -> [n, d, d] rotations."""
+    g = np.asarray(gaussians, dtype=np.float64)
+    return np.stack([haar_rotation(gi) for gi in g])
