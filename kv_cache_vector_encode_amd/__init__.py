@@ -1,0 +1,261 @@
+"""TurboQuant KV-cache codec for AMD MI355X (gfx950): thin Python binding of libtq.
+
+Every computation runs in libtq (C ABI, include/tq.h): the host float64 codebook solver and
+QR, and the HIP kernels for encode, decode, compressed scores and fused decode attention.
+This module only marshals arguments: torch supplies device memory and the current stream.
+There is no CPU fallback; if libtq.so is missing the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import math
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import AttnParams, TQError, TQ_BF16, TQ_F16, TQ_F32, check, lib
+
+__all__ = ["Codebook", "Rotation", "encode", "decode", "scores_compressed", "attn_decode",
+           "attn_workspace_size", "packed_row_bytes", "TQError", "TQ_F32", "TQ_BF16", "TQ_F16",
+           "dtype_code"]
+
+_DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}
+_DT_INV = {v: k for k, v in _DT.items()}
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DT:
+        raise TypeError("unsupported dtype %s; use float32, bfloat16 or float16" % dt)
+    return _DT[dt]
+
+
+def packed_row_bytes(d: int, bits: int) -> int:
+    return (d * bits + 7) // 8
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+class Codebook:
+    """Lloyd-Max codebook for (head_dim d, bits), solved on the host by libtq."""
+
+    def __init__(self, d: int, bits: int):
+        h = lib().tq_codebook_init(int(d), int(bits))
+        if not h:
+            raise TQError(None, _lib.last_error())
+        self._h = C.c_void_p(h)
+        self.d, self.bits = int(d), int(bits)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def get(self):
+        L = 2 ** self.bits
+        c = np.zeros(L)
+        t = np.zeros(L - 1)
+        m = C.c_double()
+        check(lib().tq_codebook_get(self._h, c.ctypes.data_as(C.c_void_p), t.ctypes.data_as(C.c_void_p),
+                                    C.byref(m)))
+        return c, t, m.value
+
+    @property
+    def centroids(self):
+        return self.get()[0]
+
+    @property
+    def thresholds(self):
+        return self.get()[1]
+
+    @property
+    def mse(self):
+        return self.get()[2]
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        try:
+            if h is not None and _lib._LIB is not None:
+                _lib._LIB.tq_codebook_free(h)
+        except Exception:
+            pass
+        self._h = None
+
+
+def rotation_compute(gaussian) -> np.ndarray:
+    """Host-only float64 rotation for one float32 Gaussian draw [d, d] (no device)."""
+    g = np.ascontiguousarray(np.asarray(gaussian, dtype=np.float32))
+    d = g.shape[0]
+    out = np.zeros((d, d))
+    check(lib().tq_rotation_compute(d, g.ctypes.data_as(C.c_void_p), out.ctypes.data_as(C.c_void_p)))
+    return out
+
+
+class Rotation:
+    """A stack of n_rot Haar rotations uploaded to the current HIP device."""
+
+    def __init__(self, handle, d: int, n_rot: int):
+        self._h = C.c_void_p(handle)
+        self.d, self.n_rot = d, n_rot
+
+    @classmethod
+    def from_gaussian(cls, gaussian):
+        """gaussian: float32 [n_rot, d, d] (or [d, d]) standard-normal draws (CPU)."""
+        g = torch.as_tensor(gaussian).detach().to("cpu", torch.float32).contiguous()
+        if g.dim() == 2:
+            g = g[None]
+        n, d, _ = g.shape
+        h = lib().tq_rotation_from_gaussian(d, n, C.c_void_p(g.data_ptr()))
+        if not h:
+            raise TQError(None, _lib.last_error())
+        return cls(h, d, n)
+
+    @classmethod
+    def from_matrix(cls, pi):
+        p = np.ascontiguousarray(np.asarray(pi, dtype=np.float64))
+        if p.ndim == 2:
+            p = p[None]
+        n, d, _ = p.shape
+        h = lib().tq_rotation_from_matrix(d, n, p.ctypes.data_as(C.c_void_p))
+        if not h:
+            raise TQError(None, _lib.last_error())
+        return cls(h, d, n)
+
+    def matrices(self) -> np.ndarray:
+        out = np.zeros((self.n_rot, self.d, self.d))
+        check(lib().tq_rotation_get(self._h, out.ctypes.data_as(C.c_void_p)))
+        return out
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        try:
+            if h is not None and _lib._LIB is not None:
+                _lib._LIB.tq_rotation_free(h)
+        except Exception:
+            pass
+        self._h = None
+
+
+def encode(cb: Codebook, rot: Rotation, x: torch.Tensor, vectors_per_rot: int = 0, packed=None, norms=None,
+           slot_mapping=None, num_slots=None, stream=None):
+    """x: [..., d] on the GPU (float32/bfloat16/float16; rows may be strided).
+    Returns (packed uint8 [rows, d*b/8], norms float32 [rows]); rows = N, or num_slots with a
+    slot_mapping (int64 [N]: destination row of each vector, negative = skip)."""
+    d = x.shape[-1]
+    x2 = x.reshape(-1, d) if x.dim() != 2 else x
+    if x2.stride(-1) != 1:
+        x2 = x2.contiguous()
+    n = x2.shape[0]
+    rows = n if slot_mapping is None else (num_slots if num_slots is not None else n)
+    if packed is None:
+        packed = torch.empty(rows, packed_row_bytes(d, cb.bits), dtype=torch.uint8, device=x.device)
+    if norms is None:
+        norms = torch.empty(rows, dtype=torch.float32, device=x.device)
+    check(lib().tq_encode(cb.handle, rot.handle, int(vectors_per_rot), _ptr(x2), dtype_code(x2.dtype), n,
+                          x2.stride(0), _ptr(packed), _ptr(norms), _ptr(slot_mapping), _stream(stream)))
+    return packed, norms
+
+
+def decode(cb: Codebook, rot: Rotation, packed: torch.Tensor, norms: torch.Tensor, n: int | None = None,
+           out_dtype=torch.bfloat16, vectors_per_rot: int = 0, slot_mapping=None, out=None, stream=None):
+    """Returns out [n, d] (out_dtype): row i decodes packed row slot_mapping[i] (or i)."""
+    d = rot.d
+    if n is None:
+        n = slot_mapping.numel() if slot_mapping is not None else packed.shape[0]
+    if out is None:
+        out = torch.empty(n, d, dtype=out_dtype, device=packed.device)
+    check(lib().tq_decode(cb.handle, rot.handle, int(vectors_per_rot), _ptr(packed), _ptr(norms),
+                          _ptr(slot_mapping), int(n), _ptr(out), dtype_code(out.dtype), _stream(stream)))
+    return out
+
+
+def _params(cb_k, rot_k, q, k_packed, k_norms, cb_v=None, rot_v=None, v_packed=None, v_norms=None,
+            seq_lens=None, max_seq_len=None, block_table=None, block_size=0, batch_per_rot=0, scale=None,
+            out=None, lse=None, num_splits=0, num_kv_heads=None):
+    B, Hq, d = q.shape
+    p = AttnParams()
+    p.cb_k, p.rot_k = cb_k.handle, rot_k.handle
+    p.cb_v = cb_v.handle if cb_v is not None else None
+    p.rot_v = rot_v.handle if rot_v is not None else None
+    p.batch, p.num_q_heads = B, Hq
+    if num_kv_heads is None:
+        num_kv_heads = k_packed.shape[1]
+    p.num_kv_heads = int(num_kv_heads)
+    p.q, p.q_dtype = q.data_ptr(), dtype_code(q.dtype)
+    p.k_packed, p.k_norms = k_packed.data_ptr(), k_norms.data_ptr()
+    p.v_packed = v_packed.data_ptr() if v_packed is not None else None
+    p.v_norms = v_norms.data_ptr() if v_norms is not None else None
+    p.seq_lens = seq_lens.data_ptr() if seq_lens is not None else None
+    if max_seq_len is None:
+        max_seq_len = k_packed.shape[2]
+    p.max_seq_len = int(max_seq_len)
+    p.block_table = block_table.data_ptr() if block_table is not None else None
+    p.block_size = int(block_size)
+    p.max_blocks_per_seq = int(block_table.shape[1]) if block_table is not None else 0
+    p.batch_per_rot = int(batch_per_rot)
+    p.scale = float(1.0 / math.sqrt(d) if scale is None else scale)
+    p.out = out.data_ptr() if out is not None else None
+    p.out_dtype = dtype_code(out.dtype) if out is not None else TQ_F32
+    p.lse = lse.data_ptr() if lse is not None else None
+    p.num_splits = int(num_splits)
+    return p
+
+
+def attn_workspace_size(p: AttnParams) -> int:
+    n = lib().tq_attn_workspace_size(C.byref(p))
+    if n == 0:
+        raise TQError(None, _lib.last_error())
+    return int(n)
+
+
+def _workspace(p: AttnParams, device, workspace=None):
+    need = attn_workspace_size(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    return workspace
+
+
+def scores_compressed(cb_k: Codebook, rot_k: Rotation, q: torch.Tensor, k_packed: torch.Tensor,
+                      k_norms: torch.Tensor, seq_lens=None, max_seq_len=None, block_table=None, block_size=0,
+                      batch_per_rot=0, scale=None, scores=None, num_kv_heads=None, workspace=None, stream=None):
+    """s[b, h, t] = scale * n_t <Pi_K q[b,h], c_K[idx_t]> for t < len_b, from the compressed keys.
+    q: [B, Hq, d]; dense k_packed [B, Hkv, T, row] / k_norms [B, Hkv, T], or paged pools with a
+    block_table [B, max_blocks] (int32) and block_size. Returns float32 [B, Hq, T]."""
+    p = _params(cb_k, rot_k, q, k_packed, k_norms, seq_lens=seq_lens, max_seq_len=max_seq_len,
+                block_table=block_table, block_size=block_size, batch_per_rot=batch_per_rot, scale=scale,
+                num_kv_heads=num_kv_heads)
+    if scores is None:
+        scores = torch.full((q.shape[0], q.shape[1], p.max_seq_len), float("nan"), dtype=torch.float32,
+                            device=q.device)
+    ws = _workspace(p, q.device, workspace)
+    check(lib().tq_scores_compressed(C.byref(p), _ptr(scores), _stream(stream)))
+    scores._tq_workspace = ws
+    return scores
+
+
+def attn_decode(cb_k: Codebook, rot_k: Rotation, cb_v: Codebook, rot_v: Rotation, q: torch.Tensor,
+                k_packed, k_norms, v_packed, v_norms, seq_lens=None, max_seq_len=None, block_table=None,
+                block_size=0, batch_per_rot=0, scale=None, out=None, out_dtype=None, return_lse=False,
+                num_splits=0, num_kv_heads=None, workspace=None, stream=None):
+    """Fused decode attention over the compressed cache; returns out [B, Hq, d] (and lse)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if return_lse else None
+    p = _params(cb_k, rot_k, q, k_packed, k_norms, cb_v, rot_v, v_packed, v_norms, seq_lens, max_seq_len,
+                block_table, block_size, batch_per_rot, scale, out, lse, num_splits, num_kv_heads)
+    ws = _workspace(p, q.device, workspace)
+    check(lib().tq_attn_decode(C.byref(p), _stream(stream)))
+    out._tq_workspace = ws
+    return (out, lse) if return_lse else out

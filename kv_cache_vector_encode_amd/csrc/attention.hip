@@ -1,0 +1,471 @@
+// Scores and fused decode attention straight from the compressed cache.
+//
+// Method: s_t = scale <q, k_hat_t> (KV Cache API page, ginkgoq.github.io/TurboQuant/api/kv,
+// TurboQuantKVCache.attention_scores) and o = softmax(s) v_hat (TurboQuantKVCache.attend).
+// Because k_hat_t = n_t Pi_K^T c_K[idx_t], <q, k_hat_t> = n_t <Pi_K q, c_K[idx_t]>: the query is
+// rotated once and keys are never un-rotated (Turbo Attention PyPI page, "The codec": queries
+// rotated the same way, so scores need no un-rotation). Likewise sum_t p_t v_hat_t =
+// Pi_V^T sum_t p_t n^v_t c_V[idx^v_t]: values are accumulated in the rotated domain and
+// rotated back once per (sequence, head). Split-K over tokens with an online softmax and a
+// log-sum-exp merge plays the role of the pages' split-K paged decode kernel (same page,
+// "Kernels").
+//
+// Work layout. Kernel 1 rotates every query (fp32). Kernel 2: a wave owns one (sequence,
+// KV head, token range) and walks it 32 tokens at a time.
+//   scores: 16x16x32 fp16 MFMA, A = centroids of 16 tokens (lane m+16g holds token m's codes
+//     for coordinates g*d/4 + 8kb .. +8), B = the G <= 16 rotated queries of the group
+//     (normalized by their max |entry| so fp16 cannot overflow), D[token][head].
+//   softmax: per head running max m, running sum l; the value weights p_t n^v_t are kept
+//     relative to the running max V norm N so they lie in [0, 1] for fp16.
+//   P.V: 16x16x32 fp16 MFMA computing acc^T[coord][head]. The 32 tokens of a block are
+//     permuted so that lane (head, g) already holds, from the score step, the weights of the
+//     8 tokens it must supply (4g..4g+3 and 16+4g..16+4g+3): no shuffles. The A operand is
+//     the V centroids of those 8 tokens for coordinate group m (coordinates m*d/16 + t').
+// Kernel 3 merges the splits: M = max m_s, L = sum l_s e^(m_s-M), o = Pi_V^T (sum acc_s
+// e^(m_s-M)) / L, lse = M + log L.
+#include <math.h>
+
+#include "device_common.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+struct AttnKArgs {
+  const float* qrot;
+  const uint8_t* kp;
+  const float* kn;
+  const uint8_t* vp;
+  const float* vn;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  float* scores;
+  float* part;
+  int32_t max_seq_len, block_size, bs_shift, mbps;
+  int32_t B, Hq, Hkv, G, s_eff;
+  float scale;
+  uint32_t ctk[16];   // K centroids as bf16 hi | lo << 16
+  uint32_t ctv[8];    // V centroids as fp16, two per word
+};
+
+constexpr int kAttnWaves = 4;
+
+__device__ __forceinline__ int64_t token_row(const AttnKArgs& a, int b, int kvh, int t) {
+  if (a.block_table) {
+    int blk, off;
+    if (a.bs_shift >= 0) {
+      blk = t >> a.bs_shift;
+      off = t & (a.block_size - 1);
+    } else {
+      blk = t / a.block_size;
+      off = t - blk * a.block_size;
+    }
+    const int phys = a.block_table[(int64_t)b * a.mbps + blk];
+    return ((int64_t)phys * a.Hkv + kvh) * a.block_size + off;
+  }
+  return ((int64_t)b * a.Hkv + kvh) * a.max_seq_len + t;
+}
+
+// NBITS bits starting at bit `off` of a row of ROW_DW dwords, shifted down to bit 0.
+template <int NBITS, int ROW_DW, bool ALIGNED>
+__device__ __forceinline__ void load_bits(const uint32_t* row, int off, uint32_t (&out)[(NBITS + 31) / 32]) {
+  constexpr int NW = (NBITS + 31) / 32;
+  const int idx = off >> 5;
+  if constexpr (ALIGNED) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) out[k] = row[idx + k];
+  } else {
+    const int sh = off & 31;
+    uint32_t w[NW + 1];
+#pragma unroll
+    for (int k = 0; k <= NW; ++k) w[k] = (idx + k < ROW_DW) ? row[idx + k] : 0u;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) out[k] = funnel(w[k + 1], w[k], (uint32_t)sh);
+  }
+}
+
+template <int BITS, int NW>
+__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[NW], int idx) {
+  const int pos = idx * BITS;
+  uint32_t c = w[pos >> 5] >> (pos & 31);
+  if ((pos & 31) + BITS > 32) c |= w[(pos >> 5) + 1] << (32 - (pos & 31));
+  return c & ((1u << BITS) - 1u);
+}
+
+template <int D, int BK, int BV, bool SCORES>
+__global__ void __launch_bounds__(kAttnWaves * 64) attn_kernel(AttnKArgs a) {
+  constexpr int KB = D / 32;            // K blocks of the score MFMA
+  constexpr int TV = D / 16;            // output tiles of the P.V MFMA
+  constexpr int NBK = D * BK / 4;       // bits of a lane's K chunk
+  constexpr int NBV = D * BV / 16;      // bits of a lane's V segment
+  constexpr int NWK = (NBK + 31) / 32, NWV = (NBV + 31) / 32;
+  constexpr int ROWK_DW = D * BK / 32, ROWV_DW = D * BV / 32;
+  constexpr bool ALK = (NBK % 32) == 0, ALV = (NBV % 32) == 0;
+  __shared__ uint32_t ctk[16];
+  __shared__ uint16_t ctv[16];
+  if (threadIdx.x < 16) {
+    ctk[threadIdx.x] = a.ctk[threadIdx.x];
+    ctv[threadIdx.x] = (uint16_t)(a.ctv[threadIdx.x >> 1] >> (16 * (threadIdx.x & 1)));
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int sidx = blockIdx.x * kAttnWaves + wave;
+  const int len = a.seq_lens ? max(0, min(a.seq_lens[b], a.max_seq_len)) : a.max_seq_len;
+  const int nblk = (len + 31) >> 5;
+  const int per = (nblk + a.s_eff - 1) / a.s_eff;
+  const int start = sidx * per * 32;
+  const int end = min(len, start + per * 32);
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const bool head_ok = n16 < a.G;
+  const int h = kvh * a.G + (head_ok ? n16 : 0);
+
+  // ---- rotated query as the score MFMA's B operand: lane (head n16, g = q4) holds
+  //      q'[h][q4*d/4 + 8kb + e] / qmax for kb < KB, e < 8, split into bf16 hi + lo. Scores
+  //      take three bf16 passes (q_hi c_hi + q_hi c_lo + q_lo c_hi, ~2^-17 relative): with
+  //      large logits (outlier tokens) softmax turns score errors into weight errors, so fp16
+  //      (2^-11) operands are not enough there.
+  u32x4 bqh[KB], bql[KB];
+  float qmax;
+  {
+    float qv[D / 4];
+    const float* qp = a.qrot + ((int64_t)b * a.Hq + h) * D + q4 * (D / 4);
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      qv[i] = head_ok ? qp[i] : 0.f;
+      mx = fmaxf(mx, fabsf(qv[i]));
+    }
+    mx = fmaxf(mx, wave_xor(mx, 16));
+    mx = fmaxf(mx, wave_xor(mx, 32));
+    qmax = mx > 0.f ? mx : 1.f;
+    const float inv = 1.0f / qmax;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float v0 = qv[8 * kb + 2 * c] * inv, v1 = qv[8 * kb + 2 * c + 1] * inv;
+        const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
+        const uint32_t l0 = f32_to_bf16_bits(v0 - bf16_bits_to_f32(h0));
+        const uint32_t l1 = f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1));
+        bqh[kb][c] = h0 | (h1 << 16);
+        bql[kb][c] = l0 | (l1 << 16);
+      }
+  }
+  const float sc = qmax * a.scale;
+
+  float m_run = -INFINITY, l_run = 0.f, n_run = 0.f;
+  f32x4 acc[TV];
+#pragma unroll
+  for (int t = 0; t < TV; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = start; t0 < end; t0 += 32) {
+    float s[8];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      // K centroids of token t0 + 16*tile + n16 (A operand row n16, K slice q4)
+      const int tk = t0 + 16 * tile + n16;
+      uint32_t kc[NWK];
+      if (tk < end) {
+        const uint32_t* row = (const uint32_t*)(a.kp + token_row(a, b, kvh, tk) * (ROWK_DW * 4));
+        load_bits<NBK, ROWK_DW, ALK>(row, q4 * NBK, kc);
+      } else {
+#pragma unroll
+        for (int k = 0; k < NWK; ++k) kc[k] = 0u;
+      }
+      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        u32x4 akh, akl;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t t0 = ctk[code_at<BK>(kc, 8 * kb + 2 * c)];
+          const uint32_t t1 = ctk[code_at<BK>(kc, 8 * kb + 2 * c + 1)];
+          akh[c] = (t0 & 0xffffu) | (t1 << 16);
+          akl[c] = (t0 >> 16) | (t1 & 0xffff0000u);
+        }
+        S = mfma16_bf16(akh, bqh[kb], S);
+        S = mfma16_bf16(akl, bqh[kb], S);
+        S = mfma16_bf16(akh, bql[kb], S);
+      }
+      // D layout: lane (head n16, q4) register r = token t0 + 16*tile + 4*q4 + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = t0 + 16 * tile + 4 * q4 + r;
+        float v = -INFINITY;
+        if (tt < end) {
+          v = S[r] * sc * a.kn[token_row(a, b, kvh, tt)];
+          if constexpr (SCORES) {
+            if (head_ok) a.scores[((int64_t)b * a.Hq + h) * a.max_seq_len + tt] = v;
+          }
+        }
+        s[4 * tile + r] = v;
+      }
+    }
+    if constexpr (!SCORES) {
+      // tokens of this lane's 8 weights: e < 4 -> t0 + 4*q4 + e, e >= 4 -> t0 + 16 + 4*q4 + e - 4
+      int tok[8];
+      float vn[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        tok[e] = t0 + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4));
+        vn[e] = tok[e] < end ? a.vn[token_row(a, b, kvh, tok[e])] : 0.f;
+      }
+      float mb = s[0], nb = vn[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) {
+        mb = fmaxf(mb, s[e]);
+        nb = fmaxf(nb, vn[e]);
+      }
+      mb = fmaxf(mb, wave_xor(mb, 16));
+      mb = fmaxf(mb, wave_xor(mb, 32));
+      nb = fmaxf(nb, wave_xor(nb, 16));
+      nb = fmaxf(nb, wave_xor(nb, 32));
+      const float m_new = fmaxf(m_run, mb);
+      const float n_new = fmaxf(n_run, nb);
+      const float al = __expf(m_run - m_new);
+      const float inv_n = n_new > 0.f ? 1.0f / n_new : 0.f;
+      const float a_acc = al * n_run * inv_n;
+      float lsum = 0.f;
+      u32x4 bw;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float p0 = __expf(s[2 * c] - m_new), p1 = __expf(s[2 * c + 1] - m_new);
+        lsum += p0 + p1;
+        bw[c] = f32_to_f16_bits(p0 * vn[2 * c] * inv_n) | (f32_to_f16_bits(p1 * vn[2 * c + 1] * inv_n) << 16);
+      }
+      l_run = l_run * al + lsum;
+      m_run = m_new;
+      n_run = n_new;
+
+      // V centroids: lane (coord group m = n16, token group g = q4), same 8 tokens
+      uint32_t seg[8][NWV];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (tok[e] < end) {
+          const uint32_t* row = (const uint32_t*)(a.vp + token_row(a, b, kvh, tok[e]) * (ROWV_DW * 4));
+          load_bits<NBV, ROWV_DW, ALV>(row, n16 * NBV, seg[e]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < NWV; ++k) seg[e][k] = 0u;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TV; ++t) {
+        u32x4 av;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t lo = ctv[code_at<BV>(seg[2 * c], t)];
+          const uint32_t hi = ctv[code_at<BV>(seg[2 * c + 1], t)];
+          av[c] = lo | (hi << 16);
+        }
+        acc[t] = acc[t] * a_acc;
+        acc[t] = mfma16_f16(av, bw, acc[t]);
+      }
+    }
+  }
+
+  if constexpr (!SCORES) {
+    float lt = l_run;
+    lt += wave_xor(lt, 16);
+    lt += wave_xor(lt, 32);
+    if (head_ok) {
+      float* P = a.part + (((int64_t)sidx * a.B + b) * a.Hq + h) * (D + 2);
+      if (q4 == 0) {
+        P[0] = m_run;
+        P[1] = lt;
+      }
+      // D layout of the P.V MFMA: lane (head n16, q4) register r = coordinate group 4*q4 + r
+#pragma unroll
+      for (int t = 0; t < TV; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P[2 + (4 * q4 + r) * (D / 16) + t] = acc[t][r] * n_run;
+    }
+  }
+}
+
+template <int D>
+__global__ void qrot_kernel(const void* q, int q_dtype, const float* pik, int64_t rot_stride, int Hq, int bpr,
+                            float* out) {
+  __shared__ float qs[D];
+  const int bh = blockIdx.x, b = bh / Hq;
+  const int r = bpr ? b / bpr : 0;
+  const int k = threadIdx.x;
+  float v;
+  if (q_dtype == TQ_F32)
+    v = ((const float*)q)[(int64_t)bh * D + k];
+  else if (q_dtype == TQ_BF16)
+    v = bf16_bits_to_f32(((const uint16_t*)q)[(int64_t)bh * D + k]);
+  else
+    v = f16_bits_to_f32(((const uint16_t*)q)[(int64_t)bh * D + k]);
+  qs[k] = v;
+  __syncthreads();
+  const float* P = pik + r * rot_stride + (int64_t)k * D;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int j = 0; j < D; ++j) acc = fmaf(P[j], qs[j], acc);
+  out[(int64_t)bh * D + k] = acc;
+}
+
+template <int D, int OUT>
+__global__ void merge_kernel(const float* part, int s_eff, int BHq, int Hq, int bpr, const float* piv,
+                             int64_t rot_stride, void* out, float* lse) {
+  __shared__ float orot[D];
+  const int bh = blockIdx.x, b = bh / Hq;
+  const int r = bpr ? b / bpr : 0;
+  const int k = threadIdx.x;
+  const int64_t stride = (int64_t)BHq * (D + 2);
+  const float* P = part + (int64_t)bh * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < s_eff; ++s) M = fmaxf(M, P[s * stride]);
+  float L = 0.f, A = 0.f;
+  if (M > -INFINITY) {
+    for (int s = 0; s < s_eff; ++s) {
+      const float ms = P[s * stride];
+      if (ms > -INFINITY) {
+        const float w = __expf(ms - M);
+        L += w * P[s * stride + 1];
+        A += w * P[s * stride + 2 + k];
+      }
+    }
+  }
+  orot[k] = L > 0.f ? A / L : 0.f;
+  __syncthreads();
+  const float* Pv = piv + r * rot_stride;
+  float o = 0.f;
+#pragma unroll 8
+  for (int kk = 0; kk < D; ++kk) o = fmaf(Pv[(int64_t)kk * D + k], orot[kk], o);
+  const int64_t idx = (int64_t)bh * D + k;
+  if constexpr (OUT == TQ_F32)
+    ((float*)out)[idx] = o;
+  else if constexpr (OUT == TQ_BF16)
+    ((uint16_t*)out)[idx] = (uint16_t)f32_to_bf16_bits(o);
+  else
+    ((uint16_t*)out)[idx] = (uint16_t)f32_to_f16_bits(o);
+  if (k == 0 && lse) lse[bh] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu) {
+  AttnLayout L;
+  int splits = p->num_splits;
+  if (splits <= 0) {
+    int64_t pairs = (int64_t)p->batch * p->num_kv_heads;
+    if (pairs < 1) pairs = 1;
+    int64_t nblk = ((int64_t)p->max_seq_len + 31) / 32;
+    if (nblk < 1) nblk = 1;
+    int64_t target = (int64_t)num_cu * 16;
+    int64_t s_eff = (target + pairs - 1) / pairs;
+    if (s_eff > nblk) s_eff = nblk;
+    if (s_eff < 1) s_eff = 1;
+    splits = (int)((s_eff + kAttnWaves - 1) / kAttnWaves);
+  }
+  L.splits = splits;
+  L.qrot_off = 0;
+  size_t qbytes = align256((size_t)p->batch * p->num_q_heads * d * sizeof(float));
+  L.part_off = qbytes;
+  L.total = qbytes + align256((size_t)kAttnWaves * splits * p->batch * p->num_q_heads * (d + 2) * sizeof(float));
+  if (L.total == 0) L.total = 256;
+  return L;
+}
+
+template <int D, int BK, int BV>
+static hipError_t launch_attn_t(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
+                                const Rotation& rv, float* scores, bool scores_only, const AttnLayout& lay,
+                                hipStream_t st) {
+  uint8_t* ws = (uint8_t*)p->workspace;
+  float* qrot = (float*)(ws + lay.qrot_off);
+  const int Hq = p->num_q_heads, B = p->batch;
+  hipLaunchKernelGGL((qrot_kernel<D>), dim3(B * Hq), dim3(D), 0, st, p->q, p->q_dtype, rk.f32(0),
+                     (int64_t)(rk.f32_stride / sizeof(float)), Hq, p->batch_per_rot, qrot);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p->max_seq_len == 0 && scores_only) return hipSuccess;
+
+  AttnKArgs a;
+  a.qrot = qrot;
+  a.kp = p->k_packed;
+  a.kn = p->k_norms;
+  a.vp = scores_only ? p->k_packed : p->v_packed;
+  a.vn = scores_only ? p->k_norms : p->v_norms;
+  a.seq_lens = p->seq_lens;
+  a.block_table = p->block_table;
+  a.scores = scores;
+  a.part = (float*)(ws + lay.part_off);
+  a.max_seq_len = p->max_seq_len;
+  a.block_size = p->block_table ? p->block_size : 1;
+  a.bs_shift = -1;
+  if (p->block_table && (p->block_size & (p->block_size - 1)) == 0) {
+    int s = 0;
+    while ((1 << s) < p->block_size) ++s;
+    a.bs_shift = s;
+  }
+  a.mbps = p->max_blocks_per_seq;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = p->num_kv_heads;
+  a.G = Hq / p->num_kv_heads;
+  a.s_eff = lay.splits * kAttnWaves;
+  a.scale = p->scale;
+  LevelArgs lk = make_levels(ck), lv = make_levels(cv);
+  for (int j = 0; j < 16; ++j) a.ctk[j] = lk.centroid_bf16x2[j];
+  for (int j = 0; j < 8; ++j)
+    a.ctv[j] = (uint32_t)lv.centroid_f16[2 * j] | ((uint32_t)lv.centroid_f16[2 * j + 1] << 16);
+  dim3 grid((unsigned)lay.splits, (unsigned)p->num_kv_heads, (unsigned)B);
+  if (scores_only) {
+    hipLaunchKernelGGL((attn_kernel<D, BK, BV, true>), grid, dim3(kAttnWaves * 64), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((attn_kernel<D, BK, BV, false>), grid, dim3(kAttnWaves * 64), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t rs = (int64_t)(rv.f32_stride / sizeof(float));
+  switch (p->out_dtype) {
+    case TQ_F32:
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F32>), dim3(B * Hq), dim3(D), 0, st, a.part, a.s_eff, B * Hq, Hq,
+                         p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
+      break;
+    case TQ_BF16:
+      hipLaunchKernelGGL((merge_kernel<D, TQ_BF16>), dim3(B * Hq), dim3(D), 0, st, a.part, a.s_eff, B * Hq, Hq,
+                         p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
+      break;
+    default:
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F16>), dim3(B * Hq), dim3(D), 0, st, a.part, a.s_eff, B * Hq, Hq,
+                         p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int BK>
+static hipError_t attn_bv(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
+                          const Rotation& rv, float* scores, bool so, const AttnLayout& lay, hipStream_t st) {
+  // scores-only calls use the K width for the (unused) V side to avoid extra instances
+  const int bv = so ? BK : cv.bits;
+  switch (bv) {
+    case 2: return launch_attn_t<D, BK, 2>(p, ck, cv, rk, rv, scores, so, lay, st);
+    case 3: return launch_attn_t<D, BK, 3>(p, ck, cv, rk, rv, scores, so, lay, st);
+    default: return launch_attn_t<D, BK, 4>(p, ck, cv, rk, rv, scores, so, lay, st);
+  }
+}
+
+template <int D>
+static hipError_t attn_bk(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
+                          const Rotation& rv, float* scores, bool so, const AttnLayout& lay, hipStream_t st) {
+  switch (ck.bits) {
+    case 2: return attn_bv<D, 2>(p, ck, cv, rk, rv, scores, so, lay, st);
+    case 3: return attn_bv<D, 3>(p, ck, cv, rk, rv, scores, so, lay, st);
+    default: return attn_bv<D, 4>(p, ck, cv, rk, rv, scores, so, lay, st);
+  }
+}
+
+hipError_t launch_attention(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
+                            const Rotation& rv, float* scores, bool scores_only, const AttnLayout& lay,
+                            hipStream_t st) {
+  switch (rk.d) {
+    case 64: return attn_bk<64>(p, ck, cv, rk, rv, scores, scores_only, lay, st);
+    case 128: return attn_bk<128>(p, ck, cv, rk, rv, scores, scores_only, lay, st);
+    default: return attn_bk<256>(p, ck, cv, rk, rv, scores, scores_only, lay, st);
+  }
+}
+
+}  // namespace tq

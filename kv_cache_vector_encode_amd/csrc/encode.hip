@@ -1,0 +1,251 @@
+// Encode kernel: norm, rotation, Lloyd-Max quantization and LSB-first packing in one pass.
+//
+// Method (KV Cache API page, ginkgoq.github.io/TurboQuant/api/kv, TurboQuantCompressorMSE
+// .compress): n = ||x||; y = Pi x / (n + 1e-8); code_i = nearest centroid of y_i; store n
+// and the packed codes. Packing is the LSB-first bitstream of the same page's value packing
+// (quantize_value_chunk) at a dense (d*b + 7)//8 bytes per vector (value_formula_nbytes).
+//
+// Layout of the work. A wave owns 32 vectors. The rotation is one 32x32x16 bf16 MFMA per
+// (output tile t of 32 coordinates, K block kb of 16 inputs, pass): the B operand is the
+// vectors' raw inputs (lane v + 32*hh holds 8 consecutive inputs of vector v, so each lane
+// reads d/2 contiguous inputs with 16-byte loads), the A operand is a prebuilt tile of Pi
+// whose row order makes lane (v, hh) end up holding rotated coordinates hh*d/2 + 16t + i in
+// accumulator register i. A lane therefore owns d/2 consecutive output coordinates of one
+// vector, which pack into whole bytes (d/2 * b bits is a multiple of 8) with no cross-lane
+// traffic, and are written with wide stores.
+//
+// Precision: a code must match the float64 definition except within 1e-5 of a decision
+// boundary. One bf16 pass perturbs y by ~1e-4, so Pi is split into bf16 hi + lo (16
+// significant bits, error ~1e-6): bf16 inputs are exact and take 2 passes; float32 and
+// float16 inputs are split too and take 3 (Pi_hi x_hi + Pi_lo x_hi + Pi_hi x_lo). Instead of
+// dividing every coordinate by (n + 1e-8), the positive boundaries are scaled by it once per
+// vector and compared with the unnormalized Pi x.
+#include "device_common.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+struct EncodeKArgs {
+  const u32x4* frag;       // rotation tiles (u32x4 units), rotation r at frag + r * frag_stride
+  int64_t frag_stride;
+  const void* x;
+  int64_t x_row_stride;    // elements
+  uint8_t* packed;
+  float* norms;
+  const int64_t* slot;
+  int64_t n, vpr;
+  float pos_t[8];
+};
+
+constexpr int kEncWaves = 8;
+
+template <int D, int BITS>
+struct EncGeo {
+  static constexpr int T = D / 32;                 // output tiles
+  static constexpr int KB = D / 16;                // K blocks
+  static constexpr int HALF = D / 2;               // coordinates per lane
+  static constexpr int ROW = D * BITS / 8;         // packed bytes per vector
+  static constexpr int CHUNK = HALF * BITS / 8;    // packed bytes per lane
+  static constexpr int CHUNK_DW = CHUNK / 4;
+  static constexpr int G = (CHUNK % 16 == 0 && ROW % 16 == 0) ? 16 : ((CHUNK % 8 == 0 && ROW % 8 == 0) ? 8 : 4);
+  static constexpr int FRAG_U4 = 2 * T * KB * 64;  // hi and lo tiles, u32x4 per lane
+  static constexpr bool LDS = (D <= 128);
+};
+
+template <int D, int BITS, int IN>
+__global__ void __launch_bounds__(kEncWaves * 64) encode_kernel(EncodeKArgs a) {
+  using Geo = EncGeo<D, BITS>;
+  constexpr int T = Geo::T, KB = Geo::KB, HALF = Geo::HALF;
+  constexpr bool SPLIT_X = (IN != TQ_BF16);
+  extern __shared__ u32x4 smem[];
+
+  const int r = blockIdx.y;
+  const u32x4* gfrag = a.frag + (int64_t)r * a.frag_stride;
+  if constexpr (Geo::LDS) {
+    for (int i = threadIdx.x; i < Geo::FRAG_U4; i += blockDim.x) smem[i] = gfrag[i];
+    __syncthreads();
+  }
+  // Tile reads go through an offset the compiler cannot prove loop-invariant; otherwise it
+  // hoists every tile of Pi into registers and spills.
+  const char* abase = Geo::LDS ? (const char*)smem : (const char*)gfrag;
+
+  const int64_t v_begin = a.vpr ? (int64_t)r * a.vpr : 0;
+  const int64_t v_end = a.vpr ? min(a.n, v_begin + a.vpr) : a.n;
+  const int64_t ntile = (v_end - v_begin + 31) / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int vl = lane & 31, hh = lane >> 5;
+
+  for (int64_t tile = (int64_t)blockIdx.x * kEncWaves + wave; tile < ntile;
+       tile += (int64_t)gridDim.x * kEncWaves) {
+    const int64_t vec = v_begin + tile * 32 + vl;
+    const bool valid = vec < v_end;
+    const int64_t vsafe = valid ? vec : v_begin;
+
+    // ---- load this lane's d/2 inputs as MFMA B operands (bf16 hi, and lo for split inputs)
+    u32x4 xh[KB], xl[SPLIT_X ? KB : 1];
+    float ss0 = 0.f, ss1 = 0.f;
+    if constexpr (IN == TQ_BF16) {
+      const uint16_t* xp = (const uint16_t*)a.x + vsafe * a.x_row_stride + hh * HALF;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        xh[kb] = *(const u32x4*)(xp + 8 * kb);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float lo = bf16_lo_to_f32(xh[kb][c]), hi = bf16_hi_to_f32(xh[kb][c]);
+          ss0 = fmaf(lo, lo, ss0);
+          ss1 = fmaf(hi, hi, ss1);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        float v[8];
+        if constexpr (IN == TQ_F32) {
+          const float* xp = (const float*)a.x + vsafe * a.x_row_stride + hh * HALF + 8 * kb;
+          u32x4 p0 = *(const u32x4*)xp, p1 = *(const u32x4*)(xp + 4);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            v[c] = __uint_as_float(p0[c]);
+            v[4 + c] = __uint_as_float(p1[c]);
+          }
+        } else {
+          const uint16_t* xp = (const uint16_t*)a.x + vsafe * a.x_row_stride + hh * HALF + 8 * kb;
+          u32x4 p = *(const u32x4*)xp;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            v[2 * c] = f16_bits_to_f32(p[c]);
+            v[2 * c + 1] = f16_bits_to_f32(p[c] >> 16);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint32_t h0 = f32_to_bf16_bits(v[2 * c]), h1 = f32_to_bf16_bits(v[2 * c + 1]);
+          uint32_t l0 = f32_to_bf16_bits(v[2 * c] - bf16_bits_to_f32(h0));
+          uint32_t l1 = f32_to_bf16_bits(v[2 * c + 1] - bf16_bits_to_f32(h1));
+          xh[kb][c] = h0 | (h1 << 16);
+          xl[kb][c] = l0 | (l1 << 16);
+          ss0 = fmaf(v[2 * c], v[2 * c], ss0);
+          ss1 = fmaf(v[2 * c + 1], v[2 * c + 1], ss1);
+        }
+      }
+    }
+    float ss = ss0 + ss1;
+    ss += wave_xor(ss, 32);            // the other half of the same vector
+    const float nrm = sqrtf(ss);
+    const float scale = nrm + 1e-8f;
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = a.pos_t[j] * scale;
+
+    // ---- rotate tile by tile, quantize, pack into this lane's chunk
+    uint32_t aoff = (uint32_t)lane * 16u;
+    asm volatile("" : "+v"(aoff));
+    uint32_t pk[Geo::CHUNK_DW];
+#pragma unroll
+    for (int w = 0; w < Geo::CHUNK_DW; ++w) pk[w] = 0u;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 ahi = *(const u32x4*)(abase + aoff + ((0 * T + t) * KB + kb) * 1024);
+        const u32x4 alo = *(const u32x4*)(abase + aoff + ((1 * T + t) * KB + kb) * 1024);
+        acc = mfma32_bf16(ahi, xh[kb], acc);
+        acc = mfma32_bf16(alo, xh[kb], acc);
+        if constexpr (SPLIT_X) acc = mfma32_bf16(ahi, xl[kb], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t code = quantize_scaled<BITS>(acc[i], p);
+        const int pos = (16 * t + i) * BITS;
+        pk[pos >> 5] |= code << (pos & 31);
+        if ((pos & 31) + BITS > 32) pk[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+      }
+    }
+
+    // ---- store
+    if (valid) {
+      const int64_t row = a.slot ? a.slot[vec] : vec;
+      if (row >= 0) {
+        uint8_t* dst = a.packed + row * Geo::ROW + hh * Geo::CHUNK;
+        if constexpr (Geo::G == 16) {
+#pragma unroll
+          for (int w = 0; w < Geo::CHUNK_DW; w += 4)
+            *(u32x4*)(dst + 4 * w) = u32x4{pk[w], pk[w + 1], pk[w + 2], pk[w + 3]};
+        } else if constexpr (Geo::G == 8) {
+#pragma unroll
+          for (int w = 0; w < Geo::CHUNK_DW; w += 2) *(u32x2*)(dst + 4 * w) = u32x2{pk[w], pk[w + 1]};
+        } else {
+#pragma unroll
+          for (int w = 0; w < Geo::CHUNK_DW; ++w) *(uint32_t*)(dst + 4 * w) = pk[w];
+        }
+        if (hh == 0) a.norms[row] = nrm;
+      }
+    }
+  }
+}
+
+template <int D, int BITS, int IN>
+static hipError_t launch_encode_t(const EncodeLaunch& L) {
+  using Geo = EncGeo<D, BITS>;
+  EncodeKArgs k;
+  k.frag = (const u32x4*)L.rot->enc(0);
+  k.frag_stride = (int64_t)(L.rot->enc_stride / sizeof(u32x4));
+  k.x = L.x;
+  k.x_row_stride = L.x_row_stride;
+  k.packed = L.packed;
+  k.norms = L.norms;
+  k.slot = L.slot_mapping;
+  k.n = L.n;
+  k.vpr = L.vectors_per_rot;
+  for (int j = 0; j < 8; ++j) k.pos_t[j] = L.lv.pos_thresholds[j];
+  const int64_t per_rot = L.vectors_per_rot ? L.vectors_per_rot : L.n;
+  const int nrot = L.vectors_per_rot ? (int)((L.n + L.vectors_per_rot - 1) / L.vectors_per_rot) : 1;
+  const int64_t tiles = (per_rot + 31) / 32;
+  const size_t lds = Geo::LDS ? Geo::FRAG_U4 * sizeof(u32x4) : 0;
+  static bool attr_done = false;
+  if (!attr_done && lds > 0) {
+    hipError_t e = hipFuncSetAttribute((const void*)encode_kernel<D, BITS, IN>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  const int cu = device_cu_count(L.rot->device);
+  const int per_cu = lds > 0 ? (int)((160 * 1024) / lds) : 2;
+  const int64_t want = (int64_t)cu * (per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu));
+  int64_t bx = (want + nrot - 1) / nrot;
+  const int64_t need = (tiles + kEncWaves - 1) / kEncWaves;
+  if (bx > need) bx = need;
+  if (bx < 1) bx = 1;
+  dim3 grid((unsigned)bx, (unsigned)nrot);
+  hipLaunchKernelGGL((encode_kernel<D, BITS, IN>), grid, dim3(kEncWaves * 64), lds, L.stream, k);
+  return hipGetLastError();
+}
+
+template <int D, int BITS>
+static hipError_t dispatch_in(const EncodeLaunch& L) {
+  switch (L.x_dtype) {
+    case TQ_F32: return launch_encode_t<D, BITS, TQ_F32>(L);
+    case TQ_BF16: return launch_encode_t<D, BITS, TQ_BF16>(L);
+    default: return launch_encode_t<D, BITS, TQ_F16>(L);
+  }
+}
+
+template <int D>
+static hipError_t dispatch_bits(const EncodeLaunch& L) {
+  switch (L.bits) {
+    case 2: return dispatch_in<D, 2>(L);
+    case 3: return dispatch_in<D, 3>(L);
+    default: return dispatch_in<D, 4>(L);
+  }
+}
+
+hipError_t launch_encode(const EncodeLaunch& L) {
+  switch (L.rot->d) {
+    case 64: return dispatch_bits<64>(L);
+    case 128: return dispatch_bits<128>(L);
+    default: return dispatch_bits<256>(L);
+  }
+}
+
+}  // namespace tq

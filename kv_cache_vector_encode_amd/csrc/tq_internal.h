@@ -1,0 +1,100 @@
+// Internal declarations shared by the host code and the kernel launchers of libtq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "tq.h"
+
+namespace tq {
+
+constexpr int kMaxLevels = 16;   // 4-bit codes on the GPU
+
+// Codebook: host float64 solution plus the float32 / fp16 copies the kernels take by value.
+struct Codebook {
+  int d = 0, bits = 0;
+  std::vector<double> centroids;   // [2^bits] ascending
+  std::vector<double> thresholds;  // [2^bits - 1]
+  double mse = 0.0;
+};
+
+// Rotation stack: float64 host copy and device operand tiles.
+struct Rotation {
+  int d = 0, n_rot = 0, device = -1;
+  std::vector<double> pi;        // [n_rot, d, d] row-major
+  // Device buffers (one allocation, offsets below), per rotation:
+  //  enc_frag: bf16 MFMA A tiles of Pi (hi then lo), 4*d*d bytes
+  //  dec_frag: fp16 MFMA A tiles of Pi^T, 2*d*d bytes
+  //  pi_f32:   Pi in float32 row-major, 4*d*d bytes
+  void* dev = nullptr;
+  size_t enc_stride = 0, dec_stride = 0, f32_stride = 0;   // bytes per rotation
+  size_t enc_off = 0, dec_off = 0, f32_off = 0;             // bytes from dev
+  const uint8_t* enc(int r) const { return (const uint8_t*)dev + enc_off + (size_t)r * enc_stride; }
+  const uint8_t* dec(int r) const { return (const uint8_t*)dev + dec_off + (size_t)r * dec_stride; }
+  const float* f32(int r) const { return (const float*)((const uint8_t*)dev + f32_off + (size_t)r * f32_stride); }
+};
+
+// Levels passed to kernels by value.
+struct LevelArgs {
+  float pos_thresholds[kMaxLevels / 2];   // t_{L/2+1} .. t_{L-1}: positive decision boundaries
+  uint16_t centroid_f16[kMaxLevels];      // c_k as fp16 bits
+  uint32_t centroid_bf16x2[kMaxLevels];   // c_k = hi + lo as bf16 bits: hi | lo << 16
+  float centroid_f32[kMaxLevels];
+};
+
+LevelArgs make_levels(const Codebook& cb);
+
+void set_error(const std::string& msg);
+
+// ---- launchers (return hipError_t) ----
+struct EncodeLaunch {
+  const Rotation* rot;
+  LevelArgs lv;
+  int bits, x_dtype;
+  int64_t vectors_per_rot, n, x_row_stride;
+  const void* x;
+  uint8_t* packed;
+  float* norms;
+  const int64_t* slot_mapping;
+  hipStream_t stream;
+};
+hipError_t launch_encode(const EncodeLaunch& a);
+
+struct DecodeLaunch {
+  const Rotation* rot;
+  LevelArgs lv;
+  int bits, out_dtype;
+  int64_t vectors_per_rot, n;
+  const uint8_t* packed;
+  const float* norms;
+  const int64_t* slot_mapping;
+  void* out;
+  hipStream_t stream;
+};
+hipError_t launch_decode(const DecodeLaunch& a);
+
+// Attention / scores: workspace layout is computed by attn_workspace_layout.
+struct AttnLayout {
+  int splits;            // token splits per (b, kv head)
+  size_t qrot_off;       // float [B, Hq, d]: Pi_K q
+  size_t part_off;       // float [splits, B, Hq, d + 2]: (m, l, acc[d])
+  size_t total;
+};
+AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu);
+hipError_t launch_attention(const tq_attn_params* p, const Codebook& ck, const Codebook& cv,
+                            const Rotation& rk, const Rotation& rv, float* scores_out,
+                            bool scores_only, const AttnLayout& lay, hipStream_t stream);
+
+int device_cu_count(int device);
+
+}  // namespace tq
+
+struct tq_codebook {
+  tq::Codebook cb;
+};
+struct tq_rotation {
+  tq::Rotation rot;
+};

@@ -1,0 +1,124 @@
+"""Parity helpers for the GPU tests: compare libtq's outputs with the float64 oracle.
+
+Bars:
+  * codes: bit-exact, except coordinates whose oracle rotated value lies within 1e-5 of a
+    decision boundary (counted and reported as flips);
+  * norms: |n_gpu - n| <= (d/4 + 4) * 2^-24 * n, the rounding bound of the kernel's float32
+    sum of squares (two chains of d/4 fused multiply-adds per lane, two adds, a square root);
+  * decode: per vector ||x_gpu - x_ref|| <= (2e-3 + u_out) ||x_ref||, x_ref = float64 oracle
+    decode of the GPU's own codes and norms, u_out the output dtype's unit roundoff (0 for
+    float32, 2^-8 bfloat16, 2^-11 float16);
+  * scores: |s_gpu - s_ref| <= 2e-3 * scale * n_t * ||q|| * ||c[idx_t]|| (Cauchy-Schwarz scale);
+  * attention: ||o_gpu - o_ref|| <= 2e-3 * sum_t p_t ||v_hat_t||; |lse_gpu - lse_ref| <= the
+    largest score bound of the row.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+from oracle import attention as oatt, codebook as ocb, codec as occ, rotation as orot
+
+WINDOW = 1e-5
+REL = 2e-3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64) if t.dtype != torch.float64 else t.cpu().numpy()
+
+
+def check_encode(x: np.ndarray, packed: np.ndarray, norms: np.ndarray, pi: np.ndarray, d: int, bits: int,
+                 what: str = ""):
+    """x float64 [N, d] (the exact input values), packed/norms from the GPU. Returns flip count."""
+    cb = ocb.codebook(d, bits)
+    codes_ref, n_ref, y = occ.encode_codes(x, pi, cb.centroids)
+    codes = occ.unpack_codes(packed, bits, d)
+    delta = occ.boundary_distance(y, cb.thresholds)
+    diff = codes != codes_ref
+    bad = diff & (delta >= WINDOW)
+    if bad.any():
+        i, j = np.argwhere(bad)[0]
+        raise AssertionError("%s: %d codes differ outside the %.0e window (first at vector %d coord %d: "
+                             "gpu %d ref %d, y=%.9g, delta=%.3g)" % (what, int(bad.sum()), WINDOW, i, j,
+                                                                     codes[i, j], codes_ref[i, j], y[i, j],
+                                                                     delta[i, j]))
+    nr = np.sqrt(np.sum(x * x, axis=1))
+    ng = norms.astype(np.float64)
+    tol = (d / 4 + 4) * 2.0 ** -24 * nr
+    assert np.all(np.abs(ng - nr) <= tol), "%s: norm error %.3g > bound" % (what, np.max(np.abs(ng - nr) / np.maximum(nr, 1e-300)))
+    flips = int(diff.sum())
+    inside = int((delta < WINDOW).sum())
+    log("%s: %d vectors, %d flips among %d coordinates inside the window" % (what, x.shape[0], flips, inside))
+    return flips
+
+
+def check_decode(out: torch.Tensor, packed: np.ndarray, norms: np.ndarray, pi: np.ndarray, d: int, bits: int,
+                 what: str = ""):
+    # against the unrounded float64 decode. A 16-bit output adds its own round-to-nearest error,
+    # at most one unit roundoff u of every element and so of the vector norm (u = 2^-8 for
+    # bfloat16, 2^-11 for float16): the bar is 2e-3 + u for those outputs.
+    cb = ocb.codebook(d, bits)
+    ref = occ.decode(packed, norms, pi, cb.centroids, bits, d)
+    got = to64(out)
+    u = {torch.float32: 0.0, torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}[out.dtype]
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    ok = (num <= (REL + u) * den) | ((den == 0) & (num == 0))
+    assert ok.all(), "%s: decode error %.3g > %.3g" % (what, np.max(num / np.maximum(den, 1e-300)), REL + u)
+    log("%s: decode max rel err %.3g" % (what, float(np.max(num / np.maximum(den, 1e-300)))))
+
+
+def rotation_pair(d: int, seeds):
+    """(device Rotation stack, list of oracle float64 rotations) from the same Gaussian draws."""
+    import kv_cache_vector_encode_amd as tq
+    import tq_inputs as ti
+    g = ti.rotation_gaussians(d, seeds)
+    rot = tq.Rotation.from_gaussian(g)
+    return rot, [orot.haar_rotation(gi.numpy()) for gi in g]
+
+
+def score_bounds(q64: np.ndarray, k_norms: np.ndarray, k_codes: np.ndarray, cb, scale: float):
+    """2e-3 * scale * n_t * ||q|| * ||c[idx_t]||, shapes [B, Hq, T] (q [B,Hq,d], k [B,Hkv,T,...])."""
+    B, Hq, d = q64.shape
+    Hkv = k_norms.shape[1]
+    G = Hq // Hkv
+    cnorm = np.linalg.norm(cb.centroids[k_codes.astype(np.int64)], axis=-1)   # [B,Hkv,T]
+    qn = np.linalg.norm(q64, axis=-1)                                         # [B,Hq]
+    kv = np.repeat(k_norms.astype(np.float64) * cnorm, G, axis=1)             # [B,Hq,T]
+    return REL * scale * kv * qn[:, :, None]
+
+
+def check_attention(o_gpu: np.ndarray, lse_gpu, q64, khat, vhat, scale, lens, what=""):
+    """khat/vhat float64 [B, Hkv, T, d] decoded from the GPU's codes."""
+    o_ref, lse_ref = oatt.attention(q64, khat, vhat, scale, seq_lens=lens)
+    s_ref = oatt.scores(q64, khat, scale, seq_lens=lens)
+    B, Hq, d = q64.shape
+    G = Hq // khat.shape[1]
+    worst = 0.0
+    for b in range(B):
+        L = int(lens[b]) if lens is not None else khat.shape[2]
+        for h in range(Hq):
+            if L == 0:
+                assert np.all(o_gpu[b, h] == 0), (what, b, h)
+                if lse_gpu is not None:
+                    assert np.isneginf(lse_gpu[b, h])
+                continue
+            p = np.exp(s_ref[b, h, :L] - lse_ref[b, h])
+            bound = REL * float(p @ np.linalg.norm(vhat[b, h // G, :L], axis=1))
+            err = float(np.linalg.norm(o_gpu[b, h] - o_ref[b, h]))
+            worst = max(worst, err / bound)
+            assert err <= bound, "%s: b=%d h=%d attention error %.3g > bound %.3g" % (what, b, h, err, bound)
+            if lse_gpu is not None:
+                kn = np.linalg.norm(khat[b, h // G, :L], axis=1)
+                lb = REL * scale * float(np.max(kn)) * float(np.linalg.norm(q64[b, h]))
+                assert abs(lse_gpu[b, h] - lse_ref[b, h]) <= lb + 1e-6, (what, b, h, lse_gpu[b, h], lse_ref[b, h])
+    log("%s: attention worst error / bound = %.3g" % (what, worst))
+    return worst
