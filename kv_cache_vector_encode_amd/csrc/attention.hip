@@ -159,42 +159,102 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_kernel(AttnKArgs a) {
 #pragma unroll
   for (int t = 0; t < TV; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // ---- operands of one 32-token block, fetched one block ahead of their use. This lane
+  //      needs the K codes of token t0 + 16*tile + n16 (score A operand row n16) and, for the
+  //      8 tokens tok(e) = t0 + (e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4) whose scores land in
+  //      it and whose weights it supplies to P.V, their K norms, V norms and V codes.
+  struct Blk {
+    uint32_t kc[2][NWK];
+    float kn[8], vn[8];
+    uint32_t seg[8][NWV];
+  };
+  const bool paged = a.block_table != nullptr;
+  const bool fastpage = paged && a.bs_shift >= 4;   // a 32-token block then spans <= 2 pages
+  const int64_t dense_base = ((int64_t)b * a.Hkv + kvh) * a.max_seq_len;
+  const int32_t* btab = paged ? a.block_table + (int64_t)b * a.mbps : nullptr;
+  auto pages = [&](int t0, int& p0, int& p1) {
+    p0 = p1 = 0;
+    if (fastpage && t0 < end) {
+      p0 = btab[t0 >> a.bs_shift];
+      p1 = btab[min(t0 + 31, end - 1) >> a.bs_shift];
+    }
+  };
+  auto row_of = [&](int tt, int t0, int p0, int p1) -> int64_t {
+    if (!paged) return dense_base + tt;
+    if (fastpage) {
+      const int phys = ((tt >> a.bs_shift) == (t0 >> a.bs_shift)) ? p0 : p1;
+      return (((int64_t)phys * a.Hkv + kvh) << a.bs_shift) + (tt & (a.block_size - 1));
+    }
+    const int blk = tt / a.block_size;
+    return ((int64_t)btab[blk] * a.Hkv + kvh) * a.block_size + (tt - blk * a.block_size);
+  };
+  auto fetch = [&](int t0, int p0, int p1, Blk& B) {
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      const int tk = t0 + 16 * tile + n16;
+      if (tk < end) {
+        const uint32_t* row = (const uint32_t*)(a.kp + row_of(tk, t0, p0, p1) * (ROWK_DW * 4));
+        load_bits<NBK, ROWK_DW, ALK>(row, q4 * NBK, B.kc[tile]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < NWK; ++k) B.kc[tile][k] = 0u;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tt = t0 + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4));
+      B.kn[e] = 0.f;
+      B.vn[e] = 0.f;
+#pragma unroll
+      for (int k = 0; k < NWV; ++k) B.seg[e][k] = 0u;
+      if (tt < end) {
+        const int64_t row = row_of(tt, t0, p0, p1);
+        B.kn[e] = a.kn[row];
+        if constexpr (!SCORES) {
+          B.vn[e] = a.vn[row];
+          load_bits<NBV, ROWV_DW, ALV>((const uint32_t*)(a.vp + row * (ROWV_DW * 4)), n16 * NBV, B.seg[e]);
+        }
+      }
+    }
+  };
+
+  Blk cur;
+  int p0, p1, np0, np1;
+  pages(start, p0, p1);
+  fetch(start, p0, p1, cur);
+  pages(start + 32, np0, np1);
+
   for (int t0 = start; t0 < end; t0 += 32) {
+    Blk nxt;
+    fetch(t0 + 32, np0, np1, nxt);
+    int nnp0, nnp1;
+    pages(t0 + 64, nnp0, nnp1);
+
     float s[8];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      // K centroids of token t0 + 16*tile + n16 (A operand row n16, K slice q4)
-      const int tk = t0 + 16 * tile + n16;
-      uint32_t kc[NWK];
-      if (tk < end) {
-        const uint32_t* row = (const uint32_t*)(a.kp + token_row(a, b, kvh, tk) * (ROWK_DW * 4));
-        load_bits<NBK, ROWK_DW, ALK>(row, q4 * NBK, kc);
-      } else {
-#pragma unroll
-        for (int k = 0; k < NWK; ++k) kc[k] = 0u;
-      }
       f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         u32x4 akh, akl;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t t0 = ctk[code_at<BK>(kc, 8 * kb + 2 * c)];
-          const uint32_t t1 = ctk[code_at<BK>(kc, 8 * kb + 2 * c + 1)];
-          akh[c] = (t0 & 0xffffu) | (t1 << 16);
-          akl[c] = (t0 >> 16) | (t1 & 0xffff0000u);
+          const uint32_t c0 = ctk[code_at<BK>(cur.kc[tile], 8 * kb + 2 * c)];
+          const uint32_t c1 = ctk[code_at<BK>(cur.kc[tile], 8 * kb + 2 * c + 1)];
+          akh[c] = (c0 & 0xffffu) | (c1 << 16);
+          akl[c] = (c0 >> 16) | (c1 & 0xffff0000u);
         }
         S = mfma16_bf16(akh, bqh[kb], S);
         S = mfma16_bf16(akl, bqh[kb], S);
         S = mfma16_bf16(akh, bql[kb], S);
       }
-      // D layout: lane (head n16, q4) register r = token t0 + 16*tile + 4*q4 + r
+      // D layout: lane (head n16, q4) register r = token t0 + 16*tile + 4*q4 + r = tok(4*tile + r)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tt = t0 + 16 * tile + 4 * q4 + r;
         float v = -INFINITY;
         if (tt < end) {
-          v = S[r] * sc * a.kn[token_row(a, b, kvh, tt)];
+          v = S[r] * sc * cur.kn[4 * tile + r];
           if constexpr (SCORES) {
             if (head_ok) a.scores[((int64_t)b * a.Hq + h) * a.max_seq_len + tt] = v;
           }
@@ -203,19 +263,11 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_kernel(AttnKArgs a) {
       }
     }
     if constexpr (!SCORES) {
-      // tokens of this lane's 8 weights: e < 4 -> t0 + 4*q4 + e, e >= 4 -> t0 + 16 + 4*q4 + e - 4
-      int tok[8];
-      float vn[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        tok[e] = t0 + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4));
-        vn[e] = tok[e] < end ? a.vn[token_row(a, b, kvh, tok[e])] : 0.f;
-      }
-      float mb = s[0], nb = vn[0];
+      float mb = s[0], nb = cur.vn[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) {
         mb = fmaxf(mb, s[e]);
-        nb = fmaxf(nb, vn[e]);
+        nb = fmaxf(nb, cur.vn[e]);
       }
       mb = fmaxf(mb, wave_xor(mb, 16));
       mb = fmaxf(mb, wave_xor(mb, 32));
@@ -230,39 +282,31 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_kernel(AttnKArgs a) {
       u32x4 bw;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float p0 = __expf(s[2 * c] - m_new), p1 = __expf(s[2 * c + 1] - m_new);
-        lsum += p0 + p1;
-        bw[c] = f32_to_f16_bits(p0 * vn[2 * c] * inv_n) | (f32_to_f16_bits(p1 * vn[2 * c + 1] * inv_n) << 16);
+        const float e0 = __expf(s[2 * c] - m_new), e1 = __expf(s[2 * c + 1] - m_new);
+        lsum += e0 + e1;
+        bw[c] = pack_f16x2(e0 * cur.vn[2 * c] * inv_n, e1 * cur.vn[2 * c + 1] * inv_n);
       }
       l_run = l_run * al + lsum;
       m_run = m_new;
       n_run = n_new;
 
-      // V centroids: lane (coord group m = n16, token group g = q4), same 8 tokens
-      uint32_t seg[8][NWV];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (tok[e] < end) {
-          const uint32_t* row = (const uint32_t*)(a.vp + token_row(a, b, kvh, tok[e]) * (ROWV_DW * 4));
-          load_bits<NBV, ROWV_DW, ALV>(row, n16 * NBV, seg[e]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < NWV; ++k) seg[e][k] = 0u;
-        }
-      }
+      // V centroids: lane (coordinate group m = n16, token group g = q4), same 8 tokens
 #pragma unroll
       for (int t = 0; t < TV; ++t) {
         u32x4 av;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t lo = ctv[code_at<BV>(seg[2 * c], t)];
-          const uint32_t hi = ctv[code_at<BV>(seg[2 * c + 1], t)];
+          const uint32_t lo = ctv[code_at<BV>(cur.seg[2 * c], t)];
+          const uint32_t hi = ctv[code_at<BV>(cur.seg[2 * c + 1], t)];
           av[c] = lo | (hi << 16);
         }
         acc[t] = acc[t] * a_acc;
         acc[t] = mfma16_f16(av, bw, acc[t]);
       }
     }
+    cur = nxt;
+    np0 = nnp0;
+    np1 = nnp1;
   }
 
   if constexpr (!SCORES) {

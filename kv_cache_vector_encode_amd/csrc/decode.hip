@@ -57,13 +57,15 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vl = lane & 31, hh = lane >> 5;
 
-  for (int64_t tile = (int64_t)blockIdx.x * kDecWaves + wave; tile < ntile;
-       tile += (int64_t)gridDim.x * kDecWaves) {
-    const int64_t vec = v_begin + tile * 32 + vl;
-    const bool valid = vec < v_end;
-    int64_t row = valid ? (a.slot ? a.slot[vec] : vec) : -1;
-    uint32_t cw[Geo::CHUNK_DW];
-    float nrm = 0.f;
+  // Two-stage prefetch: the packed row of the next tile is loaded while this tile is decoded,
+  // and with a slot gather the slot index is read one tile earlier still.
+  const int64_t wstride = (int64_t)gridDim.x * kDecWaves;
+  auto row_of = [&](int64_t tl) -> int64_t {
+    const int64_t v = v_begin + tl * 32 + vl;
+    if (tl >= ntile || v >= v_end) return -1;
+    return a.slot ? a.slot[v] : v;
+  };
+  auto fetch = [&](int64_t row, uint32_t (&cw)[Geo::CHUNK_DW], float& nrm) {
     if (row >= 0) {
       const uint8_t* src = a.packed + row * Geo::ROW + hh * Geo::CHUNK;
       if constexpr (Geo::G == 16) {
@@ -86,7 +88,24 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
     } else {
 #pragma unroll
       for (int w = 0; w < Geo::CHUNK_DW; ++w) cw[w] = 0u;
+      nrm = 0.f;
     }
+  };
+  int64_t tile = (int64_t)blockIdx.x * kDecWaves + wave;
+  uint32_t cwn[Geo::CHUNK_DW];
+  float nrmn;
+  fetch(row_of(tile), cwn, nrmn);
+  int64_t row_nn = row_of(tile + wstride);
+
+  for (; tile < ntile; tile += wstride) {
+    const int64_t vec = v_begin + tile * 32 + vl;
+    const bool valid = vec < v_end;
+    uint32_t cw[Geo::CHUNK_DW];
+#pragma unroll
+    for (int w = 0; w < Geo::CHUNK_DW; ++w) cw[w] = cwn[w];
+    const float nrm = nrmn;
+    fetch(row_nn, cwn, nrmn);
+    row_nn = row_of(tile + 2 * wstride);
 
     // ---- codes -> fp16 centroids, 8 per K block
     u32x4 bfrag[KB];
@@ -129,11 +148,8 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
           uint32_t w[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            float lo = acc[2 * j] * nrm, hi = acc[2 * j + 1] * nrm;
-            if constexpr (OUT == TQ_BF16)
-              w[j] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-            else
-              w[j] = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+            const float lo = acc[2 * j] * nrm, hi = acc[2 * j + 1] * nrm;
+            w[j] = OUT == TQ_BF16 ? pack_bf16x2(lo, hi) : pack_f16x2(lo, hi);
           }
           uint16_t* o = (uint16_t*)a.out + base;
           *(u32x4*)o = u32x4{w[0], w[1], w[2], w[3]};
@@ -170,8 +186,9 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
     attr_done = true;
   }
   const int cu = device_cu_count(L.rot->device);
+  // workgroups per CU: LDS-limited at d=256 (128 KiB of tiles), else up to 3 (24 waves)
   int per_cu = (int)((160 * 1024 - 256) / lds);
-  per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+  per_cu = per_cu < 1 ? 1 : (per_cu > 3 ? 3 : per_cu);
   const int64_t want = (int64_t)cu * per_cu;
   int64_t bx = (want + nrot - 1) / nrot;
   const int64_t need = (tiles + kDecWaves - 1) / kDecWaves;

@@ -37,7 +37,6 @@ struct EncodeKArgs {
   float pos_t[8];
 };
 
-constexpr int kEncWaves = 8;
 
 template <int D, int BITS>
 struct EncGeo {
@@ -50,10 +49,18 @@ struct EncGeo {
   static constexpr int G = (CHUNK % 16 == 0 && ROW % 16 == 0) ? 16 : ((CHUNK % 8 == 0 && ROW % 8 == 0) ? 8 : 4);
   static constexpr int FRAG_U4 = 2 * T * KB * 64;  // hi and lo tiles, u32x4 per lane
   static constexpr bool LDS = (D <= 128);
+  // Occupancy plan: at d=128 the 64 KiB of Pi tiles allow one workgroup per CU, so it has 12
+  // waves (3 per SIMD, up to 168 VGPRs: room for a prefetched tile); d=64 fits two 8-wave
+  // workgroups per CU; d=256 reads Pi from L2 and runs 8 waves.
+  static constexpr int WAVES = D == 128 ? 12 : 8;
+  static constexpr int WPE = D == 128 ? 3 : (D == 64 ? 4 : 2);
+  static constexpr int WG_PER_CU = D == 64 ? 2 : 1;
 };
 
 template <int D, int BITS, int IN>
-__global__ void __launch_bounds__(kEncWaves * 64) encode_kernel(EncodeKArgs a) {
+__global__ void __launch_bounds__((EncGeo<D, BITS>::WAVES * 64))
+__attribute__((amdgpu_waves_per_eu(EncGeo<D, BITS>::WPE)))
+encode_kernel(EncodeKArgs a) {
   using Geo = EncGeo<D, BITS>;
   constexpr int T = Geo::T, KB = Geo::KB, HALF = Geo::HALF;
   constexpr bool SPLIT_X = (IN != TQ_BF16);
@@ -75,20 +82,40 @@ __global__ void __launch_bounds__(kEncWaves * 64) encode_kernel(EncodeKArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vl = lane & 31, hh = lane >> 5;
 
-  for (int64_t tile = (int64_t)blockIdx.x * kEncWaves + wave; tile < ntile;
-       tile += (int64_t)gridDim.x * kEncWaves) {
+  // Raw inputs of one tile: lane (v, hh) reads its d/2 contiguous elements with 16-byte loads.
+  // bf16 inputs are the MFMA B operands as loaded and are prefetched one tile ahead, so every
+  // wave keeps a tile of loads in flight while it rotates and quantizes the previous one.
+  constexpr int ELEM = IN == TQ_F32 ? 4 : 2;
+  constexpr int NRAW = HALF * ELEM / 16;
+  constexpr bool PREFETCH = (IN == TQ_BF16) && D <= 128;
+  const int64_t wstride = (int64_t)gridDim.x * Geo::WAVES;
+  auto fetch = [&](int64_t tl, u32x4 (&raw)[NRAW]) {
+    const int64_t v = v_begin + tl * 32 + vl;
+    const int64_t vs = v < v_end ? v : v_begin;
+    const uint8_t* xp = (const uint8_t*)a.x + (vs * a.x_row_stride + hh * HALF) * ELEM;
+#pragma unroll
+    for (int k = 0; k < NRAW; ++k) raw[k] = *(const u32x4*)(xp + 16 * k);
+  };
+  int64_t tile = (int64_t)blockIdx.x * Geo::WAVES + wave;
+  u32x4 xr[NRAW];
+  if (PREFETCH && tile < ntile) fetch(tile, xr);
+
+  for (; tile < ntile; tile += wstride) {
     const int64_t vec = v_begin + tile * 32 + vl;
     const bool valid = vec < v_end;
-    const int64_t vsafe = valid ? vec : v_begin;
-
-    // ---- load this lane's d/2 inputs as MFMA B operands (bf16 hi, and lo for split inputs)
+    if constexpr (!PREFETCH) fetch(tile, xr);
     u32x4 xh[KB], xl[SPLIT_X ? KB : 1];
+    if constexpr (IN == TQ_BF16) {
+#pragma unroll
+      for (int k = 0; k < NRAW; ++k) xh[k] = xr[k];
+      if (PREFETCH && tile + wstride < ntile) fetch(tile + wstride, xr);
+    }
+
+    // ---- norm, and the MFMA B operands (bf16 hi, and lo for split inputs)
     float ss0 = 0.f, ss1 = 0.f;
     if constexpr (IN == TQ_BF16) {
-      const uint16_t* xp = (const uint16_t*)a.x + vsafe * a.x_row_stride + hh * HALF;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        xh[kb] = *(const u32x4*)(xp + 8 * kb);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           float lo = bf16_lo_to_f32(xh[kb][c]), hi = bf16_hi_to_f32(xh[kb][c]);
@@ -101,16 +128,14 @@ __global__ void __launch_bounds__(kEncWaves * 64) encode_kernel(EncodeKArgs a) {
       for (int kb = 0; kb < KB; ++kb) {
         float v[8];
         if constexpr (IN == TQ_F32) {
-          const float* xp = (const float*)a.x + vsafe * a.x_row_stride + hh * HALF + 8 * kb;
-          u32x4 p0 = *(const u32x4*)xp, p1 = *(const u32x4*)(xp + 4);
+          const u32x4 p0 = xr[2 * kb], p1 = xr[2 * kb + 1];
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             v[c] = __uint_as_float(p0[c]);
             v[4 + c] = __uint_as_float(p1[c]);
           }
         } else {
-          const uint16_t* xp = (const uint16_t*)a.x + vsafe * a.x_row_stride + hh * HALF + 8 * kb;
-          u32x4 p = *(const u32x4*)xp;
+          const u32x4 p = xr[kb];
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             v[2 * c] = f16_bits_to_f32(p[c]);
@@ -211,14 +236,13 @@ static hipError_t launch_encode_t(const EncodeLaunch& L) {
     attr_done = true;
   }
   const int cu = device_cu_count(L.rot->device);
-  const int per_cu = lds > 0 ? (int)((160 * 1024) / lds) : 2;
-  const int64_t want = (int64_t)cu * (per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu));
+  const int64_t want = (int64_t)cu * Geo::WG_PER_CU;
   int64_t bx = (want + nrot - 1) / nrot;
-  const int64_t need = (tiles + kEncWaves - 1) / kEncWaves;
+  const int64_t need = (tiles + Geo::WAVES - 1) / Geo::WAVES;
   if (bx > need) bx = need;
   if (bx < 1) bx = 1;
   dim3 grid((unsigned)bx, (unsigned)nrot);
-  hipLaunchKernelGGL((encode_kernel<D, BITS, IN>), grid, dim3(kEncWaves * 64), lds, L.stream, k);
+  hipLaunchKernelGGL((encode_kernel<D, BITS, IN>), grid, dim3(Geo::WAVES * 64), lds, L.stream, k);
   return hipGetLastError();
 }
 
