@@ -64,6 +64,12 @@ __device__ __forceinline__ T wave_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// acc + a.lo * b.lo + a.hi * b.hi for packed bf16 pairs (products exact in fp32).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
 // Two floats -> packed bf16 / fp16 pair (round to nearest even), one instruction on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -76,29 +82,5 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
 }
 
-// Number of positive decision boundaries below |z| turned into a code: for z > 0 the code
-// is L/2 + count, for z <= 0 its mirror L-1 - (L/2 + count). Equals #{k : t_k < z} except
-// exactly on a boundary. `p` holds the positive boundaries already scaled by (||x|| + eps).
-// The count is taken by binary search over the sorted boundaries (b-1 compares).
-template <int BITS>
-__device__ __forceinline__ uint32_t quantize_scaled(float z, const float* p) {
-  constexpr uint32_t H = 1u << (BITS - 1);
-  const float a = fabsf(z);
-  uint32_t u;
-  if constexpr (BITS == 2) {
-    u = H + (a > p[0] ? 1u : 0u);
-  } else if constexpr (BITS == 3) {
-    const bool c1 = a > p[1];
-    const bool c2 = a > (c1 ? p[2] : p[0]);
-    u = H + (c1 ? 2u : 0u) + (c2 ? 1u : 0u);
-  } else {
-    const bool c1 = a > p[3];
-    const float lo = c1 ? p[4] : p[0], hi = c1 ? p[6] : p[2];
-    const bool c2 = a > (c1 ? p[5] : p[1]);
-    const bool c3 = a > (c2 ? hi : lo);
-    u = H + (c1 ? 4u : 0u) + (c2 ? 2u : 0u) + (c3 ? 1u : 0u);
-  }
-  return z > 0.0f ? u : (u ^ (2u * H - 1u));
-}
 
 }  // namespace tq

@@ -17,9 +17,13 @@
 // Precision: a code must match the float64 definition except within 1e-5 of a decision
 // boundary. One bf16 pass perturbs y by ~1e-4, so Pi is split into bf16 hi + lo (16
 // significant bits, error ~1e-6): bf16 inputs are exact and take 2 passes; float32 and
-// float16 inputs are split too and take 3 (Pi_hi x_hi + Pi_lo x_hi + Pi_hi x_lo). Instead of
-// dividing every coordinate by (n + 1e-8), the positive boundaries are scaled by it once per
-// vector and compared with the unnormalized Pi x.
+// float16 inputs are split too and take 3 (Pi_hi x_hi + Pi_lo x_hi + Pi_hi x_lo).
+//
+// Quantization: one FMA maps the unnormalized Pi x to f = y * s + o (y = Pi x / (n + 1e-8), the
+// per-vector factor s / (n + 1e-8) computed once), and a 128-entry LDS table indexed by
+// floor(f), whose bins each hold at most one decision boundary, gives the code as
+// base + (f > boundary) = #{k : t_k < y}: about 6 VALU instructions per coordinate where a
+// compare chain over the 2^b - 1 boundaries costs 15-20.
 #include "device_common.h"
 #include "tq_internal.h"
 
@@ -34,7 +38,8 @@ struct EncodeKArgs {
   float* norms;
   const int64_t* slot;
   int64_t n, vpr;
-  float pos_t[8];
+  float lut_scale, lut_off;
+  uint32_t lut[kLutBins];
 };
 
 
@@ -49,29 +54,40 @@ struct EncGeo {
   static constexpr int G = (CHUNK % 16 == 0 && ROW % 16 == 0) ? 16 : ((CHUNK % 8 == 0 && ROW % 8 == 0) ? 8 : 4);
   static constexpr int FRAG_U4 = 2 * T * KB * 64;  // hi and lo tiles, u32x4 per lane
   static constexpr bool LDS = (D <= 128);
-  // Occupancy plan: at d=128 the 64 KiB of Pi tiles allow one workgroup per CU, so it has 12
-  // waves (3 per SIMD, up to 168 VGPRs: room for a prefetched tile); d=64 fits two 8-wave
-  // workgroups per CU; d=256 reads Pi from L2 and runs 8 waves.
-  static constexpr int WAVES = D == 128 ? 12 : 8;
-  static constexpr int WPE = D == 128 ? 3 : (D == 64 ? 4 : 2);
-  static constexpr int WG_PER_CU = D == 64 ? 2 : 1;
+  // Occupancy plan: at d <= 128, two 8-wave workgroups per CU (2 x 64 KiB of Pi tiles in LDS),
+  // i.e. 4 waves per SIMD within 128 VGPRs; d=256 reads Pi from L2 and needs up to 256 VGPRs,
+  // so one 8-wave workgroup (2 waves per SIMD).
+  static constexpr int WG_PER_CU = D == 256 ? 1 : 2;
 };
+template <int D, int IN>
+constexpr int enc_waves() { return 8; }
+template <int D, int IN>
+constexpr int enc_wpe() { return D == 256 ? 2 : 4; }
 
 template <int D, int BITS, int IN>
-__global__ void __launch_bounds__((EncGeo<D, BITS>::WAVES * 64))
-__attribute__((amdgpu_waves_per_eu(EncGeo<D, BITS>::WPE)))
+__global__ void __launch_bounds__((enc_waves<D, IN>() * 64))
+__attribute__((amdgpu_waves_per_eu(enc_wpe<D, IN>())))
 encode_kernel(EncodeKArgs a) {
   using Geo = EncGeo<D, BITS>;
   constexpr int T = Geo::T, KB = Geo::KB, HALF = Geo::HALF;
   constexpr bool SPLIT_X = (IN != TQ_BF16);
+  constexpr int WAVES = enc_waves<D, IN>();
   extern __shared__ u32x4 smem[];
+  __shared__ uint32_t lut[kLutBins];
 
   const int r = blockIdx.y;
   const u32x4* gfrag = a.frag + (int64_t)r * a.frag_stride;
   if constexpr (Geo::LDS) {
     for (int i = threadIdx.x; i < Geo::FRAG_U4; i += blockDim.x) smem[i] = gfrag[i];
-    __syncthreads();
   }
+  {
+    // read the table straight from the kernel-argument segment (the only argument is `a`, at
+    // offset 0): indexing the by-value copy would spill the whole struct to scratch
+    const uint32_t* klut = (const uint32_t*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+                                             offsetof(EncodeKArgs, lut));
+    for (int i = threadIdx.x; i < kLutBins; i += blockDim.x) lut[i] = klut[i];
+  }
+  __syncthreads();
   // Tile reads go through an offset the compiler cannot prove loop-invariant; otherwise it
   // hoists every tile of Pi into registers and spills.
   const char* abase = Geo::LDS ? (const char*)smem : (const char*)gfrag;
@@ -87,8 +103,8 @@ encode_kernel(EncodeKArgs a) {
   // wave keeps a tile of loads in flight while it rotates and quantizes the previous one.
   constexpr int ELEM = IN == TQ_F32 ? 4 : 2;
   constexpr int NRAW = HALF * ELEM / 16;
-  constexpr bool PREFETCH = (IN == TQ_BF16) && D <= 128;
-  const int64_t wstride = (int64_t)gridDim.x * Geo::WAVES;
+  constexpr bool PREFETCH = (IN == TQ_BF16);
+  const int64_t wstride = (int64_t)gridDim.x * WAVES;
   auto fetch = [&](int64_t tl, u32x4 (&raw)[NRAW]) {
     const int64_t v = v_begin + tl * 32 + vl;
     const int64_t vs = v < v_end ? v : v_begin;
@@ -96,7 +112,7 @@ encode_kernel(EncodeKArgs a) {
 #pragma unroll
     for (int k = 0; k < NRAW; ++k) raw[k] = *(const u32x4*)(xp + 16 * k);
   };
-  int64_t tile = (int64_t)blockIdx.x * Geo::WAVES + wave;
+  int64_t tile = (int64_t)blockIdx.x * WAVES + wave;
   u32x4 xr[NRAW];
   if (PREFETCH && tile < ntile) fetch(tile, xr);
 
@@ -114,14 +130,13 @@ encode_kernel(EncodeKArgs a) {
     // ---- norm, and the MFMA B operands (bf16 hi, and lo for split inputs)
     float ss0 = 0.f, ss1 = 0.f;
     if constexpr (IN == TQ_BF16) {
+      // sum of squares two elements per instruction (bf16 products are exact in fp32)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float lo = bf16_lo_to_f32(xh[kb][c]), hi = bf16_hi_to_f32(xh[kb][c]);
-          ss0 = fmaf(lo, lo, ss0);
-          ss1 = fmaf(hi, hi, ss1);
-        }
+        ss0 = dot2_bf16(xh[kb][0], xh[kb][0], ss0);
+        ss1 = dot2_bf16(xh[kb][1], xh[kb][1], ss1);
+        ss0 = dot2_bf16(xh[kb][2], xh[kb][2], ss0);
+        ss1 = dot2_bf16(xh[kb][3], xh[kb][3], ss1);
       }
     } else {
 #pragma unroll
@@ -157,10 +172,9 @@ encode_kernel(EncodeKArgs a) {
     float ss = ss0 + ss1;
     ss += wave_xor(ss, 32);            // the other half of the same vector
     const float nrm = sqrtf(ss);
-    const float scale = nrm + 1e-8f;
-    float p[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = a.pos_t[j] * scale;
+    // f = y * lut_scale + lut_off with y = z / (n + 1e-8): one FMA per coordinate
+    const float fs = a.lut_scale / (nrm + 1e-8f);
+    const float foff = a.lut_off;
 
     // ---- rotate tile by tile, quantize, pack into this lane's chunk
     uint32_t aoff = (uint32_t)lane * 16u;
@@ -170,9 +184,14 @@ encode_kernel(EncodeKArgs a) {
     for (int w = 0; w < Geo::CHUNK_DW; ++w) pk[w] = 0u;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
+      // a fresh opaque offset per tile: the scheduler cannot pull later tiles' Pi reads ahead
+      // (all 4 tiles' operands at once would not fit in registers)
+      asm volatile("" : "+v"(aoff));
       f32x16 acc = {};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
+        // Pi tiles read from L2 (d=256) are fenced in groups of 4 K blocks for the same reason
+        if (!Geo::LDS && kb % 4 == 0 && kb > 0) asm volatile("" : "+v"(aoff));
         const u32x4 ahi = *(const u32x4*)(abase + aoff + ((0 * T + t) * KB + kb) * 1024);
         const u32x4 alo = *(const u32x4*)(abase + aoff + ((1 * T + t) * KB + kb) * 1024);
         acc = mfma32_bf16(ahi, xh[kb], acc);
@@ -181,11 +200,20 @@ encode_kernel(EncodeKArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t code = quantize_scaled<BITS>(acc[i], p);
+        const float f = fmaf(acc[i], fs, foff);
+        const uint32_t e = lut[(uint32_t)f];
+        const uint32_t code = (e & 15u) + (f > __uint_as_float(e) ? 1u : 0u);
         const int pos = (16 * t + i) * BITS;
         pk[pos >> 5] |= code << (pos & 31);
         if ((pos & 31) + BITS > 32) pk[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+        // table reads in groups of 8: all 16 in flight at once would not fit in registers
+        if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       }
+      // finish this tile's packed words here: left alone, the compiler sinks the packing to the
+      // store and keeps every table entry of the vector live until then
+#pragma unroll
+      for (int w = (16 * t * BITS) >> 5; w <= ((16 * t + 16) * BITS - 1) >> 5; ++w)
+        asm volatile("" : "+v"(pk[w]));
     }
 
     // ---- store
@@ -223,7 +251,9 @@ static hipError_t launch_encode_t(const EncodeLaunch& L) {
   k.slot = L.slot_mapping;
   k.n = L.n;
   k.vpr = L.vectors_per_rot;
-  for (int j = 0; j < 8; ++j) k.pos_t[j] = L.lv.pos_thresholds[j];
+  k.lut_scale = L.lv.lut.scale;
+  k.lut_off = L.lv.lut.offset;
+  for (int j = 0; j < kLutBins; ++j) k.lut[j] = L.lv.lut.entry[j];
   const int64_t per_rot = L.vectors_per_rot ? L.vectors_per_rot : L.n;
   const int nrot = L.vectors_per_rot ? (int)((L.n + L.vectors_per_rot - 1) / L.vectors_per_rot) : 1;
   const int64_t tiles = (per_rot + 31) / 32;
@@ -235,14 +265,15 @@ static hipError_t launch_encode_t(const EncodeLaunch& L) {
     if (e != hipSuccess) return e;
     attr_done = true;
   }
+  constexpr int WAVES = enc_waves<D, IN>();
   const int cu = device_cu_count(L.rot->device);
   const int64_t want = (int64_t)cu * Geo::WG_PER_CU;
   int64_t bx = (want + nrot - 1) / nrot;
-  const int64_t need = (tiles + Geo::WAVES - 1) / Geo::WAVES;
+  const int64_t need = (tiles + WAVES - 1) / WAVES;
   if (bx > need) bx = need;
   if (bx < 1) bx = 1;
   dim3 grid((unsigned)bx, (unsigned)nrot);
-  hipLaunchKernelGGL((encode_kernel<D, BITS, IN>), grid, dim3(Geo::WAVES * 64), lds, L.stream, k);
+  hipLaunchKernelGGL((encode_kernel<D, BITS, IN>), grid, dim3(WAVES * 64), lds, L.stream, k);
   return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -217,7 +218,35 @@ LevelArgs make_levels(const Codebook& cb) {
     const uint16_t lo = to_bf16((float)(cb.centroids[k] - (double)from_bf16(hi)));
     lv.centroid_bf16x2[k] = (uint32_t)hi | ((uint32_t)lo << 16);
   }
+  // Quantization table: bin width just under the smallest gap between boundaries, so a bin
+  // holds at most one boundary; offset = bins per side so f >= 0 for every boundary.
+  double gap = INFINITY;
+  for (int k = 0; k + 1 < L - 1; ++k) gap = std::min(gap, cb.thresholds[k + 1] - cb.thresholds[k]);
+  if (!(gap < INFINITY)) gap = 1.0;   // one boundary (1 bit): any width works
+  const double w = gap * (1.0 - 1e-3);
+  const double tmax = cb.thresholds[L - 2];
+  const int per_side = (int)std::ceil(tmax / w) + 1;
+  lv.lut.scale = (float)(1.0 / w);
+  lv.lut.offset = (float)per_side;
+  float fthr[kMaxLevels];
+  for (int k = 0; k < L - 1; ++k) fthr[k] = (float)(cb.thresholds[k] / w + per_side);
+  for (int j = 0; j < kLutBins; ++j) {
+    float thr = FLT_MAX;
+    uint32_t base = 0;
+    for (int k = 0; k < L - 1; ++k) {
+      if (fthr[k] < (float)j) ++base;
+      else if (fthr[k] < (float)(j + 1)) thr = fthr[k];
+    }
+    uint32_t tb;
+    std::memcpy(&tb, &thr, 4);
+    lv.lut.entry[j] = (tb & ~15u) | base;
+  }
   return lv;
+}
+
+bool lut_covers_unit_range(const LevelArgs& lv) {
+  // |y| <= 1 must land inside the table
+  return lv.lut.scale + lv.lut.offset + 1.0f < (float)kLutBins && lv.lut.offset >= 1.0f;
 }
 
 // ------------------------------------------------------------------------------------
@@ -562,6 +591,8 @@ int tq_encode(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors
   EncodeLaunch a;
   a.rot = &rot->rot;
   a.lv = make_levels(cb->cb);
+  if (!lut_covers_unit_range(a.lv))
+    return fail(TQ_ERR_INVALID_ARG, "tq_encode: the codebook's boundaries are too close for the quantization table");
   a.bits = cb->cb.bits;
   a.x_dtype = x_dtype;
   a.vectors_per_rot = vectors_per_rot;

@@ -37,15 +37,28 @@ struct Rotation {
   const float* f32(int r) const { return (const float*)((const uint8_t*)dev + f32_off + (size_t)r * f32_stride); }
 };
 
+// Quantization table for the encode. With f = y * scale + offset (y the rotated, normalized
+// coordinate), bin = floor(f) holds at most one decision boundary: code = base[bin] + (f > thr[bin]),
+// which equals #{k : t_k < y}. Bins cover f in [0, kLutBins) for |y| <= 1. An entry is the
+// float bits of thr (FLT_MAX if the bin has no boundary) with its 4 low mantissa bits replaced by
+// base: thr moves by < 2^-19 of f, i.e. < 3e-6 of y, inside the 1e-5 parity window.
+constexpr int kLutBins = 128;
+struct QuantLut {
+  float scale, offset;
+  uint32_t entry[kLutBins];
+};
+
 // Levels passed to kernels by value.
 struct LevelArgs {
   float pos_thresholds[kMaxLevels / 2];   // t_{L/2+1} .. t_{L-1}: positive decision boundaries
   uint16_t centroid_f16[kMaxLevels];      // c_k as fp16 bits
   uint32_t centroid_bf16x2[kMaxLevels];   // c_k = hi + lo as bf16 bits: hi | lo << 16
   float centroid_f32[kMaxLevels];
+  QuantLut lut;
 };
 
 LevelArgs make_levels(const Codebook& cb);
+bool lut_covers_unit_range(const LevelArgs& lv);
 
 void set_error(const std::string& msg);
 
