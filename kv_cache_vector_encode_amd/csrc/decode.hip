@@ -26,6 +26,7 @@ struct DecodeKArgs {
 };
 
 constexpr int kDecWaves = 8;
+constexpr int kStageBytes = 4096;   // per-wave output staging buffer
 
 template <int D, int BITS>
 struct DecGeo {
@@ -35,7 +36,22 @@ struct DecGeo {
   static constexpr int CHUNK_DW = CHUNK / 4;
   static constexpr int G = (CHUNK % 16 == 0 && ROW % 16 == 0) ? 16 : ((CHUNK % 8 == 0 && ROW % 8 == 0) ? 8 : 4);
   static constexpr int FRAG_U4 = T * KB * 64;
+  // Code -> centroid table: 2-bit codes go four at a time (one byte -> four fp16), 3- and 4-bit
+  // codes two at a time (6 or 8 bits -> two fp16).
+  static constexpr int PER_LOOKUP = BITS == 2 ? 4 : 2;
+  static constexpr int TAB_N = 1 << (PER_LOOKUP * BITS);
+  static constexpr int TAB_WORDS = TAB_N * PER_LOOKUP / 2;
+  // Outputs are staged through LDS so that stores go out as 64-byte runs (d <= 128; at d=256
+  // the Pi^T tiles fill LDS and lanes store their own 16-byte pieces).
+  static constexpr bool STAGE = D <= 128;
+  static constexpr size_t lds_bytes() {
+    return (size_t)FRAG_U4 * 16 + (STAGE ? (size_t)kDecWaves * kStageBytes : 0);
+  }
 };
+
+// 16-byte chunk c of a wave's staging buffer lives at chunk c ^ ((c >> 4) & 7): the 16 lanes
+// that write (chunk stride 8) or read (stride 1) together then hit 16 distinct bank groups.
+__device__ __forceinline__ uint32_t stage_swizzle(uint32_t c) { return c ^ ((c >> 4) & 7u); }
 
 template <int D, int BITS, int OUT>
 __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
@@ -43,12 +59,26 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
   constexpr int T = Geo::T, KB = Geo::KB, HALF = Geo::HALF;
   constexpr uint32_t MASK = (1u << BITS) - 1u;
   extern __shared__ u32x4 smem[];
-  __shared__ uint16_t ctab[16];
+  __shared__ uint32_t tab[Geo::TAB_WORDS];
 
   const int r = blockIdx.y;
   const u32x4* gfrag = a.frag + (int64_t)r * a.frag_stride;
   for (int i = threadIdx.x; i < Geo::FRAG_U4; i += blockDim.x) smem[i] = gfrag[i];
-  if (threadIdx.x < 16) ctab[threadIdx.x] = (uint16_t)(a.ctab[threadIdx.x >> 1] >> (16 * (threadIdx.x & 1)));
+  {
+    // centroids straight from the kernel-argument segment (indexing the by-value copy with a
+    // lane-dependent index would go through scratch)
+    const uint32_t* kc = (const uint32_t*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+                                           offsetof(DecodeKArgs, ctab));
+    auto cent = [&](uint32_t k) -> uint32_t { return (kc[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
+    for (int j = threadIdx.x; j < Geo::TAB_N; j += blockDim.x) {
+      if constexpr (Geo::PER_LOOKUP == 4) {
+        tab[2 * j] = cent(j & MASK) | (cent((j >> BITS) & MASK) << 16);
+        tab[2 * j + 1] = cent((j >> (2 * BITS)) & MASK) | (cent(j >> (3 * BITS)) << 16);
+      } else {
+        tab[j] = cent(j & MASK) | (cent(j >> BITS) << 16);
+      }
+    }
+  }
   __syncthreads();
 
   const int64_t v_begin = a.vpr ? (int64_t)r * a.vpr : 0;
@@ -56,6 +86,7 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
   const int64_t ntile = (v_end - v_begin + 31) / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vl = lane & 31, hh = lane >> 5;
+  uint8_t* stg = (uint8_t*)(smem + Geo::FRAG_U4) + wave * kStageBytes;
 
   // Two-stage prefetch: the packed row of the next tile is loaded while this tile is decoded,
   // and with a slot gather the slot index is read one tile earlier still.
@@ -98,8 +129,8 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
   int64_t row_nn = row_of(tile + wstride);
 
   for (; tile < ntile; tile += wstride) {
-    const int64_t vec = v_begin + tile * 32 + vl;
-    const bool valid = vec < v_end;
+    const int64_t vbase = v_begin + tile * 32;
+    const int64_t vec = vbase + vl;
     uint32_t cw[Geo::CHUNK_DW];
 #pragma unroll
     for (int w = 0; w < Geo::CHUNK_DW; ++w) cw[w] = cwn[w];
@@ -107,53 +138,87 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
     fetch(row_nn, cwn, nrmn);
     row_nn = row_of(tile + 2 * wstride);
 
-    // ---- codes -> fp16 centroids, 8 per K block
+    // ---- codes -> fp16 centroids, 8 per K block (the lane's codes 8kb .. 8kb+7)
     u32x4 bfrag[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      if constexpr (BITS == 2) {
+        // 8 codes = 16 bits = two table bytes, four fp16 each
+        const uint32_t bits16 = cw[kb >> 1] >> (16 * (kb & 1));
+        const u32x2 q0 = *(const u32x2*)&tab[2 * (bits16 & 255u)];
+        const u32x2 q1 = *(const u32x2*)&tab[2 * ((bits16 >> 8) & 255u)];
+        bfrag[kb] = u32x4{q0[0], q0[1], q1[0], q1[1]};
+      } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t h2[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int pos = (8 * kb + 2 * c + s) * BITS;
-          uint32_t code = (cw[pos >> 5] >> (pos & 31));
-          if ((pos & 31) + BITS > 32) code |= cw[(pos >> 5) + 1] << (32 - (pos & 31));
-          h2[s] = ctab[code & MASK];
+        for (int c = 0; c < 4; ++c) {
+          constexpr int PB = 2 * BITS;           // bits per code pair
+          const int pos = (4 * kb + c) * PB;     // compile-time after unrolling
+          uint32_t idx;
+          if ((pos & 31) + PB <= 32)
+            idx = cw[pos >> 5] >> (pos & 31);
+          else
+            idx = funnel(cw[(pos >> 5) + 1], cw[pos >> 5], pos & 31);
+          bfrag[kb][c] = tab[idx & ((1u << PB) - 1u)];
         }
-        bfrag[kb][c] = h2[0] | (h2[1] << 16);
       }
     }
 
-    // ---- inverse rotation and store (an opaque offset keeps the Pi^T tiles in LDS instead of
-    //      letting the compiler hoist all of them into registers)
+    // ---- inverse rotation (an opaque offset keeps the Pi^T tiles in LDS instead of letting
+    //      the compiler hoist all of them into registers)
     uint32_t aoff = (uint32_t)lane * 16u;
     asm volatile("" : "+v"(aoff));
-    const bool store = valid;
+    constexpr int E = OUT == TQ_F32 ? 4 : 2;   // output bytes per element
+    constexpr int CPT = E;                     // 16-byte chunks per lane per tile (16 outputs)
+    constexpr int S = 4 / CPT;                 // tiles per 64-byte run of one half vector
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       f32x16 acc = {};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
         acc = mfma32_f16(*(const u32x4*)((const char*)smem + aoff + (t * KB + kb) * 1024), bfrag[kb], acc);
-      if (store) {
-        const int64_t base = vec * D + hh * HALF + 16 * t;
-        if constexpr (OUT == TQ_F32) {
-          float* o = (float*)a.out + base;
+      // scaled outputs of coordinates hh*d/2 + 16t .. +16 as CPT 16-byte chunks
+      u32x4 ch[CPT];
+      if constexpr (OUT == TQ_F32) {
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *(f32x4*)(o + 4 * q4) =
-                f32x4{acc[4 * q4] * nrm, acc[4 * q4 + 1] * nrm, acc[4 * q4 + 2] * nrm, acc[4 * q4 + 3] * nrm};
-        } else {
-          uint32_t w[8];
+        for (int q4 = 0; q4 < 4; ++q4)
+          ch[q4] = u32x4{__float_as_uint(acc[4 * q4] * nrm), __float_as_uint(acc[4 * q4 + 1] * nrm),
+                         __float_as_uint(acc[4 * q4 + 2] * nrm), __float_as_uint(acc[4 * q4 + 3] * nrm)};
+      } else {
+        uint32_t w[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float lo = acc[2 * j] * nrm, hi = acc[2 * j + 1] * nrm;
-            w[j] = OUT == TQ_BF16 ? pack_bf16x2(lo, hi) : pack_f16x2(lo, hi);
+        for (int j = 0; j < 8; ++j) {
+          const float lo = acc[2 * j] * nrm, hi = acc[2 * j + 1] * nrm;
+          w[j] = OUT == TQ_BF16 ? pack_bf16x2(lo, hi) : pack_f16x2(lo, hi);
+        }
+        ch[0] = u32x4{w[0], w[1], w[2], w[3]};
+        ch[1] = u32x4{w[4], w[5], w[6], w[7]};
+      }
+      if constexpr (Geo::STAGE) {
+        // piece p = 2 v + hh holds 64 bytes of one half vector: tiles t0 .. t0+S-1
+        const uint32_t c0 = 4u * (2u * vl + hh) + (t % S) * CPT;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) *(u32x4*)(stg + 16 * stage_swizzle(c0 + k)) = ch[k];
+        if (t % S == S - 1) {
+          // the wave's LDS operations run in order, so its own writes above are visible here;
+          // each group of 4 lanes then writes one 64-byte run
+          const int t0 = t - (S - 1);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t c = 64u * j + lane;
+            const u32x4 q = *(const u32x4*)(stg + 16 * stage_swizzle(c));
+            const uint32_t p = c >> 2;
+            const int64_t pv = vbase + (p >> 1);
+            if (pv < v_end) {
+              uint8_t* dst = (uint8_t*)a.out + (pv * D + (p & 1) * HALF + 16 * t0) * E + (c & 3) * 16;
+              *(u32x4*)dst = q;
+            }
           }
-          uint16_t* o = (uint16_t*)a.out + base;
-          *(u32x4*)o = u32x4{w[0], w[1], w[2], w[3]};
-          *(u32x4*)(o + 8) = u32x4{w[4], w[5], w[6], w[7]};
+        }
+      } else {
+        if (vec < v_end) {
+          uint8_t* dst = (uint8_t*)a.out + (vec * D + hh * HALF + 16 * t) * E;
+#pragma unroll
+          for (int k = 0; k < CPT; ++k) *(u32x4*)(dst + 16 * k) = ch[k];
         }
       }
     }
@@ -177,7 +242,7 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
   const int64_t per_rot = L.vectors_per_rot ? L.vectors_per_rot : L.n;
   const int nrot = L.vectors_per_rot ? (int)((L.n + L.vectors_per_rot - 1) / L.vectors_per_rot) : 1;
   const int64_t tiles = (per_rot + 31) / 32;
-  const size_t lds = Geo::FRAG_U4 * sizeof(u32x4);
+  const size_t lds = Geo::lds_bytes();
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<D, BITS, OUT>,
@@ -186,8 +251,8 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
     attr_done = true;
   }
   const int cu = device_cu_count(L.rot->device);
-  // workgroups per CU: LDS-limited at d=256 (128 KiB of tiles), else up to 3 (24 waves)
-  int per_cu = (int)((160 * 1024 - 256) / lds);
+  // workgroups per CU: as many as LDS holds (tiles, staging and the 2 KiB table), at most 3
+  int per_cu = (int)((160 * 1024) / (lds + 2048));
   per_cu = per_cu < 1 ? 1 : (per_cu > 3 ? 3 : per_cu);
   const int64_t want = (int64_t)cu * per_cu;
   int64_t bx = (want + nrot - 1) / nrot;
