@@ -40,6 +40,7 @@ struct AttnKArgs {
   const int32_t* block_table;
   float* scores;
   float* part;
+  float* sink;         // where masked lanes store scores (>= 64 floats)
   int32_t max_seq_len, block_size, bs_shift, mbps;
   int32_t B, Hq, Hkv, G, s_eff;
   float scale;
@@ -49,64 +50,114 @@ struct AttnKArgs {
 
 constexpr int kAttnWaves = 4;
 
-__device__ __forceinline__ int64_t token_row(const AttnKArgs& a, int b, int kvh, int t) {
-  if (a.block_table) {
-    int blk, off;
-    if (a.bs_shift >= 0) {
-      blk = t >> a.bs_shift;
-      off = t & (a.block_size - 1);
-    } else {
-      blk = t / a.block_size;
-      off = t - blk * a.block_size;
-    }
-    const int phys = a.block_table[(int64_t)b * a.mbps + blk];
-    return ((int64_t)phys * a.Hkv + kvh) * a.block_size + off;
-  }
-  return ((int64_t)b * a.Hkv + kvh) * a.max_seq_len + t;
-}
+// Cache addressing: 0 = dense, 1 = paged with a power-of-two block size >= 16 (a 32-token
+// block then spans at most two pages, looked up once per block), 2 = any other paging.
+enum AttnPaging { kDense = 0, kPagedPow2 = 1, kPagedAny = 2 };
 
-// NBITS bits starting at bit `off` of a row of ROW_DW dwords, shifted down to bit 0.
-template <int NBITS, int ROW_DW, bool ALIGNED>
-__device__ __forceinline__ void load_bits(const uint32_t* row, int off, uint32_t (&out)[(NBITS + 31) / 32]) {
-  constexpr int NW = (NBITS + 31) / 32;
-  const int idx = off >> 5;
-  if constexpr (ALIGNED) {
+// NB bits of a packed row starting at bit `bitoff`, shifted down to bit 0 of out[0]. Loads are
+// unconditional and stay inside the row of ROWB bytes.
+template <int NB, int ROWB>
+__device__ __forceinline__ void load_chunk(const uint8_t* row, int bitoff, uint32_t (&out)[(NB + 31) / 32]) {
+  constexpr int NW = (NB + 31) / 32;
+  if constexpr (NB % 32 == 0) {
+    // bitoff is a multiple of NB here, so the chunk is NB/8-byte aligned
+    const uint8_t* p = row + bitoff / 8;
+    if constexpr (NW == 4) {
+      const u32x4 v = *(const u32x4*)p;
+      out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+    } else if constexpr (NW == 2) {
+      const u32x2 v = *(const u32x2*)p;
+      out[0] = v[0]; out[1] = v[1];
+    } else {
 #pragma unroll
-    for (int k = 0; k < NW; ++k) out[k] = row[idx + k];
+      for (int k = 0; k < NW; ++k) out[k] = ((const uint32_t*)p)[k];
+    }
+  } else if constexpr (NB == 16) {
+    out[0] = *(const uint16_t*)(row + bitoff / 8);
+  } else if constexpr (NB == 8) {
+    out[0] = row[bitoff / 8];
   } else {
-    const int sh = off & 31;
+    constexpr int ROW_DW = ROWB / 4;
+    const uint32_t* rw = (const uint32_t*)row;
+    const int idx = bitoff >> 5;
+    const uint32_t sh = (uint32_t)bitoff & 31u;
     uint32_t w[NW + 1];
 #pragma unroll
-    for (int k = 0; k <= NW; ++k) w[k] = (idx + k < ROW_DW) ? row[idx + k] : 0u;
+    for (int k = 0; k <= NW; ++k) w[k] = rw[min(idx + k, ROW_DW - 1)];   // a clamped word only feeds bits past NB
 #pragma unroll
-    for (int k = 0; k < NW; ++k) out[k] = funnel(w[k + 1], w[k], (uint32_t)sh);
+    for (int k = 0; k < NW; ++k) out[k] = funnel(w[k + 1], w[k], sh);
   }
 }
 
-template <int BITS, int NW>
-__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[NW], int idx) {
-  const int pos = idx * BITS;
-  uint32_t c = w[pos >> 5] >> (pos & 31);
-  if ((pos & 31) + BITS > 32) c |= w[(pos >> 5) + 1] << (32 - (pos & 31));
-  return c & ((1u << BITS) - 1u);
+// PB bits at bit `pos` of w (pos is a compile-time constant after unrolling)
+template <int PB, int NW>
+__device__ __forceinline__ uint32_t bits_at(const uint32_t (&w)[NW], int pos) {
+  uint32_t v;
+  if ((pos & 31) + PB <= 32)
+    v = w[pos >> 5] >> (pos & 31);
+  else
+    v = funnel(w[(pos >> 5) + 1], w[pos >> 5], (uint32_t)(pos & 31));
+  return v & ((1u << PB) - 1u);
 }
 
-template <int D, int BK, int BV, bool SCORES>
-__global__ void __launch_bounds__(kAttnWaves * 64) attn_kernel(AttnKArgs a) {
+// a, b: up to eight 2-bit codes each (low 16 bits). Returns z with nibble t = a_t | b_t << 2,
+// so byte j of z holds codes 2j and 2j+1 of both (bytes of a and b interleaved, then two
+// swaps of bit fields inside each 16-bit half).
+__device__ __forceinline__ uint32_t interleave2(uint32_t a, uint32_t b) {
+  uint32_t y = (a & 0xffu) | ((b & 0xffu) << 8) | ((a & 0xff00u) << 8) | ((b & 0xff00u) << 16);
+  uint32_t t = (y ^ (y >> 4)) & 0x00f000f0u;
+  y ^= t ^ (t << 4);
+  t = (y ^ (y >> 2)) & 0x0c0c0c0cu;
+  y ^= t ^ (t << 2);
+  return y;
+}
+
+// register budget: waves per SIMD 4 at d=64 (<= 128 registers), 3 at d=128 (<= 168), 2 at
+// d=256 (twice the accumulators)
+template <int D>
+constexpr int attn_wpe() { return D == 256 ? 2 : D == 128 ? 3 : 4; }
+
+template <int D, int BK, int BV, bool SCORES, int PAGE>
+__global__ void __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(attn_wpe<D>())))
+attn_kernel(AttnKArgs a) {
   constexpr int KB = D / 32;            // K blocks of the score MFMA
   constexpr int TV = D / 16;            // output tiles of the P.V MFMA
   constexpr int NBK = D * BK / 4;       // bits of a lane's K chunk
   constexpr int NBV = D * BV / 16;      // bits of a lane's V segment
   constexpr int NWK = (NBK + 31) / 32, NWV = (NBV + 31) / 32;
-  constexpr int ROWK_DW = D * BK / 32, ROWV_DW = D * BV / 32;
-  constexpr bool ALK = (NBK % 32) == 0, ALV = (NBV % 32) == 0;
-  __shared__ uint32_t ctk[16];
-  __shared__ uint16_t ctv[16];
-  if (threadIdx.x < 16) {
-    ctk[threadIdx.x] = a.ctk[threadIdx.x];
-    ctv[threadIdx.x] = (uint16_t)(a.ctv[threadIdx.x >> 1] >> (16 * (threadIdx.x & 1)));
+  constexpr int ROWK = D * BK / 8, ROWV = D * BV / 8;
+  constexpr int PK = 2 * BK;            // bits of a pair of K codes
+  constexpr int KTAB = 1 << PK;
+  constexpr int VTAB = BV == 2 ? 512 : (1 << (2 * BV));
+  // Code -> operand tables: a pair of K codes -> two bf16 hi (tkh) / lo (tkl) halves; for
+  // 2-bit V a byte of interleaved codes (two coordinates of two tokens) -> two fp16 pairs,
+  // else a pair of V codes (one coordinate of two tokens) -> one fp16 pair.
+  __shared__ uint32_t tkh[KTAB], tkl[KTAB];
+  __shared__ uint32_t tv[SCORES ? 1 : VTAB];
+  __shared__ u32x4 sq[2 * KB * 64];   // query B operands [hi, lo][kb][lane], shared by the waves
+  {
+    // centroids straight from the kernel-argument segment (`a` is the only argument)
+    const char* ka = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+    const uint32_t* kk = (const uint32_t*)(ka + offsetof(AttnKArgs, ctk));
+    const uint32_t* kv = (const uint32_t*)(ka + offsetof(AttnKArgs, ctv));
+    constexpr uint32_t MK = (1u << BK) - 1u, MV = (1u << BV) - 1u;
+    for (int j = threadIdx.x; j < KTAB; j += blockDim.x) {
+      const uint32_t c0 = kk[j & MK], c1 = kk[j >> BK];
+      tkh[j] = (c0 & 0xffffu) | (c1 << 16);
+      tkl[j] = (c0 >> 16) | (c1 & 0xffff0000u);
+    }
+    if constexpr (!SCORES) {
+      auto cv = [&](uint32_t k) -> uint32_t { return (kv[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
+      if constexpr (BV == 2) {
+        for (int j = threadIdx.x; j < 256; j += blockDim.x) {
+          tv[2 * j] = cv(j & 3u) | (cv((j >> 2) & 3u) << 16);
+          tv[2 * j + 1] = cv((j >> 4) & 3u) | (cv((uint32_t)j >> 6) << 16);
+        }
+      } else {
+        for (int j = threadIdx.x; j < VTAB; j += blockDim.x) tv[j] = cv(j & MV) | (cv((uint32_t)j >> BV) << 16);
+      }
+    }
   }
-  __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.z, kvh = blockIdx.y;
@@ -116,6 +167,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_kernel(AttnKArgs a) {
   const int per = (nblk + a.s_eff - 1) / a.s_eff;
   const int start = sidx * per * 32;
   const int end = min(len, start + per * 32);
+  const int last = end - 1;
   const int n16 = lane & 15, q4 = lane >> 4;
   const bool head_ok = n16 < a.G;
   const int h = kvh * a.G + (head_ok ? n16 : 0);
@@ -124,8 +176,8 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_kernel(AttnKArgs a) {
   //      q'[h][q4*d/4 + 8kb + e] / qmax for kb < KB, e < 8, split into bf16 hi + lo. Scores
   //      take three bf16 passes (q_hi c_hi + q_hi c_lo + q_lo c_hi, ~2^-17 relative): with
   //      large logits (outlier tokens) softmax turns score errors into weight errors, so fp16
-  //      (2^-11) operands are not enough there.
-  u32x4 bqh[KB], bql[KB];
+  //      (2^-11) operands are not enough there. All waves of the workgroup serve the same
+  //      (sequence, KV head); wave 0 leaves the operands in LDS and the loop reads them there.
   float qmax;
   {
     float qv[D / 4];
@@ -148,10 +200,13 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_kernel(AttnKArgs a) {
         const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
         const uint32_t l0 = f32_to_bf16_bits(v0 - bf16_bits_to_f32(h0));
         const uint32_t l1 = f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1));
-        bqh[kb][c] = h0 | (h1 << 16);
-        bql[kb][c] = l0 | (l1 << 16);
+        if (wave == 0) {
+          ((uint32_t*)&sq[kb * 64 + lane])[c] = h0 | (h1 << 16);
+          ((uint32_t*)&sq[(KB + kb) * 64 + lane])[c] = l0 | (l1 << 16);
+        }
       }
   }
+  __syncthreads();
   const float sc = qmax * a.scale;
 
   float m_run = -INFINITY, l_run = 0.f, n_run = 0.f;
@@ -162,151 +217,185 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_kernel(AttnKArgs a) {
   // ---- operands of one 32-token block, fetched one block ahead of their use. This lane
   //      needs the K codes of token t0 + 16*tile + n16 (score A operand row n16) and, for the
   //      8 tokens tok(e) = t0 + (e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4) whose scores land in
-  //      it and whose weights it supplies to P.V, their K norms, V norms and V codes.
-  struct Blk {
+  //      it and whose weights it supplies to P.V, their K norms, V norms and V codes. Tokens
+  //      past the end are clamped to the last one (and masked later): every load is issued
+  //      unconditionally, so the in-order memory counter waits only for what is needed.
+  struct KBlk {
     uint32_t kc[2][NWK];
-    float kn[8], vn[8];
-    uint32_t seg[8][NWV];
   };
-  const bool paged = a.block_table != nullptr;
-  const bool fastpage = paged && a.bs_shift >= 4;   // a 32-token block then spans <= 2 pages
+  struct VBlk {
+    float kn[8], vn[SCORES ? 1 : 8];
+    uint32_t seg[SCORES ? 1 : 8][NWV];
+  };
   const int64_t dense_base = ((int64_t)b * a.Hkv + kvh) * a.max_seq_len;
-  const int32_t* btab = paged ? a.block_table + (int64_t)b * a.mbps : nullptr;
+  const int32_t* btab = a.block_table + (int64_t)b * a.mbps;
   auto pages = [&](int t0, int& p0, int& p1) {
-    p0 = p1 = 0;
-    if (fastpage && t0 < end) {
-      p0 = btab[t0 >> a.bs_shift];
-      p1 = btab[min(t0 + 31, end - 1) >> a.bs_shift];
+    if constexpr (PAGE == kPagedPow2) {
+      p0 = btab[min(t0, last) >> a.bs_shift];
+      p1 = btab[min(t0 + 31, last) >> a.bs_shift];
+    } else {
+      p0 = p1 = 0;
     }
   };
   auto row_of = [&](int tt, int t0, int p0, int p1) -> int64_t {
-    if (!paged) return dense_base + tt;
-    if (fastpage) {
+    if constexpr (PAGE == kDense) {
+      return dense_base + tt;
+    } else if constexpr (PAGE == kPagedPow2) {
       const int phys = ((tt >> a.bs_shift) == (t0 >> a.bs_shift)) ? p0 : p1;
       return (((int64_t)phys * a.Hkv + kvh) << a.bs_shift) + (tt & (a.block_size - 1));
+    } else {
+      const int blk = tt / a.block_size;
+      return ((int64_t)btab[blk] * a.Hkv + kvh) * a.block_size + (tt - blk * a.block_size);
     }
-    const int blk = tt / a.block_size;
-    return ((int64_t)btab[blk] * a.Hkv + kvh) * a.block_size + (tt - blk * a.block_size);
   };
-  auto fetch = [&](int t0, int p0, int p1, Blk& B) {
+  auto tok = [&](int t0, int e) { return min(t0 + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4)), last); };
+  auto fetch_k = [&](int t0, int p0, int p1, KBlk& B) {
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      const int tk = t0 + 16 * tile + n16;
-      if (tk < end) {
-        const uint32_t* row = (const uint32_t*)(a.kp + row_of(tk, t0, p0, p1) * (ROWK_DW * 4));
-        load_bits<NBK, ROWK_DW, ALK>(row, q4 * NBK, B.kc[tile]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < NWK; ++k) B.kc[tile][k] = 0u;
-      }
+      const int tk = min(t0 + 16 * tile + n16, last);
+      load_chunk<NBK, ROWK>(a.kp + row_of(tk, t0, p0, p1) * ROWK, q4 * NBK, B.kc[tile]);
     }
+  };
+  auto fetch_v = [&](int t0, int p0, int p1, VBlk& B) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int tt = t0 + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4));
-      B.kn[e] = 0.f;
-      B.vn[e] = 0.f;
-#pragma unroll
-      for (int k = 0; k < NWV; ++k) B.seg[e][k] = 0u;
-      if (tt < end) {
-        const int64_t row = row_of(tt, t0, p0, p1);
-        B.kn[e] = a.kn[row];
-        if constexpr (!SCORES) {
-          B.vn[e] = a.vn[row];
-          load_bits<NBV, ROWV_DW, ALV>((const uint32_t*)(a.vp + row * (ROWV_DW * 4)), n16 * NBV, B.seg[e]);
-        }
+      const int64_t row = row_of(tok(t0, e), t0, p0, p1);
+      B.kn[e] = a.kn[row];
+      if constexpr (!SCORES) {
+        B.vn[e] = a.vn[row];
+        load_chunk<NBV, ROWV>(a.vp + row * ROWV, n16 * NBV, B.seg[e]);
       }
     }
   };
 
-  Blk cur;
-  int p0, p1, np0, np1;
-  pages(start, p0, p1);
-  fetch(start, p0, p1, cur);
-  pages(start + 32, np0, np1);
+  // Key codes are fetched one block ahead; a block's norms and value codes are fetched at the
+  // start of its own iteration, ahead of the score MFMAs that precede their use.
+  if (start < end) {
+    KBlk cur;
+    int p0, p1, np0, np1;
+    pages(start, p0, p1);
+    fetch_k(start, p0, p1, cur);
+    pages(start + 32, np0, np1);
+    wait_vmem_all();
+    uint32_t qoff = (uint32_t)lane * 16u;
 
-  for (int t0 = start; t0 < end; t0 += 32) {
-    Blk nxt;
-    fetch(t0 + 32, np0, np1, nxt);
-    int nnp0, nnp1;
-    pages(t0 + 64, nnp0, nnp1);
+    for (int t0 = start; t0 < end; t0 += 32) {
+      VBlk vb;
+      fetch_v(t0, p0, p1, vb);
+      KBlk nxt;
+      fetch_k(t0 + 32, np0, np1, nxt);
+      int nnp0, nnp1;
+      pages(t0 + 64, nnp0, nnp1);
+      // query operands are re-read from LDS each block rather than held in 8*KB registers
+      asm volatile("" : "+v"(qoff));
+      const char* qbase = (const char*)sq + qoff;
 
-    float s[8];
+      // ---- scores of the block's two 16-token tiles
+      float s[8];
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+      for (int tile = 0; tile < 2; ++tile) {
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        u32x4 akh, akl;
+        for (int kb = 0; kb < KB; ++kb) {
+          u32x4 akh, akl;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t idx = bits_at<PK>(cur.kc[tile], (4 * kb + c) * PK);
+            akh[c] = tkh[idx];
+            akl[c] = tkl[idx];
+          }
+          const u32x4 qh = *(const u32x4*)(qbase + kb * 1024);
+          const u32x4 ql = *(const u32x4*)(qbase + (KB + kb) * 1024);
+          S = mfma16_bf16(akh, qh, S);
+          S = mfma16_bf16(akl, qh, S);
+          S = mfma16_bf16(akh, ql, S);
+        }
+        // D layout: lane (head n16, q4) register r = token t0 + 16*tile + 4*q4 + r = tok(4*tile + r)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tt = t0 + 16 * tile + 4 * q4 + r;
+          const bool ok = tt < end;
+          const float v = ok ? S[r] * sc * vb.kn[4 * tile + r] : -INFINITY;
+          if constexpr (SCORES) {
+            float* dst = ok && head_ok ? a.scores + ((int64_t)b * a.Hq + h) * a.max_seq_len + tt : a.sink + lane;
+            *dst = v;
+          }
+          s[4 * tile + r] = v;
+        }
+      }
+      if constexpr (!SCORES) {
+        // ---- online softmax; weights p_t n^v_t / N with N the running max V norm
+        float mb = s[0], nb = vb.vn[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) {
+          mb = fmaxf(mb, s[e]);
+          nb = fmaxf(nb, vb.vn[e]);
+        }
+        mb = fmaxf(mb, wave_xor(mb, 16));
+        mb = fmaxf(mb, wave_xor(mb, 32));
+        nb = fmaxf(nb, wave_xor(nb, 16));
+        nb = fmaxf(nb, wave_xor(nb, 32));
+        const float m_new = fmaxf(m_run, mb);
+        const float n_new = fmaxf(n_run, nb);
+        const float al = __expf(m_run - m_new);
+        const float inv_n = n_new > 0.f ? 1.0f / n_new : 0.f;
+        const float a_acc = al * n_run * inv_n;
+        float lsum = 0.f;
+        u32x4 bw;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t c0 = ctk[code_at<BK>(cur.kc[tile], 8 * kb + 2 * c)];
-          const uint32_t c1 = ctk[code_at<BK>(cur.kc[tile], 8 * kb + 2 * c + 1)];
-          akh[c] = (c0 & 0xffffu) | (c1 << 16);
-          akl[c] = (c0 >> 16) | (c1 & 0xffff0000u);
+          const float e0 = __expf(s[2 * c] - m_new), e1 = __expf(s[2 * c + 1] - m_new);
+          lsum += e0 + e1;
+          bw[c] = pack_f16x2(e0 * vb.vn[2 * c] * inv_n, e1 * vb.vn[2 * c + 1] * inv_n);
         }
-        S = mfma16_bf16(akh, bqh[kb], S);
-        S = mfma16_bf16(akl, bqh[kb], S);
-        S = mfma16_bf16(akh, bql[kb], S);
-      }
-      // D layout: lane (head n16, q4) register r = token t0 + 16*tile + 4*q4 + r = tok(4*tile + r)
+        l_run = l_run * al + lsum;
+        m_run = m_new;
+        n_run = n_new;
+        // the running maxima settle after a few blocks: skip the rescale once no lane needs it
+        if (__any(a_acc != 1.0f)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tt = t0 + 16 * tile + 4 * q4 + r;
-        float v = -INFINITY;
-        if (tt < end) {
-          v = S[r] * sc * cur.kn[4 * tile + r];
-          if constexpr (SCORES) {
-            if (head_ok) a.scores[((int64_t)b * a.Hq + h) * a.max_seq_len + tt] = v;
+          for (int t = 0; t < TV; ++t) acc[t] = acc[t] * a_acc;
+        }
+
+        // ---- P.V: lane (coordinate group m = n16, token group g = q4), same 8 tokens; tile t
+        //      is coordinate m*d/16 + t, component c the tokens tok(2c), tok(2c+1)
+        if constexpr (BV == 2) {
+#pragma unroll
+          for (int ch = 0; ch < (NBV + 15) / 16; ++ch) {   // 8 codes = 8 tiles per 16-bit chunk
+            uint32_t z[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              z[c] = interleave2((vb.seg[2 * c][0] >> (16 * ch)) & 0xffffu, (vb.seg[2 * c + 1][0] >> (16 * ch)) & 0xffffu);
+#pragma unroll
+            for (int j = 0; j < 4 && 8 * ch + 2 * j < TV; ++j) {
+              u32x4 av0, av1;
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const u32x2 e = *(const u32x2*)&tv[2 * ((z[c] >> (8 * j)) & 255u)];
+                av0[c] = e[0];
+                av1[c] = e[1];
+              }
+              acc[8 * ch + 2 * j] = mfma16_f16(av0, bw, acc[8 * ch + 2 * j]);
+              acc[8 * ch + 2 * j + 1] = mfma16_f16(av1, bw, acc[8 * ch + 2 * j + 1]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < TV; ++t) {
+            u32x4 av;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              av[c] = tv[bits_at<BV>(vb.seg[2 * c], BV * t) | (bits_at<BV>(vb.seg[2 * c + 1], BV * t) << BV)];
+            acc[t] = mfma16_f16(av, bw, acc[t]);
           }
         }
-        s[4 * tile + r] = v;
       }
+      cur = nxt;
+      p0 = np0;
+      p1 = np1;
+      np0 = nnp0;
+      np1 = nnp1;
     }
-    if constexpr (!SCORES) {
-      float mb = s[0], nb = cur.vn[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) {
-        mb = fmaxf(mb, s[e]);
-        nb = fmaxf(nb, cur.vn[e]);
-      }
-      mb = fmaxf(mb, wave_xor(mb, 16));
-      mb = fmaxf(mb, wave_xor(mb, 32));
-      nb = fmaxf(nb, wave_xor(nb, 16));
-      nb = fmaxf(nb, wave_xor(nb, 32));
-      const float m_new = fmaxf(m_run, mb);
-      const float n_new = fmaxf(n_run, nb);
-      const float al = __expf(m_run - m_new);
-      const float inv_n = n_new > 0.f ? 1.0f / n_new : 0.f;
-      const float a_acc = al * n_run * inv_n;
-      float lsum = 0.f;
-      u32x4 bw;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float e0 = __expf(s[2 * c] - m_new), e1 = __expf(s[2 * c + 1] - m_new);
-        lsum += e0 + e1;
-        bw[c] = pack_f16x2(e0 * cur.vn[2 * c] * inv_n, e1 * cur.vn[2 * c + 1] * inv_n);
-      }
-      l_run = l_run * al + lsum;
-      m_run = m_new;
-      n_run = n_new;
-
-      // V centroids: lane (coordinate group m = n16, token group g = q4), same 8 tokens
-#pragma unroll
-      for (int t = 0; t < TV; ++t) {
-        u32x4 av;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t lo = ctv[code_at<BV>(cur.seg[2 * c], t)];
-          const uint32_t hi = ctv[code_at<BV>(cur.seg[2 * c + 1], t)];
-          av[c] = lo | (hi << 16);
-        }
-        acc[t] = acc[t] * a_acc;
-        acc[t] = mfma16_f16(av, bw, acc[t]);
-      }
-    }
-    cur = nxt;
-    np0 = nnp0;
-    np1 = nnp1;
   }
 
   if constexpr (!SCORES) {
@@ -414,8 +503,8 @@ AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu) {
   return L;
 }
 
-template <int D, int BK, int BV>
-static hipError_t launch_attn_t(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
+template <int D, int BK, int BV, int PAGE>
+static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
                                 const Rotation& rv, float* scores, bool scores_only, const AttnLayout& lay,
                                 hipStream_t st) {
   uint8_t* ws = (uint8_t*)p->workspace;
@@ -437,6 +526,7 @@ static hipError_t launch_attn_t(const tq_attn_params* p, const Codebook& ck, con
   a.block_table = p->block_table;
   a.scores = scores;
   a.part = (float*)(ws + lay.part_off);
+  a.sink = (float*)rk.sink();
   a.max_seq_len = p->max_seq_len;
   a.block_size = p->block_table ? p->block_size : 1;
   a.bs_shift = -1;
@@ -458,10 +548,10 @@ static hipError_t launch_attn_t(const tq_attn_params* p, const Codebook& ck, con
     a.ctv[j] = (uint32_t)lv.centroid_f16[2 * j] | ((uint32_t)lv.centroid_f16[2 * j + 1] << 16);
   dim3 grid((unsigned)lay.splits, (unsigned)p->num_kv_heads, (unsigned)B);
   if (scores_only) {
-    hipLaunchKernelGGL((attn_kernel<D, BK, BV, true>), grid, dim3(kAttnWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<D, BK, BV, true, PAGE>), grid, dim3(kAttnWaves * 64), 0, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((attn_kernel<D, BK, BV, false>), grid, dim3(kAttnWaves * 64), 0, st, a);
+  hipLaunchKernelGGL((attn_kernel<D, BK, BV, false, PAGE>), grid, dim3(kAttnWaves * 64), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rs = (int64_t)(rv.f32_stride / sizeof(float));
   switch (p->out_dtype) {
@@ -478,6 +568,15 @@ static hipError_t launch_attn_t(const tq_attn_params* p, const Codebook& ck, con
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
   }
   return hipGetLastError();
+}
+
+template <int D, int BK, int BV>
+static hipError_t launch_attn_t(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
+                                const Rotation& rv, float* scores, bool so, const AttnLayout& lay, hipStream_t st) {
+  if (!p->block_table) return launch_attn_p<D, BK, BV, kDense>(p, ck, cv, rk, rv, scores, so, lay, st);
+  const int bs = p->block_size;
+  if (bs >= 16 && (bs & (bs - 1)) == 0) return launch_attn_p<D, BK, BV, kPagedPow2>(p, ck, cv, rk, rv, scores, so, lay, st);
+  return launch_attn_p<D, BK, BV, kPagedAny>(p, ck, cv, rk, rv, scores, so, lay, st);
 }
 
 template <int D, int BK>

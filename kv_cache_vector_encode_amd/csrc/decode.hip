@@ -21,6 +21,8 @@ struct DecodeKArgs {
   const float* norms;
   const int64_t* slot;
   void* out;
+  const uint8_t* zero;   // zeros that masked lanes load (>= one packed chunk)
+  uint8_t* sink;         // where masked lanes store (>= 64 lanes x 16 bytes)
   int64_t n, vpr;
   uint32_t ctab[8];   // 16 fp16 centroids, two per word
 };
@@ -53,7 +55,7 @@ struct DecGeo {
 // that write (chunk stride 8) or read (stride 1) together then hit 16 distinct bank groups.
 __device__ __forceinline__ uint32_t stage_swizzle(uint32_t c) { return c ^ ((c >> 4) & 7u); }
 
-template <int D, int BITS, int OUT>
+template <int D, int BITS, int OUT, bool SLOT>
 __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
   using Geo = DecGeo<D, BITS>;
   constexpr int T = Geo::T, KB = Geo::KB, HALF = Geo::HALF;
@@ -84,21 +86,30 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
   const int64_t v_begin = a.vpr ? (int64_t)r * a.vpr : 0;
   const int64_t v_end = a.vpr ? min(a.n, v_begin + a.vpr) : a.n;
   const int64_t ntile = (v_end - v_begin + 31) / 32;
+  if (ntile <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vl = lane & 31, hh = lane >> 5;
   uint8_t* stg = (uint8_t*)(smem + Geo::FRAG_U4) + wave * kStageBytes;
 
   // Two-stage prefetch: the packed row of the next tile is loaded while this tile is decoded,
-  // and with a slot gather the slot index is read one tile earlier still.
+  // and with a slot gather the slot index is read one tile earlier still. Every load and store
+  // is issued unconditionally (masked lanes read the zero page and write the sink): the memory
+  // counter is in order, and a branch around an access would make the wait for a prefetched
+  // load also wait for the stores issued after it.
   const int64_t wstride = (int64_t)gridDim.x * kDecWaves;
   auto row_of = [&](int64_t tl) -> int64_t {
     const int64_t v = v_begin + tl * 32 + vl;
-    if (tl >= ntile || v >= v_end) return -1;
-    return a.slot ? a.slot[v] : v;
+    const bool ok = tl < ntile && v < v_end;
+    if constexpr (SLOT) {
+      const int64_t s = a.slot[ok ? v : v_begin];
+      return ok ? s : -1;
+    } else {
+      return ok ? v : -1;
+    }
   };
   auto fetch = [&](int64_t row, uint32_t (&cw)[Geo::CHUNK_DW], float& nrm) {
-    if (row >= 0) {
-      const uint8_t* src = a.packed + row * Geo::ROW + hh * Geo::CHUNK;
+    {
+      const uint8_t* src = row >= 0 ? a.packed + row * Geo::ROW + hh * Geo::CHUNK : a.zero;
       if constexpr (Geo::G == 16) {
 #pragma unroll
         for (int w = 0; w < Geo::CHUNK_DW; w += 4) {
@@ -115,11 +126,7 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
 #pragma unroll
         for (int w = 0; w < Geo::CHUNK_DW; ++w) cw[w] = *(const uint32_t*)(src + 4 * w);
       }
-      nrm = a.norms[row];
-    } else {
-#pragma unroll
-      for (int w = 0; w < Geo::CHUNK_DW; ++w) cw[w] = 0u;
-      nrm = 0.f;
+      nrm = *(row >= 0 ? a.norms + row : (const float*)a.zero);
     }
   };
   int64_t tile = (int64_t)blockIdx.x * kDecWaves + wave;
@@ -127,6 +134,7 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
   float nrmn;
   fetch(row_of(tile), cwn, nrmn);
   int64_t row_nn = row_of(tile + wstride);
+  wait_vmem_all();
 
   for (; tile < ntile; tile += wstride) {
     const int64_t vbase = v_begin + tile * 32;
@@ -208,24 +216,21 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
             const u32x4 q = *(const u32x4*)(stg + 16 * stage_swizzle(c));
             const uint32_t p = c >> 2;
             const int64_t pv = vbase + (p >> 1);
-            if (pv < v_end) {
-              uint8_t* dst = (uint8_t*)a.out + (pv * D + (p & 1) * HALF + 16 * t0) * E + (c & 3) * 16;
-              *(u32x4*)dst = q;
-            }
+            uint8_t* dst = pv < v_end ? (uint8_t*)a.out + (pv * D + (p & 1) * HALF + 16 * t0) * E + (c & 3) * 16
+                                      : a.sink + 16 * lane;
+            *(u32x4*)dst = q;
           }
         }
       } else {
-        if (vec < v_end) {
-          uint8_t* dst = (uint8_t*)a.out + (vec * D + hh * HALF + 16 * t) * E;
+        uint8_t* dst = vec < v_end ? (uint8_t*)a.out + (vec * D + hh * HALF + 16 * t) * E : a.sink + 64 * lane;
 #pragma unroll
-          for (int k = 0; k < CPT; ++k) *(u32x4*)(dst + 16 * k) = ch[k];
-        }
+        for (int k = 0; k < CPT; ++k) *(u32x4*)(dst + 16 * k) = ch[k];
       }
     }
   }
 }
 
-template <int D, int BITS, int OUT>
+template <int D, int BITS, int OUT, bool SLOT>
 static hipError_t launch_decode_t(const DecodeLaunch& L) {
   using Geo = DecGeo<D, BITS>;
   DecodeKArgs k;
@@ -235,6 +240,8 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
   k.norms = L.norms;
   k.slot = L.slot_mapping;
   k.out = L.out;
+  k.zero = L.rot->zero();
+  k.sink = L.rot->sink();
   k.n = L.n;
   k.vpr = L.vectors_per_rot;
   for (int j = 0; j < 8; ++j)
@@ -245,7 +252,7 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
   const size_t lds = Geo::lds_bytes();
   static bool attr_done = false;
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<D, BITS, OUT>,
+    hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<D, BITS, OUT, SLOT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_done = true;
@@ -259,17 +266,22 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
   const int64_t need = (tiles + kDecWaves - 1) / kDecWaves;
   if (bx > need) bx = need;
   if (bx < 1) bx = 1;
-  hipLaunchKernelGGL((decode_kernel<D, BITS, OUT>), dim3((unsigned)bx, (unsigned)nrot), dim3(kDecWaves * 64), lds,
+  hipLaunchKernelGGL((decode_kernel<D, BITS, OUT, SLOT>), dim3((unsigned)bx, (unsigned)nrot), dim3(kDecWaves * 64), lds,
                      L.stream, k);
   return hipGetLastError();
+}
+
+template <int D, int BITS, int OUT>
+static hipError_t dec_slot(const DecodeLaunch& L) {
+  return L.slot_mapping ? launch_decode_t<D, BITS, OUT, true>(L) : launch_decode_t<D, BITS, OUT, false>(L);
 }
 
 template <int D, int BITS>
 static hipError_t dec_out(const DecodeLaunch& L) {
   switch (L.out_dtype) {
-    case TQ_F32: return launch_decode_t<D, BITS, TQ_F32>(L);
-    case TQ_BF16: return launch_decode_t<D, BITS, TQ_BF16>(L);
-    default: return launch_decode_t<D, BITS, TQ_F16>(L);
+    case TQ_F32: return dec_slot<D, BITS, TQ_F32>(L);
+    case TQ_BF16: return dec_slot<D, BITS, TQ_BF16>(L);
+    default: return dec_slot<D, BITS, TQ_F16>(L);
   }
 }
 

@@ -82,5 +82,9 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
 }
 
+// s_waitcnt vmcnt(0): wait for all of this wave's outstanding vector-memory accesses. Issued
+// once after a loop's first prefetch, so that the waits inside the loop are sized for the
+// loop's own accesses rather than for loads still in flight from before it.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace tq

@@ -37,6 +37,7 @@ struct EncodeKArgs {
   uint8_t* packed;
   float* norms;
   const int64_t* slot;
+  uint8_t* sink;           // where masked lanes store (>= 64 x 64 bytes of codes + 64 norms)
   int64_t n, vpr;
   float lut_scale, lut_off;
   uint32_t lut[kLutBins];
@@ -64,7 +65,7 @@ constexpr int enc_waves() { return 8; }
 template <int D, int IN>
 constexpr int enc_wpe() { return D == 256 ? 2 : 4; }
 
-template <int D, int BITS, int IN>
+template <int D, int BITS, int IN, bool SLOT>
 __global__ void __launch_bounds__((enc_waves<D, IN>() * 64))
 __attribute__((amdgpu_waves_per_eu(enc_wpe<D, IN>())))
 encode_kernel(EncodeKArgs a) {
@@ -95,36 +96,53 @@ encode_kernel(EncodeKArgs a) {
   const int64_t v_begin = a.vpr ? (int64_t)r * a.vpr : 0;
   const int64_t v_end = a.vpr ? min(a.n, v_begin + a.vpr) : a.n;
   const int64_t ntile = (v_end - v_begin + 31) / 32;
+  if (ntile <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vl = lane & 31, hh = lane >> 5;
 
   // Raw inputs of one tile: lane (v, hh) reads its d/2 contiguous elements with 16-byte loads.
   // bf16 inputs are the MFMA B operands as loaded and are prefetched one tile ahead, so every
   // wave keeps a tile of loads in flight while it rotates and quantizes the previous one.
+  // Every load and store is issued unconditionally (masked lanes read row v_begin and write
+  // the sink): the memory counter is in order, and a branch around an access would make the
+  // wait for a prefetched load also wait for the stores issued after it.
   constexpr int ELEM = IN == TQ_F32 ? 4 : 2;
   constexpr int NRAW = HALF * ELEM / 16;
   constexpr bool PREFETCH = (IN == TQ_BF16);
   const int64_t wstride = (int64_t)gridDim.x * WAVES;
-  auto fetch = [&](int64_t tl, u32x4 (&raw)[NRAW]) {
+  // loads tile tl's inputs and returns the packed row its codes go to (-1: none)
+  auto fetch = [&](int64_t tl, u32x4 (&raw)[NRAW]) -> int64_t {
     const int64_t v = v_begin + tl * 32 + vl;
-    const int64_t vs = v < v_end ? v : v_begin;
+    const bool ok = v < v_end;
+    const int64_t vs = ok ? v : v_begin;
     const uint8_t* xp = (const uint8_t*)a.x + (vs * a.x_row_stride + hh * HALF) * ELEM;
 #pragma unroll
     for (int k = 0; k < NRAW; ++k) raw[k] = *(const u32x4*)(xp + 16 * k);
+    if constexpr (SLOT) {
+      const int64_t s = a.slot[vs];
+      return ok ? s : -1;
+    } else {
+      return ok ? v : -1;
+    }
   };
   int64_t tile = (int64_t)blockIdx.x * WAVES + wave;
   u32x4 xr[NRAW];
-  if (PREFETCH && tile < ntile) fetch(tile, xr);
+  int64_t rown = -1;
+  if (PREFETCH) {
+    rown = fetch(tile, xr);
+    wait_vmem_all();
+  }
 
   for (; tile < ntile; tile += wstride) {
-    const int64_t vec = v_begin + tile * 32 + vl;
-    const bool valid = vec < v_end;
-    if constexpr (!PREFETCH) fetch(tile, xr);
     u32x4 xh[KB], xl[SPLIT_X ? KB : 1];
-    if constexpr (IN == TQ_BF16) {
+    int64_t row;
+    if constexpr (PREFETCH) {
 #pragma unroll
       for (int k = 0; k < NRAW; ++k) xh[k] = xr[k];
-      if (PREFETCH && tile + wstride < ntile) fetch(tile + wstride, xr);
+      row = rown;
+      rown = fetch(tile + wstride, xr);   // past the end this reads row v_begin, unused
+    } else {
+      row = fetch(tile, xr);
     }
 
     // ---- norm, and the MFMA B operands (bf16 hi, and lo for split inputs)
@@ -217,28 +235,27 @@ encode_kernel(EncodeKArgs a) {
     }
 
     // ---- store
-    if (valid) {
-      const int64_t row = a.slot ? a.slot[vec] : vec;
-      if (row >= 0) {
-        uint8_t* dst = a.packed + row * Geo::ROW + hh * Geo::CHUNK;
-        if constexpr (Geo::G == 16) {
+    {
+      const bool ok = row >= 0;
+      uint8_t* dst = ok ? a.packed + row * Geo::ROW + hh * Geo::CHUNK : a.sink + 64 * lane;
+      float* np = ok && hh == 0 ? a.norms + row : (float*)(a.sink + 4096) + lane;
+      if constexpr (Geo::G == 16) {
 #pragma unroll
-          for (int w = 0; w < Geo::CHUNK_DW; w += 4)
-            *(u32x4*)(dst + 4 * w) = u32x4{pk[w], pk[w + 1], pk[w + 2], pk[w + 3]};
-        } else if constexpr (Geo::G == 8) {
+        for (int w = 0; w < Geo::CHUNK_DW; w += 4)
+          *(u32x4*)(dst + 4 * w) = u32x4{pk[w], pk[w + 1], pk[w + 2], pk[w + 3]};
+      } else if constexpr (Geo::G == 8) {
 #pragma unroll
-          for (int w = 0; w < Geo::CHUNK_DW; w += 2) *(u32x2*)(dst + 4 * w) = u32x2{pk[w], pk[w + 1]};
-        } else {
+        for (int w = 0; w < Geo::CHUNK_DW; w += 2) *(u32x2*)(dst + 4 * w) = u32x2{pk[w], pk[w + 1]};
+      } else {
 #pragma unroll
-          for (int w = 0; w < Geo::CHUNK_DW; ++w) *(uint32_t*)(dst + 4 * w) = pk[w];
-        }
-        if (hh == 0) a.norms[row] = nrm;
+        for (int w = 0; w < Geo::CHUNK_DW; ++w) *(uint32_t*)(dst + 4 * w) = pk[w];
       }
+      *np = nrm;
     }
   }
 }
 
-template <int D, int BITS, int IN>
+template <int D, int BITS, int IN, bool SLOT>
 static hipError_t launch_encode_t(const EncodeLaunch& L) {
   using Geo = EncGeo<D, BITS>;
   EncodeKArgs k;
@@ -249,6 +266,7 @@ static hipError_t launch_encode_t(const EncodeLaunch& L) {
   k.packed = L.packed;
   k.norms = L.norms;
   k.slot = L.slot_mapping;
+  k.sink = L.rot->sink();
   k.n = L.n;
   k.vpr = L.vectors_per_rot;
   k.lut_scale = L.lv.lut.scale;
@@ -260,7 +278,7 @@ static hipError_t launch_encode_t(const EncodeLaunch& L) {
   const size_t lds = Geo::LDS ? Geo::FRAG_U4 * sizeof(u32x4) : 0;
   static bool attr_done = false;
   if (!attr_done && lds > 0) {
-    hipError_t e = hipFuncSetAttribute((const void*)encode_kernel<D, BITS, IN>,
+    hipError_t e = hipFuncSetAttribute((const void*)encode_kernel<D, BITS, IN, SLOT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_done = true;
@@ -273,16 +291,21 @@ static hipError_t launch_encode_t(const EncodeLaunch& L) {
   if (bx > need) bx = need;
   if (bx < 1) bx = 1;
   dim3 grid((unsigned)bx, (unsigned)nrot);
-  hipLaunchKernelGGL((encode_kernel<D, BITS, IN>), grid, dim3(WAVES * 64), lds, L.stream, k);
+  hipLaunchKernelGGL((encode_kernel<D, BITS, IN, SLOT>), grid, dim3(WAVES * 64), lds, L.stream, k);
   return hipGetLastError();
+}
+
+template <int D, int BITS, int IN>
+static hipError_t dispatch_slot(const EncodeLaunch& L) {
+  return L.slot_mapping ? launch_encode_t<D, BITS, IN, true>(L) : launch_encode_t<D, BITS, IN, false>(L);
 }
 
 template <int D, int BITS>
 static hipError_t dispatch_in(const EncodeLaunch& L) {
   switch (L.x_dtype) {
-    case TQ_F32: return launch_encode_t<D, BITS, TQ_F32>(L);
-    case TQ_BF16: return launch_encode_t<D, BITS, TQ_BF16>(L);
-    default: return launch_encode_t<D, BITS, TQ_F16>(L);
+    case TQ_F32: return dispatch_slot<D, BITS, TQ_F32>(L);
+    case TQ_BF16: return dispatch_slot<D, BITS, TQ_BF16>(L);
+    default: return dispatch_slot<D, BITS, TQ_F16>(L);
   }
 }
 

@@ -347,8 +347,9 @@ static int upload_rotation(Rotation& R) {
   R.enc_off = 0;
   R.dec_off = R.enc_stride * R.n_rot;
   R.f32_off = R.dec_off + R.dec_stride * R.n_rot;
-  size_t total = R.f32_off + R.f32_stride * R.n_rot;
-  std::vector<uint8_t> host(total);
+  R.pad_off = R.f32_off + R.f32_stride * R.n_rot;
+  size_t total = R.pad_off + Rotation::kZeroBytes + Rotation::kSinkBytes;
+  std::vector<uint8_t> host(total);   // the zero page and sink upload as zeros
   for (int r = 0; r < R.n_rot; ++r) {
     const double* P = R.pi.data() + (size_t)r * dd;
     uint16_t* hi = (uint16_t*)(host.data() + R.enc_off + r * R.enc_stride);
