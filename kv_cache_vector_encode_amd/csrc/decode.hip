@@ -27,7 +27,11 @@ struct DecodeKArgs {
   uint32_t ctab[8];   // 16 fp16 centroids, two per word
 };
 
-constexpr int kDecWaves = 8;
+// Four waves per workgroup and one workgroup per CU: the decode is bound by its output
+// stores, and HBM write throughput drops when more waves keep stores in flight at once
+// (fewer writers with a smaller address window sustain more bytes/s). Latency within a wave
+// is hidden by computing two output tiles at a time instead.
+constexpr int kDecWaves = 4;
 constexpr int kStageBytes = 4096;   // per-wave output staging buffer
 
 template <int D, int BITS>
@@ -178,12 +182,21 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
     constexpr int E = OUT == TQ_F32 ? 4 : 2;   // output bytes per element
     constexpr int CPT = E;                     // 16-byte chunks per lane per tile (16 outputs)
     constexpr int S = 4 / CPT;                 // tiles per 64-byte run of one half vector
+    f32x16 accp[2];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      f32x16 acc = {};
+      if (t % 2 == 0) {
+        // two independent accumulation chains in flight
+        accp[0] = f32x16{};
+        accp[1] = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        acc = mfma32_f16(*(const u32x4*)((const char*)smem + aoff + (t * KB + kb) * 1024), bfrag[kb], acc);
+        for (int kb = 0; kb < KB; ++kb) {
+          accp[0] = mfma32_f16(*(const u32x4*)((const char*)smem + aoff + (t * KB + kb) * 1024), bfrag[kb], accp[0]);
+          accp[1] = mfma32_f16(*(const u32x4*)((const char*)smem + aoff + ((t + 1) * KB + kb) * 1024), bfrag[kb],
+                               accp[1]);
+        }
+      }
+      const f32x16 acc = accp[t % 2];
       // scaled outputs of coordinates hh*d/2 + 16t .. +16 as CPT 16-byte chunks
       u32x4 ch[CPT];
       if constexpr (OUT == TQ_F32) {
@@ -258,10 +271,7 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
     attr_done = true;
   }
   const int cu = device_cu_count(L.rot->device);
-  // workgroups per CU: as many as LDS holds (tiles, staging and the 2 KiB table), at most 3
-  int per_cu = (int)((160 * 1024) / (lds + 2048));
-  per_cu = per_cu < 1 ? 1 : (per_cu > 3 ? 3 : per_cu);
-  const int64_t want = (int64_t)cu * per_cu;
+  const int64_t want = cu;   // one workgroup per CU (see kDecWaves)
   int64_t bx = (want + nrot - 1) / nrot;
   const int64_t need = (tiles + kDecWaves - 1) / kDecWaves;
   if (bx > need) bx = need;
