@@ -417,65 +417,131 @@ attn_kernel(AttnKArgs a) {
   }
 }
 
+// Query heads handled together by qrot_kernel / merge_kernel (a block reads each rotation entry
+// once for all of them); kept small so that there are enough blocks to hide load latency.
+constexpr int kHeadsPerBlock = 2;
+
+// q' = Pi_K q for up to 8 query heads of one sequence. Thread k owns output coordinate k and
+// walks Pi_K^T row by row (coalesced across threads); the queries sit in LDS.
 template <int D>
-__global__ void qrot_kernel(const void* q, int q_dtype, const float* pik, int64_t rot_stride, int Hq, int bpr,
-                            float* out) {
-  __shared__ float qs[D];
-  const int bh = blockIdx.x, b = bh / Hq;
-  const int r = bpr ? b / bpr : 0;
+__global__ void __launch_bounds__(D) qrot_kernel(const void* q, int q_dtype, const float* pikt, int64_t rot_stride,
+                                                 int Hq, int bpr, float* out) {
+  constexpr int HB = kHeadsPerBlock;
+  __shared__ float qs[HB][D];
+  const int b = blockIdx.x, h0 = blockIdx.y * HB;
+  const int nh = min(HB, Hq - h0);
   const int k = threadIdx.x;
-  float v;
-  if (q_dtype == TQ_F32)
-    v = ((const float*)q)[(int64_t)bh * D + k];
-  else if (q_dtype == TQ_BF16)
-    v = bf16_bits_to_f32(((const uint16_t*)q)[(int64_t)bh * D + k]);
-  else
-    v = f16_bits_to_f32(((const uint16_t*)q)[(int64_t)bh * D + k]);
-  qs[k] = v;
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    float v = 0.f;
+    if (h < nh) {
+      const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + k;
+      if (q_dtype == TQ_F32)
+        v = ((const float*)q)[idx];
+      else if (q_dtype == TQ_BF16)
+        v = bf16_bits_to_f32(((const uint16_t*)q)[idx]);
+      else
+        v = f16_bits_to_f32(((const uint16_t*)q)[idx]);
+    }
+    qs[h][k] = v;
+  }
   __syncthreads();
-  const float* P = pik + r * rot_stride + (int64_t)k * D;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int j = 0; j < D; ++j) acc = fmaf(P[j], qs[j], acc);
-  out[(int64_t)bh * D + k] = acc;
+  const int r = bpr ? b / bpr : 0;
+  const float* PT = pikt + r * rot_stride + k;   // PT[j*D] = Pi[k][j]
+  float acc[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) acc[h] = 0.f;
+#pragma unroll 16
+  for (int j = 0; j < D; ++j) {
+    const float pv = PT[(int64_t)j * D];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) acc[h] = fmaf(pv, qs[h][j], acc[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < HB; ++h)
+    if (h < nh) out[((int64_t)b * Hq + h0 + h) * D + k] = acc[h];
 }
 
+// Log-sum-exp merge of the token splits for up to 8 query heads of one sequence, then
+// o = Pi_V^T (sum_s acc_s e^(m_s - M)) / L. Thread k owns coordinate k.
 template <int D, int OUT>
-__global__ void merge_kernel(const float* part, int s_eff, int BHq, int Hq, int bpr, const float* piv,
-                             int64_t rot_stride, void* out, float* lse) {
-  __shared__ float orot[D];
-  const int bh = blockIdx.x, b = bh / Hq;
-  const int r = bpr ? b / bpr : 0;
-  const int k = threadIdx.x;
-  const int64_t stride = (int64_t)BHq * (D + 2);
-  const float* P = part + (int64_t)bh * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < s_eff; ++s) M = fmaxf(M, P[s * stride]);
-  float L = 0.f, A = 0.f;
-  if (M > -INFINITY) {
-    for (int s = 0; s < s_eff; ++s) {
-      const float ms = P[s * stride];
-      if (ms > -INFINITY) {
-        const float w = __expf(ms - M);
-        L += w * P[s * stride + 1];
-        A += w * P[s * stride + 2 + k];
+__global__ void __launch_bounds__(D) merge_kernel(const float* part, int s_eff, int B, int Hq, int bpr,
+                                                  const float* piv, int64_t rot_stride, void* out, float* lse) {
+  constexpr int HB = kHeadsPerBlock, NW = D / 64;
+  __shared__ float orot[HB][D];
+  __shared__ float red[HB][NW];
+  __shared__ float Ms[HB];
+  const int b = blockIdx.x, h0 = blockIdx.y * HB;
+  const int nh = min(HB, Hq - h0);
+  const int k = threadIdx.x, lane = k & 63, wv = k >> 6;
+  const int64_t sstride = (int64_t)B * Hq * (D + 2);
+  const float* P0 = part + ((int64_t)b * Hq + h0) * (D + 2);   // split s, head h: + s*sstride + h*(D+2)
+
+  // M_h = max over splits of m_s (threads stride over the splits)
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    float m = -INFINITY;
+    if (h < nh)
+      for (int s = k; s < s_eff; s += D) m = fmaxf(m, P0[(int64_t)s * sstride + h * (D + 2)]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, wave_xor(m, o));
+    if (lane == 0) red[h][wv] = m;
+  }
+  __syncthreads();
+  if (k < HB) {
+    float m = red[k][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, red[k][w]);
+    Ms[k] = m;
+  }
+  __syncthreads();
+
+  float acc[HB], lsum[HB], M[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    acc[h] = 0.f;
+    lsum[h] = 0.f;
+    M[h] = Ms[h];
+  }
+#pragma unroll 4
+  for (int s = 0; s < s_eff; ++s) {
+    const float* Ps = P0 + (int64_t)s * sstride;
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      if (h < nh && M[h] > -INFINITY) {
+        const float ms = Ps[h * (D + 2)];
+        const float w = ms > -INFINITY ? __expf(ms - M[h]) : 0.f;
+        lsum[h] = fmaf(w, Ps[h * (D + 2) + 1], lsum[h]);
+        acc[h] = fmaf(w, Ps[h * (D + 2) + 2 + k], acc[h]);
       }
     }
   }
-  orot[k] = L > 0.f ? A / L : 0.f;
+#pragma unroll
+  for (int h = 0; h < HB; ++h) orot[h][k] = lsum[h] > 0.f ? acc[h] / lsum[h] : 0.f;
   __syncthreads();
-  const float* Pv = piv + r * rot_stride;
-  float o = 0.f;
-#pragma unroll 8
-  for (int kk = 0; kk < D; ++kk) o = fmaf(Pv[(int64_t)kk * D + k], orot[kk], o);
-  const int64_t idx = (int64_t)bh * D + k;
-  if constexpr (OUT == TQ_F32)
-    ((float*)out)[idx] = o;
-  else if constexpr (OUT == TQ_BF16)
-    ((uint16_t*)out)[idx] = (uint16_t)f32_to_bf16_bits(o);
-  else
-    ((uint16_t*)out)[idx] = (uint16_t)f32_to_f16_bits(o);
-  if (k == 0 && lse) lse[bh] = L > 0.f ? M + logf(L) : -INFINITY;
+
+  const float* Pv = piv + (bpr ? b / bpr : 0) * rot_stride + k;   // Pv[kk*D] = Pi[kk][k]
+  float o[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) o[h] = 0.f;
+#pragma unroll 16
+  for (int kk = 0; kk < D; ++kk) {
+    const float pv = Pv[(int64_t)kk * D];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) o[h] = fmaf(pv, orot[h][kk], o[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    if (h >= nh) continue;
+    const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + k;
+    if constexpr (OUT == TQ_F32)
+      ((float*)out)[idx] = o[h];
+    else if constexpr (OUT == TQ_BF16)
+      ((uint16_t*)out)[idx] = (uint16_t)f32_to_bf16_bits(o[h]);
+    else
+      ((uint16_t*)out)[idx] = (uint16_t)f32_to_f16_bits(o[h]);
+    if (k == 0 && lse) lse[(int64_t)b * Hq + h0 + h] = lsum[h] > 0.f ? M[h] + logf(lsum[h]) : -INFINITY;
+  }
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -510,7 +576,8 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   uint8_t* ws = (uint8_t*)p->workspace;
   float* qrot = (float*)(ws + lay.qrot_off);
   const int Hq = p->num_q_heads, B = p->batch;
-  hipLaunchKernelGGL((qrot_kernel<D>), dim3(B * Hq), dim3(D), 0, st, p->q, p->q_dtype, rk.f32(0),
+  const unsigned hblocks = (unsigned)((Hq + kHeadsPerBlock - 1) / kHeadsPerBlock);
+  hipLaunchKernelGGL((qrot_kernel<D>), dim3(B, hblocks), dim3(D), 0, st, p->q, p->q_dtype, rk.f32t(0),
                      (int64_t)(rk.f32_stride / sizeof(float)), Hq, p->batch_per_rot, qrot);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -556,15 +623,15 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   const int64_t rs = (int64_t)(rv.f32_stride / sizeof(float));
   switch (p->out_dtype) {
     case TQ_F32:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_F32>), dim3(B * Hq), dim3(D), 0, st, a.part, a.s_eff, B * Hq, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F32>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
       break;
     case TQ_BF16:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_BF16>), dim3(B * Hq), dim3(D), 0, st, a.part, a.s_eff, B * Hq, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_BF16>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
       break;
     default:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_F16>), dim3(B * Hq), dim3(D), 0, st, a.part, a.s_eff, B * Hq, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F16>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
   }
   return hipGetLastError();

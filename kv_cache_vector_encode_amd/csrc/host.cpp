@@ -347,7 +347,8 @@ static int upload_rotation(Rotation& R) {
   R.enc_off = 0;
   R.dec_off = R.enc_stride * R.n_rot;
   R.f32_off = R.dec_off + R.dec_stride * R.n_rot;
-  R.pad_off = R.f32_off + R.f32_stride * R.n_rot;
+  R.f32t_off = R.f32_off + R.f32_stride * R.n_rot;
+  R.pad_off = R.f32t_off + R.f32_stride * R.n_rot;
   size_t total = R.pad_off + Rotation::kZeroBytes + Rotation::kSinkBytes;
   std::vector<uint8_t> host(total);   // the zero page and sink upload as zeros
   for (int r = 0; r < R.n_rot; ++r) {
@@ -366,6 +367,9 @@ static int upload_rotation(Rotation& R) {
     build_tiles(d, [&](int row, int col) { return to_f16(P[(size_t)col * d + row]); }, de);
     float* f = (float*)(host.data() + R.f32_off + r * R.f32_stride);
     for (size_t i = 0; i < dd; ++i) f[i] = (float)P[i];
+    float* ft = (float*)(host.data() + R.f32t_off + r * R.f32_stride);
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) ft[(size_t)j * d + i] = (float)P[(size_t)i * d + j];
   }
   hipError_t e = hipMalloc(&R.dev, total);
   if (e != hipSuccess) return fail(TQ_ERR_HIP, std::string("tq_rotation: hipMalloc: ") + hipGetErrorString(e));

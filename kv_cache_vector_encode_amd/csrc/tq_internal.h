@@ -29,14 +29,18 @@ struct Rotation {
   //  enc_frag: bf16 MFMA A tiles of Pi (hi then lo), 4*d*d bytes
   //  dec_frag: fp16 MFMA A tiles of Pi^T, 2*d*d bytes
   //  pi_f32:   Pi in float32 row-major, 4*d*d bytes
+  //  pit_f32:  Pi^T in float32 row-major, 4*d*d bytes
   //  pad:      kZeroBytes of zeros that masked lanes load from, then kSinkBytes that masked
   //            lanes store to (contents undefined), so kernels issue every access unconditionally
   void* dev = nullptr;
   size_t enc_stride = 0, dec_stride = 0, f32_stride = 0;   // bytes per rotation
-  size_t enc_off = 0, dec_off = 0, f32_off = 0, pad_off = 0; // bytes from dev
+  size_t enc_off = 0, dec_off = 0, f32_off = 0, f32t_off = 0, pad_off = 0;  // bytes from dev
   const uint8_t* enc(int r) const { return (const uint8_t*)dev + enc_off + (size_t)r * enc_stride; }
   const uint8_t* dec(int r) const { return (const uint8_t*)dev + dec_off + (size_t)r * dec_stride; }
   const float* f32(int r) const { return (const float*)((const uint8_t*)dev + f32_off + (size_t)r * f32_stride); }
+  const float* f32t(int r) const {
+    return (const float*)((const uint8_t*)dev + f32t_off + (size_t)r * f32_stride);
+  }
   const uint8_t* zero() const { return (const uint8_t*)dev + pad_off; }
   uint8_t* sink() const { return (uint8_t*)dev + pad_off + kZeroBytes; }
   static constexpr size_t kZeroBytes = 256, kSinkBytes = 8192;
