@@ -48,6 +48,24 @@ def encode_codes(x, pi, centroids):
     return codes, n.astype(np.float32), y
 
 
+def encode_codes_norm_corrected(x, pi, centroids):
+    """Encode with key-side norm correction: the stored norm is n / ||c[idx]||, so the decoded
+    vector n / ||c[idx]|| * Pi^T c[idx] has the input's length n.
+
+    Turbo Attention PyPI page, "The codec" table, "Norms" row (key-side norm correction keeps
+    the decoded key's length). Reading: the codes are those of the plain encode; only the
+    stored scalar changes, to n / ||c[idx]||_2 (float32, round to nearest even), which makes
+    decode, scores and attention need no change. A zero vector keeps norm 0.
+    Returns (codes, corrected norms float32, y).
+    """
+    codes, _, y = encode_codes(x, pi, centroids)
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=1))
+    c = np.asarray(centroids, dtype=np.float64)
+    cn = np.sqrt(np.sum(c[codes.astype(np.int64)] ** 2, axis=1))
+    return codes, (n / cn).astype(np.float32), y
+
+
 def boundary_distance(y, thresholds):
     """min_k |y_i - t_k|: how far each rotated coordinate is from a decision boundary."""
     y = np.asarray(y, dtype=np.float64)

@@ -52,3 +52,29 @@ def haar_rotations(gaussians):
     """Stack version: [n, d, d] draws -> [n, d, d] rotations."""
     g = np.asarray(gaussians, dtype=np.float64)
     return np.stack([haar_rotation(gi) for gi in g])
+
+
+def hadamard_matrix(d: int):
+    """Walsh-Hadamard matrix of order d (a power of two), Sylvester's doubling:
+    H_1 = [1], H_2k = [[H_k, H_k], [H_k, -H_k]]. Entries are +-1 and H H^T = d I."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("hadamard_matrix: d must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard_rotation(d: int, signs=None):
+    """Hadamard rotation: Pi = H_d diag(s) / sqrt(d), s in {+1, -1}^d (all +1 if None).
+
+    Turbo Attention PyPI page, "The codec" table, "Hadamard rotation" row: a Walsh-Hadamard
+    transform spreads outlier channels across the vector and queries are rotated the same
+    way. Reading: the orthonormal Sylvester-ordered transform, optionally preceded by a sign
+    flip per input channel (a randomized Hadamard transform when the signs are drawn at
+    random); y = Pi x means y = H (s * x) / sqrt(d).
+    """
+    s = np.ones(d) if signs is None else np.asarray(signs, dtype=np.float64).reshape(d)
+    if not np.all(np.abs(s) == 1.0):
+        raise ValueError("hadamard_rotation: signs must be +1 or -1")
+    return hadamard_matrix(d) * s[None, :] / np.sqrt(d)
