@@ -93,6 +93,14 @@ void tq_codebook_free(tq_codebook_t* cb);
 tq_rotation_t* tq_rotation_from_gaussian(int d, int n_rot, const float* gaussian);
 tq_rotation_t* tq_rotation_from_matrix(int d, int n_rot, const double* pi);
 
+/* Hadamard rotation (Turbo Attention PyPI page, "The codec", Hadamard rotation row: a
+ * Walsh-Hadamard transform spreads outlier channels; queries are rotated the same way):
+ * Pi_r = H_d diag(s_r) / sqrt(d), H_d Sylvester's +-1 Walsh-Hadamard matrix
+ * (H[i][j] = (-1)^popcount(i & j)), s_r = signs[r] (host int8 [n_rot, d], each +1 or -1;
+ * NULL = all +1). Uploaded like the other constructors; every kernel takes it unchanged.
+ * Returns NULL on error (bad d/n_rot, a sign other than +-1, no device, HIP failure). */
+tq_rotation_t* tq_rotation_hadamard(int d, int n_rot, const int8_t* signs);
+
 /* Host only, no device: the float64 rotation (host, [d, d]) that tq_rotation_from_gaussian
  * makes from one Gaussian draw (host, float32 [d, d]). 3 <= d <= 4096. */
 int tq_rotation_compute(int d, const float* gaussian, double* pi);
@@ -117,6 +125,14 @@ void tq_rotation_free(tq_rotation_t* rot);
 int tq_encode(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors_per_rot,
               const void* x, int x_dtype, int64_t n, int64_t x_row_stride,
               uint8_t* packed, float* norms, const int64_t* slot_mapping, tq_stream_t stream);
+
+/* tq_encode with key-side norm correction (Turbo Attention PyPI page, "The codec", Norms
+ * row: the decoded key keeps its length): same codes, same arguments, same errors, but
+ * norms[j] = ||x_i|| / ||c[codes of row j]||_2, so tq_decode returns a vector of length
+ * ||x_i|| and scores / attention use the corrected length with no other change. */
+int tq_encode_norm_corrected(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors_per_rot,
+                             const void* x, int x_dtype, int64_t n, int64_t x_row_stride,
+                             uint8_t* packed, float* norms, const int64_t* slot_mapping, tq_stream_t stream);
 
 /* ---- decode -------------------------------------------------------------------------------
  * Inverse of tq_encode: out[i] (device, dtype out_dtype, contiguous [n, d], 16-byte aligned)

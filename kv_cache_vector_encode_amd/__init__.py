@@ -128,6 +128,22 @@ class Rotation:
             raise TQError(None, _lib.last_error())
         return cls(h, d, n)
 
+    @classmethod
+    def hadamard(cls, d: int, signs=None, n_rot: int | None = None):
+        """Pi_r = H_d diag(signs[r]) / sqrt(d) (signs: int8-convertible [n_rot, d] of +-1, or
+        None for all +1 with n_rot rotations, default 1)."""
+        if signs is None:
+            n = 1 if n_rot is None else int(n_rot)
+            ptr, keep = None, None
+        else:
+            keep = np.ascontiguousarray(np.asarray(signs).reshape(-1, d).astype(np.int8))
+            n = keep.shape[0]
+            ptr = keep.ctypes.data_as(C.c_void_p)
+        h = lib().tq_rotation_hadamard(int(d), n, ptr)
+        if not h:
+            raise TQError(None, _lib.last_error())
+        return cls(h, d, n)
+
     def matrices(self) -> np.ndarray:
         out = np.zeros((self.n_rot, self.d, self.d))
         check(lib().tq_rotation_get(self._h, out.ctypes.data_as(C.c_void_p)))
@@ -148,10 +164,11 @@ class Rotation:
 
 
 def encode(cb: Codebook, rot: Rotation, x: torch.Tensor, vectors_per_rot: int = 0, packed=None, norms=None,
-           slot_mapping=None, num_slots=None, stream=None):
+           slot_mapping=None, num_slots=None, stream=None, norm_correction: bool = False):
     """x: [..., d] on the GPU (float32/bfloat16/float16; rows may be strided).
     Returns (packed uint8 [rows, d*b/8], norms float32 [rows]); rows = N, or num_slots with a
-    slot_mapping (int64 [N]: destination row of each vector, negative = skip)."""
+    slot_mapping (int64 [N]: destination row of each vector, negative = skip).
+    norm_correction: store ||x|| / ||c[codes]|| so that the decode keeps ||x||."""
     d = x.shape[-1]
     x2 = x.reshape(-1, d) if x.dim() != 2 else x
     if x2.stride(-1) != 1:
@@ -162,8 +179,9 @@ def encode(cb: Codebook, rot: Rotation, x: torch.Tensor, vectors_per_rot: int = 
         packed = torch.empty(rows, packed_row_bytes(d, cb.bits), dtype=torch.uint8, device=x.device)
     if norms is None:
         norms = torch.empty(rows, dtype=torch.float32, device=x.device)
-    check(lib().tq_encode(cb.handle, rot.handle, int(vectors_per_rot), _ptr(x2), dtype_code(x2.dtype), n,
-                          x2.stride(0), _ptr(packed), _ptr(norms), _ptr(slot_mapping), _stream(stream)))
+    fn = lib().tq_encode_norm_corrected if norm_correction else lib().tq_encode
+    check(fn(cb.handle, rot.handle, int(vectors_per_rot), _ptr(x2), dtype_code(x2.dtype), n,
+             x2.stride(0), _ptr(packed), _ptr(norms), _ptr(slot_mapping), _stream(stream)))
     return packed, norms
 
 

@@ -16,7 +16,8 @@ STATUS = {0: "TQ_OK", -1: "TQ_ERR_INVALID_ARG", -2: "TQ_ERR_NULL", -3: "TQ_ERR_A
 EXPORTS = (
     "tq_version", "tq_last_error", "tq_codebook_init", "tq_codebook_get", "tq_codebook_dims",
     "tq_codebook_free", "tq_rotation_from_gaussian", "tq_rotation_from_matrix", "tq_rotation_compute",
-    "tq_rotation_get", "tq_rotation_dims", "tq_rotation_free", "tq_encode", "tq_decode",
+    "tq_rotation_get", "tq_rotation_dims", "tq_rotation_free", "tq_rotation_hadamard", "tq_encode",
+    "tq_encode_norm_corrected", "tq_decode",
     "tq_attn_workspace_size", "tq_scores_compressed", "tq_attn_decode",
 )
 
@@ -57,11 +58,13 @@ def lib():
         "tq_codebook_free": ([vp], None),
         "tq_rotation_from_gaussian": ([i32, i32, vp], vp),
         "tq_rotation_from_matrix": ([i32, i32, vp], vp),
+        "tq_rotation_hadamard": ([i32, i32, vp], vp),
         "tq_rotation_compute": ([i32, vp, vp], i32),
         "tq_rotation_get": ([vp, vp], i32),
         "tq_rotation_dims": ([vp, vp, vp], i32),
         "tq_rotation_free": ([vp], None),
         "tq_encode": ([vp, vp, i64, vp, i32, i64, i64, vp, vp, vp, vp], i32),
+        "tq_encode_norm_corrected": ([vp, vp, i64, vp, i32, i64, i64, vp, vp, vp, vp], i32),
         "tq_decode": ([vp, vp, i64, vp, vp, vp, i64, vp, i32, vp], i32),
         "tq_attn_workspace_size": ([C.POINTER(AttnParams)], C.c_size_t),
         "tq_scores_compressed": ([C.POINTER(AttnParams), vp, vp], i32),

@@ -40,7 +40,9 @@ struct EncodeKArgs {
   uint8_t* sink;           // where masked lanes store (>= 64 x 64 bytes of codes + 64 norms)
   int64_t n, vpr;
   float lut_scale, lut_off;
+  int32_t norm_correct;    // store n / ||c[idx]|| instead of n
   uint32_t lut[kLutBins];
+  float csq[kMaxLevels];   // c_k^2, for the norm correction
 };
 
 
@@ -75,6 +77,7 @@ encode_kernel(EncodeKArgs a) {
   constexpr int WAVES = enc_waves<D, IN>();
   extern __shared__ u32x4 smem[];
   __shared__ uint32_t lut[kLutBins];
+  __shared__ float csq[kMaxLevels];
 
   const int r = blockIdx.y;
   const u32x4* gfrag = a.frag + (int64_t)r * a.frag_stride;
@@ -87,6 +90,9 @@ encode_kernel(EncodeKArgs a) {
     const uint32_t* klut = (const uint32_t*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
                                              offsetof(EncodeKArgs, lut));
     for (int i = threadIdx.x; i < kLutBins; i += blockDim.x) lut[i] = klut[i];
+    const float* kcsq = (const float*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+                                       offsetof(EncodeKArgs, csq));
+    if (threadIdx.x < kMaxLevels) csq[threadIdx.x] = kcsq[threadIdx.x];
   }
   __syncthreads();
   // Tile reads go through an offset the compiler cannot prove loop-invariant; otherwise it
@@ -234,6 +240,28 @@ encode_kernel(EncodeKArgs a) {
         asm volatile("" : "+v"(pk[w]));
     }
 
+    // ---- norm correction (Turbo Attention page, "The codec", Norms row: the decoded key keeps
+    //      the input's length): store n / ||c[idx]||, ||c[idx]||^2 summed over this lane's codes
+    //      and the other half of the vector
+    float nst = nrm;
+    if (a.norm_correct) {
+      float cs0 = 0.f, cs1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < HALF; ++j) {
+        const int pos = j * BITS;
+        uint32_t code = pk[pos >> 5] >> (pos & 31);
+        if ((pos & 31) + BITS > 32) code |= pk[(pos >> 5) + 1] << (32 - (pos & 31));
+        const float c2 = csq[code & ((1u << BITS) - 1u)];
+        if (j & 1)
+          cs1 += c2;
+        else
+          cs0 += c2;
+      }
+      float cs = cs0 + cs1;
+      cs += wave_xor(cs, 32);
+      nst = nrm / sqrtf(cs);
+    }
+
     // ---- store
     {
       const bool ok = row >= 0;
@@ -250,7 +278,7 @@ encode_kernel(EncodeKArgs a) {
 #pragma unroll
         for (int w = 0; w < Geo::CHUNK_DW; ++w) *(uint32_t*)(dst + 4 * w) = pk[w];
       }
-      *np = nrm;
+      *np = nst;
     }
   }
 }
@@ -271,6 +299,8 @@ static hipError_t launch_encode_t(const EncodeLaunch& L) {
   k.vpr = L.vectors_per_rot;
   k.lut_scale = L.lv.lut.scale;
   k.lut_off = L.lv.lut.offset;
+  k.norm_correct = L.norm_correct ? 1 : 0;
+  for (int j = 0; j < kMaxLevels; ++j) k.csq[j] = L.lv.centroid_sq[j];
   for (int j = 0; j < kLutBins; ++j) k.lut[j] = L.lv.lut.entry[j];
   const int64_t per_rot = L.vectors_per_rot ? L.vectors_per_rot : L.n;
   const int nrot = L.vectors_per_rot ? (int)((L.n + L.vectors_per_rot - 1) / L.vectors_per_rot) : 1;

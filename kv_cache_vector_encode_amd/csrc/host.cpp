@@ -214,6 +214,7 @@ LevelArgs make_levels(const Codebook& cb) {
   for (int k = 0; k < L; ++k) {
     lv.centroid_f16[k] = to_f16(cb.centroids[k]);
     lv.centroid_f32[k] = (float)cb.centroids[k];
+    lv.centroid_sq[k] = (float)(cb.centroids[k] * cb.centroids[k]);
     const uint16_t hi = to_bf16((float)cb.centroids[k]);
     const uint16_t lo = to_bf16((float)(cb.centroids[k] - (double)from_bf16(hi)));
     lv.centroid_bf16x2[k] = (uint32_t)hi | ((uint32_t)lo << 16);
@@ -524,6 +525,38 @@ tq_rotation_t* tq_rotation_from_matrix(int d, int n_rot, const double* pi_in) {
   return make_rotation(d, n_rot, std::move(pi));
 }
 
+tq_rotation_t* tq_rotation_hadamard(int d, int n_rot, const int8_t* signs) {
+  if (!gpu_dim_ok(d)) {
+    set_error("tq_rotation_hadamard: d = " + std::to_string(d) + " is not supported; accepted 64, 128, 256");
+    return nullptr;
+  }
+  if (n_rot < 1 || n_rot > 65535) {
+    set_error("tq_rotation_hadamard: n_rot = " + std::to_string(n_rot) + " is out of range; accepted 1..65535");
+    return nullptr;
+  }
+  const size_t dd = (size_t)d * d;
+  if (signs) {
+    for (size_t i = 0; i < (size_t)n_rot * d; ++i)
+      if (signs[i] != 1 && signs[i] != -1) {
+        set_error("tq_rotation_hadamard: signs[" + std::to_string(i) + "] = " + std::to_string((int)signs[i]) +
+                  "; accepted +1 or -1");
+        return nullptr;
+      }
+  }
+  // Pi[i][j] = (-1)^popcount(i & j) * s_j / sqrt(d): Sylvester's Walsh-Hadamard matrix with a
+  // sign per input channel, orthonormal
+  const double inv = 1.0 / std::sqrt((double)d);
+  std::vector<double> pi(dd * n_rot);
+  for (int r = 0; r < n_rot; ++r)
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) {
+        const double h = (__builtin_popcount((unsigned)(i & j)) & 1) ? -inv : inv;
+        const double sj = signs ? (double)signs[(size_t)r * d + j] : 1.0;
+        pi[(size_t)r * dd + (size_t)i * d + j] = h * sj;
+      }
+  return make_rotation(d, n_rot, std::move(pi));
+}
+
 int tq_rotation_get(const tq_rotation_t* rot, double* pi) {
   if (!rot) return fail(TQ_ERR_NULL, "tq_rotation_get: rot is NULL");
   if (!pi) return fail(TQ_ERR_NULL, "tq_rotation_get: pi is NULL");
@@ -569,35 +602,36 @@ static int check_rot_index(int64_t n, int64_t vpr, int n_rot, const char* who) {
   return TQ_OK;
 }
 
-int tq_encode(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors_per_rot, const void* x,
-              int x_dtype, int64_t n, int64_t x_row_stride, uint8_t* packed, float* norms,
-              const int64_t* slot_mapping, tq_stream_t stream) {
-  int s = check_pair(cb, rot, "tq_encode");
+static int encode_impl(const char* who, bool norm_correct, const tq_codebook_t* cb, const tq_rotation_t* rot,
+                       int64_t vectors_per_rot, const void* x, int x_dtype, int64_t n, int64_t x_row_stride,
+                       uint8_t* packed, float* norms, const int64_t* slot_mapping, tq_stream_t stream) {
+  const std::string W(who);
+  int s = check_pair(cb, rot, who);
   if (s) return s;
   const int d = rot->rot.d;
-  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "tq_encode: n must be >= 0");
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, W + ": n must be >= 0");
   int es = dtype_size(x_dtype);
-  if (!es) return fail(TQ_ERR_INVALID_ARG, "tq_encode: x_dtype = " + std::to_string(x_dtype) +
+  if (!es) return fail(TQ_ERR_INVALID_ARG, W + ": x_dtype = " + std::to_string(x_dtype) +
                                                " is not supported; accepted TQ_F32 (0), TQ_BF16 (1), TQ_F16 (2)");
   if (x_row_stride < d)
-    return fail(TQ_ERR_INVALID_ARG, "tq_encode: x_row_stride = " + std::to_string(x_row_stride) +
+    return fail(TQ_ERR_INVALID_ARG, W + ": x_row_stride = " + std::to_string(x_row_stride) +
                                         " is smaller than d = " + std::to_string(d));
-  if ((s = check_rot_index(n, vectors_per_rot, rot->rot.n_rot, "tq_encode"))) return s;
+  if ((s = check_rot_index(n, vectors_per_rot, rot->rot.n_rot, who))) return s;
   if (n == 0) return TQ_OK;
-  if (!x) return fail(TQ_ERR_NULL, "tq_encode: x is NULL");
-  if (!packed) return fail(TQ_ERR_NULL, "tq_encode: packed is NULL");
-  if (!norms) return fail(TQ_ERR_NULL, "tq_encode: norms is NULL");
-  if (!aligned(x, 16)) return fail(TQ_ERR_ALIGN, "tq_encode: x must be 16-byte aligned");
-  if ((x_row_stride * es) % 16) return fail(TQ_ERR_ALIGN, "tq_encode: x_row_stride * element size must be a multiple of 16 bytes");
-  if (!aligned(packed, 8)) return fail(TQ_ERR_ALIGN, "tq_encode: packed must be 8-byte aligned");
-  if (!aligned(norms, 4)) return fail(TQ_ERR_ALIGN, "tq_encode: norms must be 4-byte aligned");
-  if (slot_mapping && !aligned(slot_mapping, 8)) return fail(TQ_ERR_ALIGN, "tq_encode: slot_mapping must be 8-byte aligned");
-  if ((s = check_device(rot->rot, "tq_encode"))) return s;
+  if (!x) return fail(TQ_ERR_NULL, W + ": x is NULL");
+  if (!packed) return fail(TQ_ERR_NULL, W + ": packed is NULL");
+  if (!norms) return fail(TQ_ERR_NULL, W + ": norms is NULL");
+  if (!aligned(x, 16)) return fail(TQ_ERR_ALIGN, W + ": x must be 16-byte aligned");
+  if ((x_row_stride * es) % 16) return fail(TQ_ERR_ALIGN, W + ": x_row_stride * element size must be a multiple of 16 bytes");
+  if (!aligned(packed, 8)) return fail(TQ_ERR_ALIGN, W + ": packed must be 8-byte aligned");
+  if (!aligned(norms, 4)) return fail(TQ_ERR_ALIGN, W + ": norms must be 4-byte aligned");
+  if (slot_mapping && !aligned(slot_mapping, 8)) return fail(TQ_ERR_ALIGN, W + ": slot_mapping must be 8-byte aligned");
+  if ((s = check_device(rot->rot, who))) return s;
   EncodeLaunch a;
   a.rot = &rot->rot;
   a.lv = make_levels(cb->cb);
   if (!lut_covers_unit_range(a.lv))
-    return fail(TQ_ERR_INVALID_ARG, "tq_encode: the codebook's boundaries are too close for the quantization table");
+    return fail(TQ_ERR_INVALID_ARG, W + ": the codebook's boundaries are too close for the quantization table");
   a.bits = cb->cb.bits;
   a.x_dtype = x_dtype;
   a.vectors_per_rot = vectors_per_rot;
@@ -607,8 +641,23 @@ int tq_encode(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors
   a.packed = packed;
   a.norms = norms;
   a.slot_mapping = slot_mapping;
+  a.norm_correct = norm_correct;
   a.stream = (hipStream_t)stream;
-  return hip_status(launch_encode(a), "tq_encode");
+  return hip_status(launch_encode(a), who);
+}
+
+int tq_encode(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors_per_rot, const void* x,
+              int x_dtype, int64_t n, int64_t x_row_stride, uint8_t* packed, float* norms,
+              const int64_t* slot_mapping, tq_stream_t stream) {
+  return encode_impl("tq_encode", false, cb, rot, vectors_per_rot, x, x_dtype, n, x_row_stride, packed, norms,
+                     slot_mapping, stream);
+}
+
+int tq_encode_norm_corrected(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors_per_rot,
+                             const void* x, int x_dtype, int64_t n, int64_t x_row_stride, uint8_t* packed,
+                             float* norms, const int64_t* slot_mapping, tq_stream_t stream) {
+  return encode_impl("tq_encode_norm_corrected", true, cb, rot, vectors_per_rot, x, x_dtype, n, x_row_stride,
+                     packed, norms, slot_mapping, stream);
 }
 
 int tq_decode(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors_per_rot, const uint8_t* packed,

@@ -63,6 +63,7 @@ struct LevelArgs {
   uint16_t centroid_f16[kMaxLevels];      // c_k as fp16 bits
   uint32_t centroid_bf16x2[kMaxLevels];   // c_k = hi + lo as bf16 bits: hi | lo << 16
   float centroid_f32[kMaxLevels];
+  float centroid_sq[kMaxLevels];          // c_k^2 (float64 square, rounded once)
   QuantLut lut;
 };
 
@@ -81,6 +82,7 @@ struct EncodeLaunch {
   uint8_t* packed;
   float* norms;
   const int64_t* slot_mapping;
+  bool norm_correct;   // store n / ||c[idx]|| instead of n
   hipStream_t stream;
 };
 hipError_t launch_encode(const EncodeLaunch& a);

@@ -104,3 +104,13 @@ def test_hot_path_calls_validate_before_any_launch(L):
     assert L.tq_attn_workspace_size(None) == 0
     assert L.tq_attn_decode(None, None) == -2
     assert L.tq_scores_compressed(None, None, None) == -2
+
+
+def test_hadamard_rejects_bad_arguments():
+    from kv_cache_vector_encode_amd import _lib
+    L = _lib.lib()
+    assert not L.tq_rotation_hadamard(96, 1, None)
+    assert b"d = 96" in L.tq_last_error()
+    bad = (C.c_int8 * 64)(*([1] * 63 + [0]))
+    assert not L.tq_rotation_hadamard(64, 1, C.cast(bad, C.c_void_p))
+    assert b"signs[63]" in L.tq_last_error()
