@@ -180,6 +180,18 @@ typedef struct {
   void* workspace;          /* device, >= tq_attn_workspace_size bytes, 256-byte aligned */
   size_t workspace_bytes;
   int32_t num_splits;       /* token splits per (sequence, KV head); 0 = chosen by the library */
+  /* Recent-token window (optional; KV Cache API page, TurboQuantKVCache.prefill / append /
+   * attention_scores / attend: the newest tokens stay at full precision beside the compressed
+   * ones). With window = R > 0, sequence b has L_b = seq_lens[b] tokens (<= max_seq_len) in
+   * total: the newest w_b = min(L_b, R) are read from the rings k_window / v_window (device
+   * [batch, num_kv_heads, R, d], dtype window_dtype, the token at position t in slot t mod R)
+   * and only positions [0, L_b - w_b) from the compressed cache (rows indexed by position as
+   * above). tq_attn_decode takes one softmax over all L_b tokens; tq_scores_compressed scores
+   * the compressed positions only. window = 0 (and NULL rings): every token is compressed. */
+  const void* k_window;
+  const void* v_window;
+  int32_t window;
+  int32_t window_dtype;
 } tq_attn_params;
 
 /* Bytes of workspace tq_attn_decode and tq_scores_compressed need for these parameters. */
@@ -195,6 +207,47 @@ int tq_scores_compressed(const tq_attn_params* p, float* scores, tq_stream_t str
  * tokens with an online softmax, then a log-sum-exp merge of the splits. len_b = 0 gives
  * o = 0 and lse = -inf. */
 int tq_attn_decode(const tq_attn_params* p, tq_stream_t stream);
+
+/* ---- recent-token window: append and flush ------------------------------------------------
+ * KV Cache API page, TurboQuantKVCache.prefill / append: the newest R = window tokens of each
+ * sequence stay at full precision; tokens leaving the window are compressed. One call appends
+ * n_new tokens to every sequence of the batch: with L = seq_lens[b] tokens before, positions
+ * [L - min(L, R), L + n_new - min(L + n_new, R)) are encoded (codebook/rotation of each side,
+ * as tq_encode) into the compressed cache rows of their positions, the new tokens that stay
+ * in the window are written to ring slot (position mod R), and seq_lens[b] += n_new. A first
+ * call on empty sequences with n_new = prompt length is the page's prefill split; repeated
+ * calls with n_new = 1 are its decode-time append (same final state either way).
+ * Layouts (device): k_new / v_new [batch, num_kv_heads, n_new, d] and the rings
+ * [batch, num_kv_heads, window, d], all of dtype window_dtype, 16-byte aligned; compressed
+ * cache dense [batch, num_kv_heads, max_seq_len, row] or paged as in tq_attn_params.
+ * The caller keeps seq_lens[b] + n_new <= max_seq_len (rows past it are not written). The
+ * workspace (device, 256-byte aligned) holds the staged rows and their slot mapping. */
+typedef struct {
+  const tq_codebook_t* cb_k;
+  const tq_codebook_t* cb_v;
+  const tq_rotation_t* rot_k;
+  const tq_rotation_t* rot_v;
+  int32_t batch, num_kv_heads, n_new;
+  const void* k_new;
+  const void* v_new;
+  void* k_window;
+  void* v_window;
+  int32_t window, window_dtype;
+  int32_t* seq_lens;        /* device int32 [batch]: tokens before the call; advanced by n_new */
+  uint8_t* k_packed;
+  float* k_norms;
+  uint8_t* v_packed;
+  float* v_norms;
+  int32_t max_seq_len;
+  const int32_t* block_table;
+  int32_t block_size, max_blocks_per_seq;
+  int32_t batch_per_rot;    /* rotation of sequence b: b / batch_per_rot (0 = rotation 0) */
+  void* workspace;
+  size_t workspace_bytes;
+} tq_window_append_params;
+
+size_t tq_window_append_workspace_size(const tq_window_append_params* p);
+int tq_window_append(const tq_window_append_params* p, tq_stream_t stream);
 
 #ifdef __cplusplus
 }

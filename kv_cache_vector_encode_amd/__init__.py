@@ -200,7 +200,7 @@ def decode(cb: Codebook, rot: Rotation, packed: torch.Tensor, norms: torch.Tenso
 
 def _params(cb_k, rot_k, q, k_packed, k_norms, cb_v=None, rot_v=None, v_packed=None, v_norms=None,
             seq_lens=None, max_seq_len=None, block_table=None, block_size=0, batch_per_rot=0, scale=None,
-            out=None, lse=None, num_splits=0, num_kv_heads=None):
+            out=None, lse=None, num_splits=0, num_kv_heads=None, k_window=None, v_window=None):
     B, Hq, d = q.shape
     p = AttnParams()
     p.cb_k, p.rot_k = cb_k.handle, rot_k.handle
@@ -227,6 +227,9 @@ def _params(cb_k, rot_k, q, k_packed, k_norms, cb_v=None, rot_v=None, v_packed=N
     p.out_dtype = dtype_code(out.dtype) if out is not None else TQ_F32
     p.lse = lse.data_ptr() if lse is not None else None
     p.num_splits = int(num_splits)
+    if k_window is not None:
+        p.k_window, p.v_window = k_window.data_ptr(), v_window.data_ptr()
+        p.window, p.window_dtype = int(k_window.shape[2]), dtype_code(k_window.dtype)
     return p
 
 
@@ -266,14 +269,53 @@ def scores_compressed(cb_k: Codebook, rot_k: Rotation, q: torch.Tensor, k_packed
 def attn_decode(cb_k: Codebook, rot_k: Rotation, cb_v: Codebook, rot_v: Rotation, q: torch.Tensor,
                 k_packed, k_norms, v_packed, v_norms, seq_lens=None, max_seq_len=None, block_table=None,
                 block_size=0, batch_per_rot=0, scale=None, out=None, out_dtype=None, return_lse=False,
-                num_splits=0, num_kv_heads=None, workspace=None, stream=None):
-    """Fused decode attention over the compressed cache; returns out [B, Hq, d] (and lse)."""
+                num_splits=0, num_kv_heads=None, workspace=None, stream=None, k_window=None, v_window=None):
+    """Fused decode attention over the compressed cache; returns out [B, Hq, d] (and lse).
+    k_window / v_window: optional rings [B, Hkv, R, d] holding each sequence's newest
+    min(len, R) tokens at full precision (token t in slot t % R); seq_lens are then total
+    lengths and only the older positions are read from the compressed cache."""
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if return_lse else None
     p = _params(cb_k, rot_k, q, k_packed, k_norms, cb_v, rot_v, v_packed, v_norms, seq_lens, max_seq_len,
-                block_table, block_size, batch_per_rot, scale, out, lse, num_splits, num_kv_heads)
+                block_table, block_size, batch_per_rot, scale, out, lse, num_splits, num_kv_heads, k_window,
+                v_window)
     ws = _workspace(p, q.device, workspace)
     check(lib().tq_attn_decode(C.byref(p), _stream(stream)))
     out._tq_workspace = ws
     return (out, lse) if return_lse else out
+
+
+def window_append(cb_k: Codebook, rot_k: Rotation, cb_v: Codebook, rot_v: Rotation, k_new: torch.Tensor,
+                  v_new: torch.Tensor, k_window: torch.Tensor, v_window: torch.Tensor, seq_lens: torch.Tensor,
+                  k_packed, k_norms, v_packed, v_norms, max_seq_len=None, block_table=None, block_size=0,
+                  batch_per_rot=0, workspace=None, stream=None):
+    """Append n_new tokens per sequence (k_new / v_new [B, Hkv, n_new, d], the rings' dtype) to
+    the full-precision rings [B, Hkv, R, d]; tokens leaving the window are encoded into the
+    compressed cache (dense [B, Hkv, max_seq_len, row] or paged pools); seq_lens (device
+    int32 [B]) is advanced by n_new on the stream."""
+    B, Hkv, n_new, d = k_new.shape
+    p = _lib.WindowAppendParams()
+    p.cb_k, p.cb_v, p.rot_k, p.rot_v = cb_k.handle, cb_v.handle, rot_k.handle, rot_v.handle
+    p.batch, p.num_kv_heads, p.n_new = B, Hkv, n_new
+    p.k_new, p.v_new = k_new.data_ptr(), v_new.data_ptr()
+    p.k_window, p.v_window = k_window.data_ptr(), v_window.data_ptr()
+    p.window, p.window_dtype = int(k_window.shape[2]), dtype_code(k_window.dtype)
+    p.seq_lens = seq_lens.data_ptr()
+    p.k_packed, p.k_norms, p.v_packed, p.v_norms = (k_packed.data_ptr(), k_norms.data_ptr(), v_packed.data_ptr(),
+                                                    v_norms.data_ptr())
+    if max_seq_len is None:
+        max_seq_len = k_packed.shape[2]
+    p.max_seq_len = int(max_seq_len)
+    p.block_table = block_table.data_ptr() if block_table is not None else None
+    p.block_size = int(block_size)
+    p.max_blocks_per_seq = int(block_table.shape[1]) if block_table is not None else 0
+    p.batch_per_rot = int(batch_per_rot)
+    need = lib().tq_window_append_workspace_size(C.byref(p))
+    if need == 0:
+        raise TQError(None, _lib.last_error())
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k_new.device)
+    p.workspace, p.workspace_bytes = workspace.data_ptr(), int(workspace.numel())
+    check(lib().tq_window_append(C.byref(p), _stream(stream)))
+    return workspace

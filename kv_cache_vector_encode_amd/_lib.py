@@ -18,7 +18,8 @@ EXPORTS = (
     "tq_codebook_free", "tq_rotation_from_gaussian", "tq_rotation_from_matrix", "tq_rotation_compute",
     "tq_rotation_get", "tq_rotation_dims", "tq_rotation_free", "tq_rotation_hadamard", "tq_encode",
     "tq_encode_norm_corrected", "tq_decode",
-    "tq_attn_workspace_size", "tq_scores_compressed", "tq_attn_decode",
+    "tq_attn_workspace_size", "tq_scores_compressed", "tq_attn_decode", "tq_window_append_workspace_size",
+    "tq_window_append",
 )
 
 
@@ -33,6 +34,20 @@ class AttnParams(C.Structure):
         ("batch_per_rot", C.c_int32), ("scale", C.c_float),
         ("out", C.c_void_p), ("out_dtype", C.c_int32), ("lse", C.c_void_p),
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("num_splits", C.c_int32),
+        ("k_window", C.c_void_p), ("v_window", C.c_void_p), ("window", C.c_int32), ("window_dtype", C.c_int32),
+    ]
+
+
+class WindowAppendParams(C.Structure):
+    _fields_ = [
+        ("cb_k", C.c_void_p), ("cb_v", C.c_void_p), ("rot_k", C.c_void_p), ("rot_v", C.c_void_p),
+        ("batch", C.c_int32), ("num_kv_heads", C.c_int32), ("n_new", C.c_int32),
+        ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("k_window", C.c_void_p), ("v_window", C.c_void_p),
+        ("window", C.c_int32), ("window_dtype", C.c_int32), ("seq_lens", C.c_void_p),
+        ("k_packed", C.c_void_p), ("k_norms", C.c_void_p), ("v_packed", C.c_void_p), ("v_norms", C.c_void_p),
+        ("max_seq_len", C.c_int32), ("block_table", C.c_void_p), ("block_size", C.c_int32),
+        ("max_blocks_per_seq", C.c_int32), ("batch_per_rot", C.c_int32),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
     ]
 
 
@@ -69,6 +84,8 @@ def lib():
         "tq_attn_workspace_size": ([C.POINTER(AttnParams)], C.c_size_t),
         "tq_scores_compressed": ([C.POINTER(AttnParams), vp, vp], i32),
         "tq_attn_decode": ([C.POINTER(AttnParams), vp], i32),
+        "tq_window_append_workspace_size": ([C.POINTER(WindowAppendParams)], C.c_size_t),
+        "tq_window_append": ([C.POINTER(WindowAppendParams), vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)

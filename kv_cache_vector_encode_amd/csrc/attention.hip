@@ -43,6 +43,7 @@ struct AttnKArgs {
   float* sink;         // where masked lanes store scores (>= 64 floats)
   int32_t max_seq_len, block_size, bs_shift, mbps;
   int32_t B, Hq, Hkv, G, s_eff;
+  int32_t window;     // newest tokens held in the full-precision window (0: none)
   float scale;
   uint32_t ctk[16];   // K centroids as bf16 hi | lo << 16
   uint32_t ctv[8];    // V centroids as fp16, two per word
@@ -162,7 +163,9 @@ attn_kernel(AttnKArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.z, kvh = blockIdx.y;
   const int sidx = blockIdx.x * kAttnWaves + wave;
-  const int len = a.seq_lens ? max(0, min(a.seq_lens[b], a.max_seq_len)) : a.max_seq_len;
+  // compressed tokens: all but the newest min(L, window) of the sequence's L tokens
+  const int total = a.seq_lens ? max(0, min(a.seq_lens[b], a.max_seq_len)) : a.max_seq_len;
+  const int len = total - min(total, a.window);
   const int nblk = (len + 31) >> 5;
   const int per = (nblk + a.s_eff - 1) / a.s_eff;
   const int start = sidx * per * 32;
@@ -417,6 +420,140 @@ attn_kernel(AttnKArgs a) {
   }
 }
 
+// ---- recent-token window (KV Cache API page, TurboQuantKVCache.attention_scores / attend: the
+//      buffered newest tokens are scored exactly and their values added at full precision).
+// One workgroup per (sequence, KV head) computes the window's split partial (m, l, acc[d]) for
+// the group's query heads, in the original (unrotated) value domain, into the split slot after
+// the compressed ones; the merge adds it beside the rotated-back compressed accumulator.
+// Token at absolute position t sits at ring slot t mod R. Chunks of kWinChunk tokens: thread i
+// scores token i of the chunk against every head (queries in LDS), then an online softmax per
+// head, then thread k accumulates coordinate k over the chunk.
+struct WinKArgs {
+  const void* q;
+  const void* kw;
+  const void* vw;
+  const int32_t* seq_lens;
+  float* part;
+  int32_t q_dtype, w_dtype, window, max_seq_len;
+  int32_t B, Hq, Hkv, G, slot;   // slot: the split index the window partial is written to
+  float scale;
+};
+
+constexpr int kWinChunk = 256;
+
+__device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
+  if (dt == TQ_F32) return ((const float*)p)[i];
+  const uint32_t bits = ((const uint16_t*)p)[i];
+  return dt == TQ_BF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kWinChunk) window_kernel(WinKArgs a) {
+  constexpr int MAXG = 16;
+  __shared__ float qs[MAXG][D];
+  __shared__ float ps[MAXG][kWinChunk];
+  __shared__ float red[MAXG][kWinChunk / 64];
+  __shared__ float mrun[MAXG], lrun[MAXG], alpha[MAXG];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int G = a.G, R = a.window;
+  const int total = a.seq_lens ? max(0, min(a.seq_lens[b], a.max_seq_len)) : a.max_seq_len;
+  const int w = min(total, R), c = total - w;
+  for (int i = tid; i < G * D; i += blockDim.x) {
+    const int g = i / D, k = i - g * D;
+    qs[g][k] = load_elem(a.q, ((int64_t)b * a.Hq + kvh * G + g) * D + k, a.q_dtype);
+  }
+  if (tid < MAXG) {
+    mrun[tid] = -INFINITY;
+    lrun[tid] = 0.f;
+  }
+  float acc[MAXG];
+#pragma unroll
+  for (int g = 0; g < MAXG; ++g) acc[g] = 0.f;
+  __syncthreads();
+  const int64_t ring = ((int64_t)b * a.Hkv + kvh) * R;   // first row of this head's ring
+  for (int i0 = 0; i0 < w; i0 += kWinChunk) {
+    const int n = min(kWinChunk, w - i0);
+    // scores of token i0 + tid against every head
+    float s[MAXG];
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) s[g] = -INFINITY;
+    if (tid < n) {
+      const int64_t row = ring + (c + i0 + tid) % R;
+#pragma unroll
+      for (int g = 0; g < MAXG; ++g)
+        if (g < G) s[g] = 0.f;
+      for (int k = 0; k < D; ++k) {
+        const float kv = load_elem(a.kw, row * D + k, a.w_dtype);
+#pragma unroll
+        for (int g = 0; g < MAXG; ++g)
+          if (g < G) s[g] = fmaf(kv, qs[g][k], s[g]);
+      }
+#pragma unroll
+      for (int g = 0; g < MAXG; ++g)
+        if (g < G) s[g] *= a.scale;
+    }
+    // chunk max per head
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) {
+      if (g >= G) break;
+      float m = s[g];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, wave_xor(m, o));
+      if (lane == 0) red[g][wv] = m;
+    }
+    __syncthreads();
+    if (tid < G) {
+      float m = red[tid][0];
+      for (int j = 1; j < kWinChunk / 64; ++j) m = fmaxf(m, red[tid][j]);
+      const float mn = fmaxf(mrun[tid], m);
+      alpha[tid] = __expf(mrun[tid] - mn);   // 0 when mrun is -inf
+      mrun[tid] = mn;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) {
+      if (g >= G) break;
+      const float p = tid < n ? __expf(s[g] - mrun[g]) : 0.f;
+      ps[g][tid] = p;
+      float l = p;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) l += wave_xor(l, o);
+      if (lane == 0) red[g][wv] = l;
+    }
+    __syncthreads();   // the chunk's weights and per-wave sums are visible from here
+    if (tid < G) {
+      float l = 0.f;
+      for (int j = 0; j < kWinChunk / 64; ++j) l += red[tid][j];
+      lrun[tid] = lrun[tid] * alpha[tid] + l;
+    }
+    // values: thread k < D accumulates coordinate k over the chunk
+    if (tid < D) {
+#pragma unroll
+      for (int g = 0; g < MAXG; ++g)
+        if (g < G) acc[g] *= alpha[g];
+      for (int i = 0; i < n; ++i) {
+        const int64_t row = ring + (c + i0 + i) % R;
+        const float vv = load_elem(a.vw, row * D + tid, a.w_dtype);
+#pragma unroll
+        for (int g = 0; g < MAXG; ++g)
+          if (g < G) acc[g] = fmaf(ps[g][i], vv, acc[g]);
+      }
+    }
+    __syncthreads();
+  }
+  if (tid < D) {
+    for (int g = 0; g < G; ++g) {
+      float* P = a.part + (((int64_t)a.slot * a.B + b) * a.Hq + kvh * G + g) * (D + 2);
+      if (tid == 0) {
+        P[0] = mrun[g];
+        P[1] = lrun[g];
+      }
+      P[2 + tid] = acc[g];
+    }
+  }
+}
+
 // Query heads handled together by qrot_kernel / merge_kernel (a block reads each rotation entry
 // once for all of them); kept small so that there are enough blocks to hide load latency.
 constexpr int kHeadsPerBlock = 2;
@@ -465,8 +602,9 @@ __global__ void __launch_bounds__(D) qrot_kernel(const void* q, int q_dtype, con
 // Log-sum-exp merge of the token splits for up to 8 query heads of one sequence, then
 // o = Pi_V^T (sum_s acc_s e^(m_s - M)) / L. Thread k owns coordinate k.
 template <int D, int OUT>
-__global__ void __launch_bounds__(D) merge_kernel(const float* part, int s_eff, int B, int Hq, int bpr,
-                                                  const float* piv, int64_t rot_stride, void* out, float* lse) {
+__global__ void __launch_bounds__(D) merge_kernel(const float* part, int s_eff, int has_window, int B, int Hq,
+                                                  int bpr, const float* piv, int64_t rot_stride, void* out,
+                                                  float* lse) {
   constexpr int HB = kHeadsPerBlock, NW = D / 64;
   __shared__ float orot[HB][D];
   __shared__ float red[HB][NW];
@@ -482,7 +620,7 @@ __global__ void __launch_bounds__(D) merge_kernel(const float* part, int s_eff, 
   for (int h = 0; h < HB; ++h) {
     float m = -INFINITY;
     if (h < nh)
-      for (int s = k; s < s_eff; s += D) m = fmaxf(m, P0[(int64_t)s * sstride + h * (D + 2)]);
+      for (int s = k; s < s_eff + has_window; s += D) m = fmaxf(m, P0[(int64_t)s * sstride + h * (D + 2)]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, wave_xor(m, o));
     if (lane == 0) red[h][wv] = m;
@@ -516,6 +654,19 @@ __global__ void __launch_bounds__(D) merge_kernel(const float* part, int s_eff, 
       }
     }
   }
+  // the window's partial (original value domain) joins after the rotation back
+  float accw[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    accw[h] = 0.f;
+    if (has_window && h < nh && M[h] > -INFINITY) {
+      const float* Pw = P0 + (int64_t)s_eff * sstride + h * (D + 2);
+      const float ms = Pw[0];
+      const float w = ms > -INFINITY ? __expf(ms - M[h]) : 0.f;
+      lsum[h] = fmaf(w, Pw[1], lsum[h]);
+      accw[h] = w * Pw[2 + k];
+    }
+  }
 #pragma unroll
   for (int h = 0; h < HB; ++h) orot[h][k] = lsum[h] > 0.f ? acc[h] / lsum[h] : 0.f;
   __syncthreads();
@@ -533,6 +684,7 @@ __global__ void __launch_bounds__(D) merge_kernel(const float* part, int s_eff, 
 #pragma unroll
   for (int h = 0; h < HB; ++h) {
     if (h >= nh) continue;
+    if (lsum[h] > 0.f) o[h] += accw[h] / lsum[h];
     const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + k;
     if constexpr (OUT == TQ_F32)
       ((float*)out)[idx] = o[h];
@@ -564,7 +716,9 @@ AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu) {
   L.qrot_off = 0;
   size_t qbytes = align256((size_t)p->batch * p->num_q_heads * d * sizeof(float));
   L.part_off = qbytes;
-  L.total = qbytes + align256((size_t)kAttnWaves * splits * p->batch * p->num_q_heads * (d + 2) * sizeof(float));
+  // one partial per split, plus one for the recent-token window
+  const size_t nparts = (size_t)kAttnWaves * splits + (p->window > 0 ? 1 : 0);
+  L.total = qbytes + align256(nparts * p->batch * p->num_q_heads * (d + 2) * sizeof(float));
   if (L.total == 0) L.total = 256;
   return L;
 }
@@ -608,6 +762,7 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   a.Hkv = p->num_kv_heads;
   a.G = Hq / p->num_kv_heads;
   a.s_eff = lay.splits * kAttnWaves;
+  a.window = p->window;
   a.scale = p->scale;
   LevelArgs lk = make_levels(ck), lv = make_levels(cv);
   for (int j = 0; j < 16; ++j) a.ctk[j] = lk.centroid_bf16x2[j];
@@ -620,18 +775,39 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   }
   hipLaunchKernelGGL((attn_kernel<D, BK, BV, false, PAGE>), grid, dim3(kAttnWaves * 64), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int has_win = p->window > 0 ? 1 : 0;
+  if (has_win) {
+    WinKArgs w;
+    w.q = p->q;
+    w.kw = p->k_window;
+    w.vw = p->v_window;
+    w.seq_lens = p->seq_lens;
+    w.part = a.part;
+    w.q_dtype = p->q_dtype;
+    w.w_dtype = p->window_dtype;
+    w.window = p->window;
+    w.max_seq_len = p->max_seq_len;
+    w.B = B;
+    w.Hq = Hq;
+    w.Hkv = p->num_kv_heads;
+    w.G = a.G;
+    w.slot = a.s_eff;
+    w.scale = p->scale;
+    hipLaunchKernelGGL((window_kernel<D>), dim3((unsigned)p->num_kv_heads, (unsigned)B), dim3(kWinChunk), 0, st, w);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int64_t rs = (int64_t)(rv.f32_stride / sizeof(float));
   switch (p->out_dtype) {
     case TQ_F32:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_F32>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, B, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F32>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, has_win, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
       break;
     case TQ_BF16:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_BF16>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, B, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_BF16>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, has_win, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
       break;
     default:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_F16>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, B, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F16>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, has_win, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
   }
   return hipGetLastError();

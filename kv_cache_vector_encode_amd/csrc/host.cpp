@@ -732,6 +732,16 @@ static int check_attn(const tq_attn_params* p, bool scores_only, const char* who
       return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": block_size * max_blocks_per_seq < max_seq_len");
   }
   if (p->num_splits < 0) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": num_splits must be >= 0");
+  if (p->window < 0) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": window must be >= 0");
+  if (p->window > 0 && !scores_only) {
+    const int es = dtype_size(p->window_dtype);
+    if (!es)
+      return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": window_dtype is not supported; accepted TQ_F32, TQ_BF16, TQ_F16");
+    if (p->batch > 0 && (!p->k_window || !p->v_window))
+      return fail(TQ_ERR_NULL, std::string(who) + ": window > 0 needs k_window and v_window");
+    if (!aligned(p->k_window, es) || !aligned(p->v_window, es))
+      return fail(TQ_ERR_ALIGN, std::string(who) + ": k_window / v_window must be aligned to the element size");
+  }
   return TQ_OK;
 }
 
@@ -791,3 +801,120 @@ int tq_attn_decode(const tq_attn_params* p, tq_stream_t stream) {
 }
 
 }  // extern "C"
+
+// ---- recent-token window append --------------------------------------------------------------
+
+namespace {
+struct WinLayout {
+  size_t k_stage, v_stage, slot, total;
+};
+WinLayout win_layout(const tq_window_append_params* p, int d) {
+  auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = (size_t)std::max(p->batch, 0) * std::max(p->num_kv_heads, 0) * std::max(p->n_new, 0);
+  const size_t stage = a256(rows * d * dtype_size(p->window_dtype));
+  WinLayout L;
+  L.k_stage = 0;
+  L.v_stage = stage;
+  L.slot = 2 * stage;
+  L.total = 2 * stage + a256(rows * sizeof(int64_t));
+  if (L.total == 0) L.total = 256;
+  return L;
+}
+}  // namespace
+
+static int check_window(const tq_window_append_params* p, const char* who) {
+  const std::string W(who);
+  if (!p) return fail(TQ_ERR_NULL, W + ": params is NULL");
+  int s = check_pair(p->cb_k, p->rot_k, who);
+  if (s) return s;
+  if ((s = check_pair(p->cb_v, p->rot_v, who))) return s;
+  if (p->rot_v->rot.d != p->rot_k->rot.d) return fail(TQ_ERR_INVALID_ARG, W + ": K and V rotations have different d");
+  if (p->rot_v->rot.device != p->rot_k->rot.device)
+    return fail(TQ_ERR_NO_DEVICE, W + ": K and V rotations live on different devices");
+  if (p->batch < 0 || p->num_kv_heads <= 0 || p->n_new < 0)
+    return fail(TQ_ERR_INVALID_ARG, W + ": batch and n_new must be >= 0 and num_kv_heads > 0");
+  if (p->window < 0) return fail(TQ_ERR_INVALID_ARG, W + ": window must be >= 0");
+  if (!dtype_size(p->window_dtype))
+    return fail(TQ_ERR_INVALID_ARG, W + ": window_dtype is not supported; accepted TQ_F32, TQ_BF16, TQ_F16");
+  if (p->max_seq_len <= 0) return fail(TQ_ERR_INVALID_ARG, W + ": max_seq_len must be > 0");
+  if (p->batch_per_rot < 0) return fail(TQ_ERR_INVALID_ARG, W + ": batch_per_rot must be >= 0");
+  if (p->batch_per_rot > 0 && p->batch > 0) {
+    int64_t need = ((int64_t)p->batch + p->batch_per_rot - 1) / p->batch_per_rot;
+    if (need > p->rot_k->rot.n_rot || need > p->rot_v->rot.n_rot)
+      return fail(TQ_ERR_INVALID_ARG, W + ": batch / batch_per_rot exceeds the rotation stack");
+  }
+  if (p->block_table) {
+    if (p->block_size <= 0 || p->max_blocks_per_seq <= 0)
+      return fail(TQ_ERR_INVALID_ARG, W + ": paged layout needs block_size > 0 and max_blocks_per_seq > 0");
+    if ((int64_t)p->block_size * p->max_blocks_per_seq < p->max_seq_len)
+      return fail(TQ_ERR_INVALID_ARG, W + ": block_size * max_blocks_per_seq < max_seq_len");
+  }
+  return TQ_OK;
+}
+
+size_t tq_window_append_workspace_size(const tq_window_append_params* p) {
+  if (check_window(p, "tq_window_append_workspace_size")) return 0;
+  return win_layout(p, p->rot_k->rot.d).total;
+}
+
+int tq_window_append(const tq_window_append_params* p, tq_stream_t stream) {
+  const char* who = "tq_window_append";
+  const std::string W(who);
+  int s = check_window(p, who);
+  if (s) return s;
+  if (p->batch == 0 || p->n_new == 0) return TQ_OK;
+  if (!p->k_new || !p->v_new) return fail(TQ_ERR_NULL, W + ": k_new / v_new is NULL");
+  if (p->window > 0 && (!p->k_window || !p->v_window)) return fail(TQ_ERR_NULL, W + ": k_window / v_window is NULL");
+  if (!p->seq_lens) return fail(TQ_ERR_NULL, W + ": seq_lens is NULL");
+  if (!p->k_packed || !p->k_norms || !p->v_packed || !p->v_norms)
+    return fail(TQ_ERR_NULL, W + ": the compressed cache pointers must not be NULL");
+  if (!aligned(p->k_new, 16) || !aligned(p->v_new, 16) || !aligned(p->k_window, 16) || !aligned(p->v_window, 16))
+    return fail(TQ_ERR_ALIGN, W + ": k_new, v_new, k_window and v_window must be 16-byte aligned");
+  if (!aligned(p->k_packed, 8) || !aligned(p->v_packed, 8) || !aligned(p->k_norms, 4) || !aligned(p->v_norms, 4))
+    return fail(TQ_ERR_ALIGN, W + ": packed caches must be 8-byte and norms 4-byte aligned");
+  const int d = p->rot_k->rot.d;
+  const WinLayout lay = win_layout(p, d);
+  if (!p->workspace) return fail(TQ_ERR_WORKSPACE, W + ": workspace is NULL");
+  if (!aligned(p->workspace, 256)) return fail(TQ_ERR_ALIGN, W + ": workspace must be 256-byte aligned");
+  if (p->workspace_bytes < lay.total)
+    return fail(TQ_ERR_WORKSPACE, W + ": workspace_bytes = " + std::to_string(p->workspace_bytes) + " < " +
+                                      std::to_string(lay.total) + " needed");
+  if ((s = check_device(p->rot_k->rot, who))) return s;
+  WindowAppendLaunch L;
+  const int64_t vpr = p->batch_per_rot > 0 ? (int64_t)p->num_kv_heads * p->n_new * p->batch_per_rot : 0;
+  for (int side = 0; side < 2; ++side) {
+    EncodeLaunch& e = side == 0 ? L.enc_k : L.enc_v;
+    const tq_codebook_t* cb = side == 0 ? p->cb_k : p->cb_v;
+    e.rot = side == 0 ? &p->rot_k->rot : &p->rot_v->rot;
+    e.lv = make_levels(cb->cb);
+    if (!lut_covers_unit_range(e.lv))
+      return fail(TQ_ERR_INVALID_ARG, W + ": a codebook's boundaries are too close for the quantization table");
+    e.bits = cb->cb.bits;
+    e.x_dtype = p->window_dtype;
+    e.vectors_per_rot = vpr;
+    e.packed = side == 0 ? p->k_packed : p->v_packed;
+    e.norms = side == 0 ? p->k_norms : p->v_norms;
+    e.norm_correct = false;
+  }
+  uint8_t* ws = (uint8_t*)p->workspace;
+  L.k_new = p->k_new;
+  L.v_new = p->v_new;
+  L.k_ring = p->k_window;
+  L.v_ring = p->v_window;
+  L.k_stage = ws + lay.k_stage;
+  L.v_stage = ws + lay.v_stage;
+  L.slot = (int64_t*)(ws + lay.slot);
+  L.seq_lens = p->seq_lens;
+  L.block_table = p->block_table;
+  L.B = p->batch;
+  L.Hkv = p->num_kv_heads;
+  L.n_new = p->n_new;
+  L.R = p->window;
+  L.d = d;
+  L.elem = dtype_size(p->window_dtype);
+  L.max_seq_len = p->max_seq_len;
+  L.block_size = p->block_table ? p->block_size : 1;
+  L.mbps = p->max_blocks_per_seq;
+  L.stream = (hipStream_t)stream;
+  return hip_status(launch_window_append(L), who);
+}

@@ -87,6 +87,23 @@ struct EncodeLaunch {
 };
 hipError_t launch_encode(const EncodeLaunch& a);
 
+// Recent-token window append: stage the flushed rows, encode them (K and V), fill the rings.
+struct WindowAppendLaunch {
+  EncodeLaunch enc_k, enc_v;   // codebook, rotation, output cache and vectors_per_rot of each side
+  const void* k_new;
+  const void* v_new;
+  void* k_ring;
+  void* v_ring;
+  void* k_stage;
+  void* v_stage;
+  int64_t* slot;
+  int32_t* seq_lens;
+  const int32_t* block_table;
+  int B, Hkv, n_new, R, d, elem, max_seq_len, block_size, mbps;
+  hipStream_t stream;
+};
+hipError_t launch_window_append(const WindowAppendLaunch& a);
+
 struct DecodeLaunch {
   const Rotation* rot;
   LevelArgs lv;
