@@ -208,6 +208,22 @@ int tq_scores_compressed(const tq_attn_params* p, float* scores, tq_stream_t str
  * o = 0 and lse = -inf. */
 int tq_attn_decode(const tq_attn_params* p, tq_stream_t stream);
 
+/* ---- affine group quantization of values ---------------------------------------------------
+ * KV Cache API page, quantize_values / dequantize_values: per group of 32 consecutive
+ * elements of a vector, zero = min, scale = max((max - min) / (2^bits - 1), 1e-12) in float32,
+ * q = clamp(round_half_even((x - zero) / scale), 0, 2^bits - 1); the decode is
+ * x_hat = q * scale16 + zero16 (float32 product, then sum) with scale16 / zero16 the float16
+ * copies the encode stores. All float32 steps are IEEE, so codes, metadata and outputs are
+ * exact functions of the input. bits in {2, 3, 4, 8}; d a multiple of 32 (32..8192).
+ * Layouts (device): x [n, d] (row stride x_row_stride elements, 16-byte aligned rows);
+ * packed [n, d*bits/8] bytes, the 32 codes of a group as an LSB-first bitstream of 4*bits
+ * bytes (16-byte aligned base); scales / zeros float16 [n, d/32]; out [n, d] contiguous,
+ * 16-byte aligned. Launch on the current device; n = 0 is a no-op. */
+int tq_gq_encode(int d, int bits, const void* x, int x_dtype, int64_t n, int64_t x_row_stride,
+                 uint8_t* packed, uint16_t* scales, uint16_t* zeros, tq_stream_t stream);
+int tq_gq_decode(int d, int bits, const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                 int64_t n, void* out, int out_dtype, tq_stream_t stream);
+
 /* ---- recent-token window: append and flush ------------------------------------------------
  * KV Cache API page, TurboQuantKVCache.prefill / append: the newest R = window tokens of each
  * sequence stay at full precision; tokens leaving the window are compressed. One call appends

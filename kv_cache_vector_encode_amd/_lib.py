@@ -19,7 +19,7 @@ EXPORTS = (
     "tq_rotation_get", "tq_rotation_dims", "tq_rotation_free", "tq_rotation_hadamard", "tq_encode",
     "tq_encode_norm_corrected", "tq_decode",
     "tq_attn_workspace_size", "tq_scores_compressed", "tq_attn_decode", "tq_window_append_workspace_size",
-    "tq_window_append",
+    "tq_window_append", "tq_gq_encode", "tq_gq_decode",
 )
 
 
@@ -86,6 +86,8 @@ def lib():
         "tq_attn_decode": ([C.POINTER(AttnParams), vp], i32),
         "tq_window_append_workspace_size": ([C.POINTER(WindowAppendParams)], C.c_size_t),
         "tq_window_append": ([C.POINTER(WindowAppendParams), vp], i32),
+        "tq_gq_encode": ([i32, i32, vp, i32, i64, i64, vp, vp, vp, vp], i32),
+        "tq_gq_decode": ([i32, i32, vp, vp, vp, i64, vp, i32, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)

@@ -918,3 +918,82 @@ int tq_window_append(const tq_window_append_params* p, tq_stream_t stream) {
   L.stream = (hipStream_t)stream;
   return hip_status(launch_window_append(L), who);
 }
+
+// ---- affine group quantization of values --------------------------------------------------------
+
+static int gq_common(const char* who, int d, int bits, int64_t n) {
+  const std::string W(who);
+  if (d < 32 || d > 8192 || d % 32)
+    return fail(TQ_ERR_INVALID_ARG, W + ": d = " + std::to_string(d) + " is not supported; accepted multiples of 32 in 32..8192");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(TQ_ERR_INVALID_ARG, W + ": bits = " + std::to_string(bits) + " is not supported; accepted 2, 3, 4, 8");
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, W + ": n must be >= 0");
+  return TQ_OK;
+}
+
+int tq_gq_encode(int d, int bits, const void* x, int x_dtype, int64_t n, int64_t x_row_stride, uint8_t* packed,
+                 uint16_t* scales, uint16_t* zeros, tq_stream_t stream) {
+  const char* who = "tq_gq_encode";
+  const std::string W(who);
+  int s = gq_common(who, d, bits, n);
+  if (s) return s;
+  const int es = dtype_size(x_dtype);
+  if (!es)
+    return fail(TQ_ERR_INVALID_ARG, W + ": x_dtype = " + std::to_string(x_dtype) +
+                                        " is not supported; accepted TQ_F32 (0), TQ_BF16 (1), TQ_F16 (2)");
+  if (x_row_stride < d)
+    return fail(TQ_ERR_INVALID_ARG, W + ": x_row_stride = " + std::to_string(x_row_stride) + " is smaller than d");
+  if (n == 0) return TQ_OK;
+  if (!x || !packed || !scales || !zeros) return fail(TQ_ERR_NULL, W + ": x, packed, scales and zeros must not be NULL");
+  if (!aligned(x, 16) || (x_row_stride * es) % 16)
+    return fail(TQ_ERR_ALIGN, W + ": x and x_row_stride * element size must be 16-byte aligned");
+  if (!aligned(packed, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
+    return fail(TQ_ERR_ALIGN, W + ": packed must be 16-byte and scales / zeros 2-byte aligned");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(TQ_ERR_NO_DEVICE, W + ": no HIP device");
+  GqLaunch L;
+  L.encode = true;
+  L.bits = bits;
+  L.d = d;
+  L.dtype = x_dtype;
+  L.n = n;
+  L.x_row_stride = x_row_stride;
+  L.x = x;
+  L.packed = packed;
+  L.scales = scales;
+  L.zeros = zeros;
+  L.out = nullptr;
+  L.stream = (hipStream_t)stream;
+  return hip_status(launch_gq(L), who);
+}
+
+int tq_gq_decode(int d, int bits, const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t n,
+                 void* out, int out_dtype, tq_stream_t stream) {
+  const char* who = "tq_gq_decode";
+  const std::string W(who);
+  int s = gq_common(who, d, bits, n);
+  if (s) return s;
+  if (!dtype_size(out_dtype))
+    return fail(TQ_ERR_INVALID_ARG, W + ": out_dtype = " + std::to_string(out_dtype) +
+                                        " is not supported; accepted TQ_F32 (0), TQ_BF16 (1), TQ_F16 (2)");
+  if (n == 0) return TQ_OK;
+  if (!packed || !scales || !zeros || !out) return fail(TQ_ERR_NULL, W + ": packed, scales, zeros and out must not be NULL");
+  if (!aligned(packed, 16) || !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(out, 16))
+    return fail(TQ_ERR_ALIGN, W + ": packed and out must be 16-byte and scales / zeros 2-byte aligned");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(TQ_ERR_NO_DEVICE, W + ": no HIP device");
+  GqLaunch L;
+  L.encode = false;
+  L.bits = bits;
+  L.d = d;
+  L.dtype = out_dtype;
+  L.n = n;
+  L.x_row_stride = d;
+  L.x = nullptr;
+  L.packed = const_cast<uint8_t*>(packed);
+  L.scales = const_cast<uint16_t*>(scales);
+  L.zeros = const_cast<uint16_t*>(zeros);
+  L.out = out;
+  L.stream = (hipStream_t)stream;
+  return hip_status(launch_gq(L), who);
+}

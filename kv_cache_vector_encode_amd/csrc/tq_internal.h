@@ -104,6 +104,21 @@ struct WindowAppendLaunch {
 };
 hipError_t launch_window_append(const WindowAppendLaunch& a);
 
+// Affine group quantization of values (groups of 32): encode (x -> packed, scales, zeros) or
+// decode (packed, scales, zeros -> out).
+struct GqLaunch {
+  bool encode;
+  int bits, d, dtype;   // dtype: x_dtype (encode) or out_dtype (decode)
+  int64_t n, x_row_stride;
+  const void* x;
+  uint8_t* packed;
+  uint16_t* scales;
+  uint16_t* zeros;
+  void* out;
+  hipStream_t stream;
+};
+hipError_t launch_gq(const GqLaunch& a);
+
 struct DecodeLaunch {
   const Rotation* rot;
   LevelArgs lv;
