@@ -45,6 +45,9 @@ def parse():
                     help="untimed steps first; the GPU clocks take some tens of steps to settle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the 70B-class per-layer figures")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the figures of the recent-token window, Hadamard rotation, norm-corrected encode "
+                         "and group-quantized values")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for scaling HBM byte counters)")
     return ap.parse_args()
@@ -236,6 +239,8 @@ def main():
         "encode_vectors_per_s": round(2 * N / ((per["encode_k"] + per["encode_v"]) * 1e-3), 1),
         "attn_context_tokens_per_s": round(L * T / (per["attention"] * 1e-3), 1),
     }
+    nxt = None if args.no_next else next_rows(tq, ti, torch, dev, K, V, kp, kn, vp, vn, rot, ck, cv, q, kp4, kn4,
+                                              vp4, vn4, ws, L, H, T, d, per["attention"])
     del K, V, ko, vo
     torch.cuda.empty_cache()
     if args.copy_probe:
@@ -265,6 +270,7 @@ def main():
         "kernels_note": "per-call ms from an untimed calibration pass (3 steps, every call bracketed by events)",
         **extra,
         "long_context_layer": long,
+        "next_rows": nxt,
         "source_hash": src_hash,
     }
     if not args.no_cpu_baseline:
@@ -273,6 +279,73 @@ def main():
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
+
+
+def _time(torch, fn, reps: int = 10):
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def next_rows(tq, ti, torch, dev, K, V, kp, kn, vp, vn, rot, ck, cv, q, kp4, kn4, vp4, vn4, ws, L, H, T, d,
+              attn_ms):
+    """Figures for the rows beside the hot path, on the same Llama-3-8B-shaped cache:
+    the recent-token window (attention over 8064 compressed + 128 full-precision tokens per
+    sequence, and a one-token append that flushes one token per (layer, KV head)), the Hadamard
+    rotation and the norm-corrected encode (keys, 4 bits), and affine group quantization of the
+    values (2 bits, groups of 32)."""
+    N = L * H * T
+    out = {}
+    # Hadamard rotation: same encode kernel, a different Pi
+    g = torch.Generator().manual_seed(1)
+    signs = (torch.randint(0, 2, (L, d), generator=g) * 2 - 1).to(torch.int8).numpy()
+    rh = tq.Rotation.hadamard(d, signs)
+    ms = _time(torch, lambda: tq.encode(ck, rh, K, vectors_per_rot=H * T, packed=kp, norms=kn))
+    alg = N * (d * 2 + d // 2 + 4)
+    out["hadamard_encode_k"] = {"ms": round(ms, 4), "GB/s": round(alg / (ms * 1e-3) / 1e9, 1),
+                                "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    ms = _time(torch, lambda: tq.encode(ck, rot, K, vectors_per_rot=H * T, packed=kp, norms=kn,
+                                        norm_correction=True))
+    out["norm_corrected_encode_k"] = {"ms": round(ms, 4), "GB/s": round(alg / (ms * 1e-3) / 1e9, 1),
+                                      "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    tq.encode(ck, rot, K, vectors_per_rot=H * T, packed=kp, norms=kn)   # restore the keys' cache
+    # group-quantized values, 2 bits
+    gp = torch.empty(N, d // 4, dtype=torch.uint8, device=dev)
+    gs = torch.empty(N, d // 32, dtype=torch.float16, device=dev)
+    gz = torch.empty_like(gs)
+    go = torch.empty(N, d, dtype=torch.bfloat16, device=dev)
+    ms_e = _time(torch, lambda: tq.gq_encode(V, 2, packed=gp, scales=gs, zeros=gz))
+    ms_d = _time(torch, lambda: tq.gq_decode(gp, gs, gz, 2, out=go))
+    ae, ad = N * (d * 2 + d // 4 + 4 * (d // 32)), N * (d // 4 + 4 * (d // 32) + d * 2)
+    out["group_quant_v2"] = {"encode_ms": round(ms_e, 4), "encode_hbm_frac": round(ae / (ms_e * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "decode_ms": round(ms_d, 4), "decode_hbm_frac": round(ad / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del gp, gs, gz, go
+    # recent-token window of 128 tokens
+    R = 128
+    kw = K[:, :, T - R:].contiguous()
+    vw = V[:, :, T - R:].contiguous()
+    ao = torch.empty(L, q.shape[1], d, dtype=torch.bfloat16, device=dev)
+    lens = torch.full((L,), T, dtype=torch.int32, device=dev)
+    ms = _time(torch, lambda: tq.attn_decode(ck, rot, cv, rot, q, kp4, kn4, vp4, vn4, seq_lens=lens, batch_per_rot=1,
+                                             out=ao, k_window=kw, v_window=vw))
+    out["window_attention"] = {"window": R, "ms": round(ms, 4), "without_window_ms": round(attn_ms, 4),
+                               "context_tokens_per_s": round(L * T / (ms * 1e-3), 1)}
+    kn1 = K[:, :, :1].contiguous()
+    vn1 = V[:, :, :1].contiguous()
+    alen = torch.full((L,), T - 64, dtype=torch.int32, device=dev)
+    wsa = tq.window_append(ck, rot, cv, rot, kn1, vn1, kw, vw, alen, kp4, kn4, vp4, vn4, batch_per_rot=1)
+    reps = 20
+    alen.fill_(T - 64)
+    ms = _time(torch, lambda: tq.window_append(ck, rot, cv, rot, kn1, vn1, kw, vw, alen, kp4, kn4, vp4, vn4,
+                                               batch_per_rot=1, workspace=wsa), reps=reps)
+    out["window_append_1_token"] = {"batch": L, "kv_heads": H, "us": round(ms * 1e3, 2)}
+    return out
 
 
 def long_context_layer(tq, ti, torch, dev, reps: int = 10):

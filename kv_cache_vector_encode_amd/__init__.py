@@ -321,7 +321,7 @@ def window_append(cb_k: Codebook, rot_k: Rotation, cb_v: Codebook, rot_v: Rotati
     return workspace
 
 
-def gq_encode(x: torch.Tensor, bits: int, stream=None):
+def gq_encode(x: torch.Tensor, bits: int, stream=None, packed=None, scales=None, zeros=None):
     """Affine group quantization (groups of 32) of x [..., d] (float32/bfloat16/float16 on the GPU).
     Returns (packed uint8 [N, d*bits/8], scales float16 [N, d/32], zeros float16 [N, d/32])."""
     d = x.shape[-1]
@@ -329,18 +329,23 @@ def gq_encode(x: torch.Tensor, bits: int, stream=None):
     if x2.stride(-1) != 1:
         x2 = x2.contiguous()
     n = x2.shape[0]
-    packed = torch.empty(n, d * bits // 8, dtype=torch.uint8, device=x.device)
-    scales = torch.empty(n, d // 32, dtype=torch.float16, device=x.device)
-    zeros = torch.empty_like(scales)
+    if packed is None:
+        packed = torch.empty(n, d * bits // 8, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(n, d // 32, dtype=torch.float16, device=x.device)
+    if zeros is None:
+        zeros = torch.empty_like(scales)
     check(lib().tq_gq_encode(int(d), int(bits), _ptr(x2), dtype_code(x2.dtype), n, x2.stride(0), _ptr(packed),
                              _ptr(scales), _ptr(zeros), _stream(stream)))
     return packed, scales, zeros
 
 
 def gq_decode(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, bits: int,
-              out_dtype=torch.float32, stream=None):
+              out_dtype=torch.float32, stream=None, out=None):
     n, d = packed.shape[0], scales.shape[-1] * 32
-    out = torch.empty(n, d, dtype=out_dtype, device=packed.device)
+    if out is None:
+        out = torch.empty(n, d, dtype=out_dtype, device=packed.device)
+    out_dtype = out.dtype
     check(lib().tq_gq_decode(int(d), int(bits), _ptr(packed), _ptr(scales), _ptr(zeros), n, _ptr(out),
                              dtype_code(out_dtype), _stream(stream)))
     return out
