@@ -450,6 +450,7 @@ __device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
 template <int D>
 __global__ void __launch_bounds__(kWinChunk) window_kernel(WinKArgs a) {
   constexpr int MAXG = 16;
+  constexpr int NP = kWinChunk / D;   // token parts in the value phase (D <= kWinChunk)
   __shared__ float qs[MAXG][D];
   __shared__ float ps[MAXG][kWinChunk];
   __shared__ float red[MAXG][kWinChunk / 64];
@@ -483,11 +484,29 @@ __global__ void __launch_bounds__(kWinChunk) window_kernel(WinKArgs a) {
 #pragma unroll
       for (int g = 0; g < MAXG; ++g)
         if (g < G) s[g] = 0.f;
-      for (int k = 0; k < D; ++k) {
-        const float kv = load_elem(a.kw, row * D + k, a.w_dtype);
+      // the key row in 16-byte pieces, all loads in flight before the arithmetic
+      constexpr int NPIECE = D / 4;   // upper bound (float32); 16-bit rows use half of them
+      const int esz = a.w_dtype == TQ_F32 ? 4 : 2, per = 16 / esz, np = D / per;
+      const u32x4* kr = (const u32x4*)((const uint8_t*)a.kw + row * D * esz);
+      u32x4 pieces[NPIECE];
 #pragma unroll
-        for (int g = 0; g < MAXG; ++g)
-          if (g < G) s[g] = fmaf(kv, qs[g][k], s[g]);
+      for (int j = 0; j < NPIECE; ++j)
+        if (j < np) pieces[j] = kr[j];
+#pragma unroll
+      for (int j = 0; j < NPIECE; ++j) {
+        if (j >= np) break;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (e >= per) break;
+          const uint32_t w32 = pieces[j][per == 4 ? e : e >> 1];
+          const float kv = a.w_dtype == TQ_F32 ? __uint_as_float(w32)
+                           : a.w_dtype == TQ_BF16 ? ((e & 1) ? bf16_hi_to_f32(w32) : bf16_lo_to_f32(w32))
+                                                  : f16_bits_to_f32((e & 1) ? (w32 >> 16) : w32);
+          const int k = j * per + e;
+#pragma unroll
+          for (int g = 0; g < MAXG; ++g)
+            if (g < G) s[g] = fmaf(kv, qs[g][k], s[g]);
+        }
       }
 #pragma unroll
       for (int g = 0; g < MAXG; ++g)
@@ -527,14 +546,17 @@ __global__ void __launch_bounds__(kWinChunk) window_kernel(WinKArgs a) {
       for (int j = 0; j < kWinChunk / 64; ++j) l += red[tid][j];
       lrun[tid] = lrun[tid] * alpha[tid] + l;
     }
-    // values: thread k < D accumulates coordinate k over the chunk
-    if (tid < D) {
+    // values: thread (k = tid % D, part = tid / D) accumulates coordinate k over the chunk's
+    // tokens i = part, part + NP, ...; the parts are summed once at the end
 #pragma unroll
-      for (int g = 0; g < MAXG; ++g)
-        if (g < G) acc[g] *= alpha[g];
-      for (int i = 0; i < n; ++i) {
+    for (int g = 0; g < MAXG; ++g)
+      if (g < G) acc[g] *= alpha[g];
+    {
+      const int k = tid % D, part = tid / D;
+#pragma unroll 8
+      for (int i = part; i < n; i += NP) {
         const int64_t row = ring + (c + i0 + i) % R;
-        const float vv = load_elem(a.vw, row * D + tid, a.w_dtype);
+        const float vv = load_elem(a.vw, row * D + k, a.w_dtype);
 #pragma unroll
         for (int g = 0; g < MAXG; ++g)
           if (g < G) acc[g] = fmaf(ps[g][i], vv, acc[g]);
@@ -542,14 +564,22 @@ __global__ void __launch_bounds__(kWinChunk) window_kernel(WinKArgs a) {
     }
     __syncthreads();
   }
-  if (tid < D) {
+  // sum the parts: part 0 threads collect the others through LDS (reusing ps)
+  float* red2 = &ps[0][0];   // needs NP * G * D floats <= MAXG * kWinChunk
+  const int k = tid % D, part = tid / D;
+  if (part > 0)
+    for (int g = 0; g < G; ++g) red2[((part - 1) * G + g) * D + k] = acc[g];
+  __syncthreads();
+  if (part == 0) {
     for (int g = 0; g < G; ++g) {
+      float v = acc[g];
+      for (int pp = 1; pp < NP; ++pp) v += red2[((pp - 1) * G + g) * D + k];
       float* P = a.part + (((int64_t)a.slot * a.B + b) * a.Hq + kvh * G + g) * (D + 2);
-      if (tid == 0) {
+      if (k == 0) {
         P[0] = mrun[g];
         P[1] = lrun[g];
       }
-      P[2 + tid] = acc[g];
+      P[2 + k] = v;
     }
   }
 }

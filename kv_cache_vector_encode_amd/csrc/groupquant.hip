@@ -5,10 +5,10 @@
 // the page, so the kernels use correctly rounded float32 division and no fused multiply-add:
 // codes, metadata and reconstructions equal the float32 definition bit for bit.
 //
-// One thread owns one group: it reads the group's 32 elements with 16-byte loads, reduces
-// min / max, quantizes, and writes the 32 codes (4*b bytes, the LSB-first bitstream of the
-// key codes) and the two float16 values. Threads are laid out along the flattened groups, so a
-// wave covers 64 consecutive groups.
+// Encode: one thread owns one group: it reads the group's 32 elements with 16-byte loads,
+// reduces min / max, quantizes, and writes the 32 codes (4*b bytes, the LSB-first bitstream of
+// the key codes) and the two float16 values. Threads are laid out along the flattened groups,
+// so a wave covers 64 consecutive groups.
 #include "device_common.h"
 #include "tq_internal.h"
 
@@ -99,9 +99,13 @@ struct GqDecKArgs {
   int64_t n_groups;
 };
 
+// Decode: four threads per group, each producing 8 consecutive outputs, so that consecutive
+// threads write consecutive 16-byte pieces (fully coalesced stores).
 template <int BITS, int OUT>
 __global__ void __launch_bounds__(256) gq_decode_kernel(GqDecKArgs a) {
-  const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t gi = t >> 2;
+  const int q4 = (int)(t & 3);
   if (gi >= a.n_groups) return;
   constexpr int NW = kGqGroup * BITS / 32;
   uint32_t pk[NW];
@@ -109,31 +113,34 @@ __global__ void __launch_bounds__(256) gq_decode_kernel(GqDecKArgs a) {
 #pragma unroll
   for (int w = 0; w < NW; ++w) pk[w] = src[w];
   const float s = f16_bits_to_f32(a.scales[gi]), z = f16_bits_to_f32(a.zeros[gi]);
-  float o[kGqGroup];
+  float o[8];
 #pragma unroll
-  for (int k = 0; k < kGqGroup; ++k) {
-    const int pos = k * BITS;
-    uint32_t q = pk[pos >> 5] >> (pos & 31);
-    if ((pos & 31) + BITS > 32) q |= pk[(pos >> 5) + 1] << (32 - (pos & 31));
+  for (int e = 0; e < 8; ++e) {
+    const int pos = (8 * q4 + e) * BITS;   // q4 is not a compile-time value: index by cases
+    uint32_t q = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w == (pos >> 5)) q = pk[w] >> (pos & 31);
+    if ((pos & 31) + BITS > 32) {
+#pragma unroll
+      for (int w = 1; w < NW; ++w)
+        if (w == (pos >> 5) + 1) q |= pk[w] << (32 - (pos & 31));
+    }
     q &= (1u << BITS) - 1u;
-    o[k] = __fadd_rn(__fmul_rn((float)q, s), z);   // a product then a sum, as on the page
+    o[e] = __fadd_rn(__fmul_rn((float)q, s), z);   // a product then a sum, as on the page
   }
   if constexpr (OUT == TQ_F32) {
-    float* dst = (float*)a.out + gi * kGqGroup;
-#pragma unroll
-    for (int k = 0; k < kGqGroup; k += 4)
-      *(u32x4*)(dst + k) = u32x4{__float_as_uint(o[k]), __float_as_uint(o[k + 1]), __float_as_uint(o[k + 2]),
-                                 __float_as_uint(o[k + 3])};
+    float* dst = (float*)a.out + gi * kGqGroup + 8 * q4;
+    *(u32x4*)dst = u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+    *(u32x4*)(dst + 4) =
+        u32x4{__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])};
   } else {
-    uint16_t* dst = (uint16_t*)a.out + gi * kGqGroup;
+    uint16_t* dst = (uint16_t*)a.out + gi * kGqGroup + 8 * q4;
+    uint32_t w[4];
 #pragma unroll
-    for (int k = 0; k < kGqGroup; k += 8) {
-      uint32_t w[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        w[c] = OUT == TQ_BF16 ? pack_bf16x2(o[k + 2 * c], o[k + 2 * c + 1]) : pack_f16x2(o[k + 2 * c], o[k + 2 * c + 1]);
-      *(u32x4*)(dst + k) = u32x4{w[0], w[1], w[2], w[3]};
-    }
+    for (int c = 0; c < 4; ++c)
+      w[c] = OUT == TQ_BF16 ? pack_bf16x2(o[2 * c], o[2 * c + 1]) : pack_f16x2(o[2 * c], o[2 * c + 1]);
+    *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -177,6 +184,7 @@ hipError_t launch_gq(const GqLaunch& L) {
       default: return gq_enc_in<8>(L, k, grid);
     }
   }
+  const dim3 dgrid((unsigned)((4 * n_groups + 255) / 256));   // four threads per group
   GqDecKArgs k;
   k.packed = L.packed;
   k.scales = L.scales;
@@ -184,10 +192,10 @@ hipError_t launch_gq(const GqLaunch& L) {
   k.out = L.out;
   k.n_groups = n_groups;
   switch (L.bits) {
-    case 2: return gq_dec_out<2>(L, k, grid);
-    case 3: return gq_dec_out<3>(L, k, grid);
-    case 4: return gq_dec_out<4>(L, k, grid);
-    default: return gq_dec_out<8>(L, k, grid);
+    case 2: return gq_dec_out<2>(L, k, dgrid);
+    case 3: return gq_dec_out<3>(L, k, dgrid);
+    case 4: return gq_dec_out<4>(L, k, dgrid);
+    default: return gq_dec_out<8>(L, k, dgrid);
   }
 }
 
