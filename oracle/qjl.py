@@ -1,0 +1,69 @@
+"""QJL residual stage of keys and the asymmetric score estimator (float64 oracle; test
+infrastructure only).
+
+KV Cache API page (ginkgoq.github.io/TurboQuant/api/kv), TurboQuantCompressorV2:
+  __init__: the MSE stage uses max(b - 1, 1) bits (the same Lloyd-Max codebook family); the
+    sketch S is a d x d standard-normal draw from a CPU generator seeded seed + 10000.
+  compress, in order: n = ||x||; codes of x / (n + 1e-8) rotated, as the MSE compressor;
+    k_mse = (c[idx] Pi) * n; residual r = x - k_mse; residual norm ||r||; signs of S r,
+    a zero projection counting as +1.
+  asymmetric_attention_scores: <q, k> ~ <q, k_mse> + ||r|| sqrt(pi/2) / m <S q, signs>, m the
+    number of sketch rows (d); the attention scale multiplies the sum (TurboQuantKVCache).
+The module's header on the same page states the estimator is unbiased with variance O(1/d).
+
+Readings: norms and residual norms are kept in float32 (the page stores float16; the MSE
+codec here keeps float32 norms, reading 1 of the codec); k_mse uses the exact norm, as the
+page's compress does (it multiplies by the unrounded norm).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import codec
+
+
+def mse_bits(bits: int) -> int:
+    return max(bits - 1, 1)
+
+
+def encode(x, pi, S, centroids_mse):
+    """Returns (codes uint8 [N, d], norms float32 [N], signs int8 [N, d] in {-1, +1},
+    residual norms float32 [N], y float64 [N, d], projections float64 [N, d])."""
+    x = np.asarray(x, dtype=np.float64)
+    pi = np.asarray(pi, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    codes, _, y = codec.encode_codes(x, pi, centroids_mse)
+    n = np.sqrt(np.sum(x * x, axis=1))
+    c = np.asarray(centroids_mse, dtype=np.float64)
+    k_mse = (c[codes.astype(np.int64)] @ pi) * n[:, None]
+    r = x - k_mse
+    rn = np.sqrt(np.sum(r * r, axis=1))
+    proj = r @ S.T
+    signs = np.where(proj >= 0, 1, -1).astype(np.int8)
+    return codes, n.astype(np.float32), signs, rn.astype(np.float32), y, proj
+
+
+def pack_signs(signs):
+    """1 bit per coordinate, LSB-first (bit i of the stream = coordinate i), 1 = +1."""
+    return codec.pack_codes((np.asarray(signs) > 0).astype(np.uint8), 1)
+
+
+def unpack_signs(packed, d: int):
+    return np.where(codec.unpack_codes(packed, 1, d) > 0, 1, -1).astype(np.int8)
+
+
+def scores(q, codes, norms, signs, rnorms, pi, S, centroids_mse, scale: float):
+    """s[i, t] = scale * (<q_i, k_mse_t> + ||r_t|| sqrt(pi/2)/m <S q_i, signs_t>).
+    q [Q, d]; per-key arrays over T keys. Returns [Q, T]."""
+    q = np.asarray(q, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    c = np.asarray(centroids_mse, dtype=np.float64)
+    chat = c[np.asarray(codes).astype(np.int64)]
+    k_mse = (chat @ np.asarray(pi, dtype=np.float64)) * np.asarray(norms, dtype=np.float64)[:, None]
+    m = S.shape[0]
+    term1 = q @ k_mse.T
+    term2 = (q @ S.T) @ np.asarray(signs, dtype=np.float64).T
+    return scale * (term1 + math.sqrt(math.pi / 2) / m * term2 * np.asarray(rnorms, dtype=np.float64)[None, :])

@@ -11,6 +11,8 @@ Sources for the recipes:
     TurboQuantCompressorV2.__init__ / TurboQuantCompressorMSE.__init__).
   * Per-layer seeds: keys 42 + 7*layer, values that plus 500 (same page,
     CompressedKVStore.__init__).
+  * QJL sketch draw: d x d float32 standard normal from a CPU generator seeded seed + 10000
+    (same page, TurboQuantCompressorV2.__init__).
   * The 8-key example: torch.randn(8, 128) under manual_seed(0) (Turbo Attention
     (turbo-attn) PyPI page, "Install and try it").
 """

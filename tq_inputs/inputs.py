@@ -13,7 +13,7 @@ from dataclasses import dataclass, field
 import torch
 
 __all__ = [
-    "key_seed", "value_seed", "rotation_gaussian", "rotation_gaussians",
+    "key_seed", "value_seed", "rotation_gaussian", "rotation_gaussians", "qjl_sketch_gaussian",
     "example_keys", "codec_check_inputs", "LlamaCacheShape", "llama_layer_kv",
     "LongCacheShape", "long_cache_layer_kv", "AttnShape", "attn_inputs",
     "PagedShape", "paged_layout", "paged_layer_bits", "paged_layer_tokens", "paged_queries",
@@ -47,6 +47,12 @@ def rotation_gaussian(d: int, seed: int) -> torch.Tensor:
 def rotation_gaussians(d: int, seeds) -> torch.Tensor:
     """Stack of draws, one per seed: [len(seeds), d, d] float32."""
     return torch.stack([rotation_gaussian(d, s) for s in seeds])
+
+
+def qjl_sketch_gaussian(d: int, seed: int) -> torch.Tensor:
+    """The float32 d x d standard-normal sketch matrix of the QJL stage for a key compressor
+    seeded `seed`: a CPU generator seeded seed + 10000 (the key compressor's second draw)."""
+    return torch.randn(d, d, generator=generator("cpu", seed + 10000), dtype=torch.float32)
 
 
 # --- small codec workloads ----------------------------------------------------------
