@@ -17,7 +17,8 @@
  *   - Sizes are element counts unless named *_bytes. Pointers named "device" must be HIP
  *     device memory on the device the handles were created on; "host" pointers are CPU memory.
  *   - The caller owns every buffer. The library owns only the handles (freed by *_free).
- *     Hot-path calls (tq_encode, tq_decode, tq_scores_compressed, tq_attn_decode) never
+ *     Hot-path calls (tq_encode*, tq_qjl_encode, tq_decode, tq_scores_compressed,
+ *     tq_attn_decode, tq_gq_*, tq_window_append) never
  *     allocate device memory and never synchronize: they enqueue kernels on `stream`
  *     (a hipStream_t; NULL is the null stream) and return.
  *   - Return value: TQ_OK (0) or a negative tq_status. On error nothing is launched and
@@ -39,6 +40,7 @@ extern "C" {
 
 typedef struct tq_codebook tq_codebook_t;
 typedef struct tq_rotation tq_rotation_t;
+typedef struct tq_qjl tq_qjl_t;
 typedef void* tq_stream_t; /* hipStream_t */
 
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
@@ -134,6 +136,30 @@ int tq_encode_norm_corrected(const tq_codebook_t* cb, const tq_rotation_t* rot, 
                              const void* x, int x_dtype, int64_t n, int64_t x_row_stride,
                              uint8_t* packed, float* norms, const int64_t* slot_mapping, tq_stream_t stream);
 
+/* ---- QJL residual stage of keys -------------------------------------------------------------
+ * KV Cache API page (ginkgoq.github.io/TurboQuant/api/kv), TurboQuantCompressorV2: a key of b
+ * bits keeps the MSE codes of its direction at max(b - 1, 1) bits, its norm n, the residual
+ * norm ||r|| with r = x - n Pi^T c[idx], and the signs of S r for a d x d sketch S (a zero
+ * projection counts as +1); scores use <q, k> ~ n <Pi q, c[idx]> + ||r|| sqrt(pi/2)/d <S q, signs>.
+ *
+ * tq_qjl_create: sketch is host float32 [n_rot, d, d] row-major, one S_r per rotation of rot
+ * (the page draws S from a CPU generator seeded seed + 10000). The library forms
+ * M_r = S_r Pi_r^T in float64 and uploads M_r's MFMA tiles and S_r^T (float32) to rot's device.
+ * The handle refers to rot, which must outlive it; d in {64, 128, 256}. NULL on error. */
+tq_qjl_t* tq_qjl_create(const tq_rotation_t* rot, const float* sketch);
+void tq_qjl_free(tq_qjl_t* qjl);
+
+/* QJL encode of keys with qjl's rotation: packed / norms exactly as tq_encode with cb (the
+ * MSE codebook, 2..4 bits, same d), plus (device, row j as in tq_encode)
+ *   signs[j]:  d/8 bytes, bit i (LSB-first stream as the codes) = 1 iff (S_r r)_i >= 0;
+ *   rnorms[j]: ||r||_2 as float32.
+ * signs must be 16-byte aligned, rnorms 4-byte aligned; other arguments and errors as in
+ * tq_encode (norm correction does not apply). n = 0 is a no-op. */
+int tq_qjl_encode(const tq_codebook_t* cb, const tq_qjl_t* qjl, int64_t vectors_per_rot,
+                  const void* x, int x_dtype, int64_t n, int64_t x_row_stride,
+                  uint8_t* packed, float* norms, uint8_t* signs, float* rnorms,
+                  const int64_t* slot_mapping, tq_stream_t stream);
+
 /* ---- decode -------------------------------------------------------------------------------
  * Inverse of tq_encode: out[i] (device, dtype out_dtype, contiguous [n, d], 16-byte aligned)
  * = norms[j] * Pi_r^T c[codes of row j] with j = slot_mapping[i] (NULL = identity; a negative
@@ -192,13 +218,22 @@ typedef struct {
   const void* v_window;
   int32_t window;
   int32_t window_dtype;
+  /* QJL keys (optional; KV Cache API page, TurboQuantCompressorV2.asymmetric_attention_scores):
+   * with qjl_k != NULL the compressed keys were written by tq_qjl_encode with cb_k and qjl_k
+   * (built on rot_k), and every compressed score becomes
+   *   scale * (n_t <Pi_K q, c_K[idx_t]> + ||r_t|| sqrt(pi/2)/d <S q, signs_t>).
+   * k_signs (d/8 bytes per token, 16-byte aligned base) and k_rnorms (float32) follow the
+   * layout of k_packed / k_norms (dense or paged). qjl_k = NULL: plain MSE keys. */
+  const tq_qjl_t* qjl_k;
+  const uint8_t* k_signs;
+  const float* k_rnorms;
 } tq_attn_params;
 
 /* Bytes of workspace tq_attn_decode and tq_scores_compressed need for these parameters. */
 size_t tq_attn_workspace_size(const tq_attn_params* p);
 
-/* s[b, h, t] = scale * n_t * <Pi_K q[b, h], c_K[idx_t]> for t < seq_lens[b] (entries beyond
- * are left untouched). scores: device float32 [batch, num_q_heads, max_seq_len]. Uses the K
+/* s[b, h, t] = scale * n_t * <Pi_K q[b, h], c_K[idx_t]> (plus the QJL term with qjl_k) for
+ * t < seq_lens[b] (entries beyond are left untouched). scores: device float32 [batch, num_q_heads, max_seq_len]. Uses the K
  * fields of p (cb_v, rot_v, v_*, out, lse are ignored) and p->workspace. */
 int tq_scores_compressed(const tq_attn_params* p, float* scores, tq_stream_t stream);
 

@@ -17,7 +17,7 @@ import torch
 from . import _lib
 from ._lib import AttnParams, TQError, TQ_BF16, TQ_F16, TQ_F32, check, lib
 
-__all__ = ["Codebook", "Rotation", "encode", "decode", "scores_compressed", "attn_decode",
+__all__ = ["Codebook", "Rotation", "QJLSketch", "encode", "qjl_encode", "decode", "scores_compressed", "attn_decode",
            "attn_workspace_size", "packed_row_bytes", "TQError", "TQ_F32", "TQ_BF16", "TQ_F16",
            "dtype_code"]
 
@@ -163,6 +163,63 @@ class Rotation:
         self._h = None
 
 
+class QJLSketch:
+    """QJL sketch of a rotation stack: S_r (float32 [n_rot, d, d], one per rotation of `rot`),
+    uploaded by libtq as the tiles of S_r Pi_r^T and S_r^T. Keeps `rot` alive."""
+
+    def __init__(self, rot: Rotation, sketch):
+        s = torch.as_tensor(sketch).detach().to("cpu", torch.float32).contiguous()
+        if s.dim() == 2:
+            s = s[None]
+        if tuple(s.shape) != (rot.n_rot, rot.d, rot.d):
+            raise ValueError("sketch must be [n_rot, d, d] = [%d, %d, %d]" % (rot.n_rot, rot.d, rot.d))
+        h = lib().tq_qjl_create(rot.handle, C.c_void_p(s.data_ptr()))
+        if not h:
+            raise TQError(None, _lib.last_error())
+        self._h = C.c_void_p(h)
+        self.rot = rot
+        self.d, self.n_rot = rot.d, rot.n_rot
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        try:
+            if h is not None and _lib._LIB is not None:
+                _lib._LIB.tq_qjl_free(h)
+        except Exception:
+            pass
+        self._h = None
+
+
+def qjl_encode(cb: Codebook, qjl: QJLSketch, x: torch.Tensor, vectors_per_rot: int = 0, packed=None, norms=None,
+               signs=None, rnorms=None, slot_mapping=None, num_slots=None, stream=None):
+    """QJL key encode of x [..., d] with the MSE codebook cb (max(b-1, 1) bits for b-bit keys).
+    Returns (packed uint8 [rows, d*cb.bits/8], norms float32 [rows], signs uint8 [rows, d/8],
+    rnorms float32 [rows]); rows as in encode()."""
+    d = x.shape[-1]
+    x2 = x.reshape(-1, d) if x.dim() != 2 else x
+    if x2.stride(-1) != 1:
+        x2 = x2.contiguous()
+    n = x2.shape[0]
+    rows = n if slot_mapping is None else (num_slots if num_slots is not None else n)
+    dev = x.device
+    if packed is None:
+        packed = torch.empty(rows, packed_row_bytes(d, cb.bits), dtype=torch.uint8, device=dev)
+    if norms is None:
+        norms = torch.empty(rows, dtype=torch.float32, device=dev)
+    if signs is None:
+        signs = torch.empty(rows, d // 8, dtype=torch.uint8, device=dev)
+    if rnorms is None:
+        rnorms = torch.empty(rows, dtype=torch.float32, device=dev)
+    check(lib().tq_qjl_encode(cb.handle, qjl.handle, int(vectors_per_rot), _ptr(x2), dtype_code(x2.dtype), n,
+                              x2.stride(0), _ptr(packed), _ptr(norms), _ptr(signs), _ptr(rnorms),
+                              _ptr(slot_mapping), _stream(stream)))
+    return packed, norms, signs, rnorms
+
+
 def encode(cb: Codebook, rot: Rotation, x: torch.Tensor, vectors_per_rot: int = 0, packed=None, norms=None,
            slot_mapping=None, num_slots=None, stream=None, norm_correction: bool = False):
     """x: [..., d] on the GPU (float32/bfloat16/float16; rows may be strided).
@@ -200,7 +257,8 @@ def decode(cb: Codebook, rot: Rotation, packed: torch.Tensor, norms: torch.Tenso
 
 def _params(cb_k, rot_k, q, k_packed, k_norms, cb_v=None, rot_v=None, v_packed=None, v_norms=None,
             seq_lens=None, max_seq_len=None, block_table=None, block_size=0, batch_per_rot=0, scale=None,
-            out=None, lse=None, num_splits=0, num_kv_heads=None, k_window=None, v_window=None):
+            out=None, lse=None, num_splits=0, num_kv_heads=None, k_window=None, v_window=None, qjl=None,
+            k_signs=None, k_rnorms=None):
     B, Hq, d = q.shape
     p = AttnParams()
     p.cb_k, p.rot_k = cb_k.handle, rot_k.handle
@@ -230,6 +288,9 @@ def _params(cb_k, rot_k, q, k_packed, k_norms, cb_v=None, rot_v=None, v_packed=N
     if k_window is not None:
         p.k_window, p.v_window = k_window.data_ptr(), v_window.data_ptr()
         p.window, p.window_dtype = int(k_window.shape[2]), dtype_code(k_window.dtype)
+    if qjl is not None:
+        p.qjl_k = qjl.handle
+        p.k_signs, p.k_rnorms = k_signs.data_ptr(), k_rnorms.data_ptr()
     return p
 
 
@@ -250,13 +311,16 @@ def _workspace(p: AttnParams, device, workspace=None):
 
 def scores_compressed(cb_k: Codebook, rot_k: Rotation, q: torch.Tensor, k_packed: torch.Tensor,
                       k_norms: torch.Tensor, seq_lens=None, max_seq_len=None, block_table=None, block_size=0,
-                      batch_per_rot=0, scale=None, scores=None, num_kv_heads=None, workspace=None, stream=None):
+                      batch_per_rot=0, scale=None, scores=None, num_kv_heads=None, workspace=None, stream=None,
+                      qjl=None, k_signs=None, k_rnorms=None):
     """s[b, h, t] = scale * n_t <Pi_K q[b,h], c_K[idx_t]> for t < len_b, from the compressed keys.
     q: [B, Hq, d]; dense k_packed [B, Hkv, T, row] / k_norms [B, Hkv, T], or paged pools with a
-    block_table [B, max_blocks] (int32) and block_size. Returns float32 [B, Hq, T]."""
+    block_table [B, max_blocks] (int32) and block_size. Returns float32 [B, Hq, T].
+    qjl (a QJLSketch) with k_signs [.., d/8] / k_rnorms in the layout of k_packed / k_norms: QJL
+    keys, scored with the added term ||r_t|| sqrt(pi/2)/d <S q, signs_t>."""
     p = _params(cb_k, rot_k, q, k_packed, k_norms, seq_lens=seq_lens, max_seq_len=max_seq_len,
                 block_table=block_table, block_size=block_size, batch_per_rot=batch_per_rot, scale=scale,
-                num_kv_heads=num_kv_heads)
+                num_kv_heads=num_kv_heads, qjl=qjl, k_signs=k_signs, k_rnorms=k_rnorms)
     if scores is None:
         scores = torch.full((q.shape[0], q.shape[1], p.max_seq_len), float("nan"), dtype=torch.float32,
                             device=q.device)
@@ -269,17 +333,19 @@ def scores_compressed(cb_k: Codebook, rot_k: Rotation, q: torch.Tensor, k_packed
 def attn_decode(cb_k: Codebook, rot_k: Rotation, cb_v: Codebook, rot_v: Rotation, q: torch.Tensor,
                 k_packed, k_norms, v_packed, v_norms, seq_lens=None, max_seq_len=None, block_table=None,
                 block_size=0, batch_per_rot=0, scale=None, out=None, out_dtype=None, return_lse=False,
-                num_splits=0, num_kv_heads=None, workspace=None, stream=None, k_window=None, v_window=None):
+                num_splits=0, num_kv_heads=None, workspace=None, stream=None, k_window=None, v_window=None,
+                qjl=None, k_signs=None, k_rnorms=None):
     """Fused decode attention over the compressed cache; returns out [B, Hq, d] (and lse).
     k_window / v_window: optional rings [B, Hkv, R, d] holding each sequence's newest
     min(len, R) tokens at full precision (token t in slot t % R); seq_lens are then total
-    lengths and only the older positions are read from the compressed cache."""
+    lengths and only the older positions are read from the compressed cache.
+    qjl / k_signs / k_rnorms: QJL keys, as in scores_compressed."""
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if return_lse else None
     p = _params(cb_k, rot_k, q, k_packed, k_norms, cb_v, rot_v, v_packed, v_norms, seq_lens, max_seq_len,
                 block_table, block_size, batch_per_rot, scale, out, lse, num_splits, num_kv_heads, k_window,
-                v_window)
+                v_window, qjl, k_signs, k_rnorms)
     ws = _workspace(p, q.device, workspace)
     check(lib().tq_attn_decode(C.byref(p), _stream(stream)))
     out._tq_workspace = ws

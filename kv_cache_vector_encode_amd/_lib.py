@@ -19,7 +19,7 @@ EXPORTS = (
     "tq_rotation_get", "tq_rotation_dims", "tq_rotation_free", "tq_rotation_hadamard", "tq_encode",
     "tq_encode_norm_corrected", "tq_decode",
     "tq_attn_workspace_size", "tq_scores_compressed", "tq_attn_decode", "tq_window_append_workspace_size",
-    "tq_window_append", "tq_gq_encode", "tq_gq_decode",
+    "tq_window_append", "tq_gq_encode", "tq_gq_decode", "tq_qjl_create", "tq_qjl_free", "tq_qjl_encode",
 )
 
 
@@ -35,6 +35,7 @@ class AttnParams(C.Structure):
         ("out", C.c_void_p), ("out_dtype", C.c_int32), ("lse", C.c_void_p),
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("num_splits", C.c_int32),
         ("k_window", C.c_void_p), ("v_window", C.c_void_p), ("window", C.c_int32), ("window_dtype", C.c_int32),
+        ("qjl_k", C.c_void_p), ("k_signs", C.c_void_p), ("k_rnorms", C.c_void_p),
     ]
 
 
@@ -88,6 +89,9 @@ def lib():
         "tq_window_append": ([C.POINTER(WindowAppendParams), vp], i32),
         "tq_gq_encode": ([i32, i32, vp, i32, i64, i64, vp, vp, vp, vp], i32),
         "tq_gq_decode": ([i32, i32, vp, vp, vp, i64, vp, i32, vp], i32),
+        "tq_qjl_create": ([vp, vp], vp),
+        "tq_qjl_free": ([vp], None),
+        "tq_qjl_encode": ([vp, vp, i64, vp, i32, i64, i64, vp, vp, vp, vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
-SOURCES = ["host.cpp", "encode.hip", "decode.hip", "attention.hip", "window.hip", "groupquant.hip"]
+SOURCES = ["host.cpp", "encode.hip", "decode.hip", "attention.hip", "attention_qjl.hip", "window.hip",
+           "groupquant.hip", "qjl.hip"]
 
 
 def hipcc() -> str:

@@ -1,0 +1,907 @@
+// Scores and fused decode attention straight from the compressed cache (kernels and their
+// launch templates, shared by attention.hip and attention_qjl.hip).
+//
+// Method: s_t = scale <q, k_hat_t> (KV Cache API page, ginkgoq.github.io/TurboQuant/api/kv,
+// TurboQuantKVCache.attention_scores) and o = softmax(s) v_hat (TurboQuantKVCache.attend).
+// Because k_hat_t = n_t Pi_K^T c_K[idx_t], <q, k_hat_t> = n_t <Pi_K q, c_K[idx_t]>: the query is
+// rotated once and keys are never un-rotated (Turbo Attention PyPI page, "The codec": queries
+// rotated the same way, so scores need no un-rotation). Likewise sum_t p_t v_hat_t =
+// Pi_V^T sum_t p_t n^v_t c_V[idx^v_t]: values are accumulated in the rotated domain and
+// rotated back once per (sequence, head). Split-K over tokens with an online softmax and a
+// log-sum-exp merge plays the role of the pages' split-K paged decode kernel (same page,
+// "Kernels").
+//
+// Work layout. Kernel 1 rotates every query (fp32). Kernel 2: a wave owns one (sequence,
+// KV head, token range) and walks it 32 tokens at a time.
+//   scores: 16x16x32 bf16 MFMA in three hi/lo passes, A = centroids of 16 tokens (lane m+16g
+//     holds token m's codes for coordinates g*d/4 + 8kb .. +8), B = the G <= 16 rotated
+//     queries of the group (normalized by their max |entry|), D[token][head].
+//   QJL keys (TurboQuantCompressorV2.asymmetric_attention_scores on the same page) add
+//     ||r_t|| sqrt(pi/2)/d <S q, signs_t>: a second product with A = the token's signs as
+//     bf16 +-1 (exact; same lane layout as the codes) and B = S q split into bf16 hi + lo.
+//   softmax: per head running max m, running sum l; the value weights p_t n^v_t are kept
+//     relative to the running max V norm N so they lie in [0, 1] for fp16.
+//   P.V: 16x16x32 fp16 MFMA computing acc^T[coord][head]. The 32 tokens of a block are
+//     permuted so that lane (head, g) already holds, from the score step, the weights of the
+//     8 tokens it must supply (4g..4g+3 and 16+4g..16+4g+3): no shuffles. The A operand is
+//     the V centroids of those 8 tokens for coordinate group m (coordinates m*d/16 + t').
+// Kernel 3 merges the splits: M = max m_s, L = sum l_s e^(m_s-M), o = Pi_V^T (sum acc_s
+// e^(m_s-M)) / L, lse = M + log L.
+#pragma once
+
+#include <math.h>
+
+#include <cmath>
+
+#include "device_common.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+struct AttnKArgs {
+  const float* qrot;
+  const uint8_t* kp;
+  const float* kn;
+  const uint8_t* vp;
+  const float* vn;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  float* scores;
+  float* part;
+  float* sink;         // where masked lanes store scores (>= 64 floats)
+  int32_t max_seq_len, block_size, bs_shift, mbps;
+  int32_t B, Hq, Hkv, G, s_eff;
+  int32_t window;     // newest tokens held in the full-precision window (0: none)
+  float scale;
+  uint32_t ctk[16];   // K centroids as bf16 hi | lo << 16
+  uint32_t ctv[8];    // V centroids as fp16, two per word
+  // QJL keys
+  const uint8_t* ksg;  // sign rows, d/8 bytes per token
+  const float* krn;    // residual norms
+  const float* qsk;    // S q [B, Hq, d]
+  float qjl_c;         // sqrt(pi/2) / d
+};
+
+constexpr int kAttnWaves = 4;
+
+// Cache addressing: 0 = dense, 1 = paged with a power-of-two block size >= 16 (a 32-token
+// block then spans at most two pages, looked up once per block), 2 = any other paging.
+enum AttnPaging { kDense = 0, kPagedPow2 = 1, kPagedAny = 2 };
+
+// NB bits of a packed row starting at bit `bitoff`, shifted down to bit 0 of out[0]. Loads are
+// unconditional and stay inside the row of ROWB bytes.
+template <int NB, int ROWB>
+__device__ __forceinline__ void load_chunk(const uint8_t* row, int bitoff, uint32_t (&out)[(NB + 31) / 32]) {
+  constexpr int NW = (NB + 31) / 32;
+  if constexpr (NB % 32 == 0) {
+    // bitoff is a multiple of NB here, so the chunk is NB/8-byte aligned
+    const uint8_t* p = row + bitoff / 8;
+    if constexpr (NW == 4) {
+      const u32x4 v = *(const u32x4*)p;
+      out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+    } else if constexpr (NW == 2) {
+      const u32x2 v = *(const u32x2*)p;
+      out[0] = v[0]; out[1] = v[1];
+    } else {
+#pragma unroll
+      for (int k = 0; k < NW; ++k) out[k] = ((const uint32_t*)p)[k];
+    }
+  } else if constexpr (NB == 16) {
+    out[0] = *(const uint16_t*)(row + bitoff / 8);
+  } else if constexpr (NB == 8) {
+    out[0] = row[bitoff / 8];
+  } else {
+    constexpr int ROW_DW = ROWB / 4;
+    const uint32_t* rw = (const uint32_t*)row;
+    const int idx = bitoff >> 5;
+    const uint32_t sh = (uint32_t)bitoff & 31u;
+    uint32_t w[NW + 1];
+#pragma unroll
+    for (int k = 0; k <= NW; ++k) w[k] = rw[min(idx + k, ROW_DW - 1)];   // a clamped word only feeds bits past NB
+#pragma unroll
+    for (int k = 0; k < NW; ++k) out[k] = funnel(w[k + 1], w[k], sh);
+  }
+}
+
+// PB bits at bit `pos` of w (pos is a compile-time constant after unrolling)
+template <int PB, int NW>
+__device__ __forceinline__ uint32_t bits_at(const uint32_t (&w)[NW], int pos) {
+  uint32_t v;
+  if ((pos & 31) + PB <= 32)
+    v = w[pos >> 5] >> (pos & 31);
+  else
+    v = funnel(w[(pos >> 5) + 1], w[pos >> 5], (uint32_t)(pos & 31));
+  return v & ((1u << PB) - 1u);
+}
+
+// a, b: up to eight 2-bit codes each (low 16 bits). Returns z with nibble t = a_t | b_t << 2,
+// so byte j of z holds codes 2j and 2j+1 of both (bytes of a and b interleaved, then two
+// swaps of bit fields inside each 16-bit half).
+__device__ __forceinline__ uint32_t interleave2(uint32_t a, uint32_t b) {
+  uint32_t y = (a & 0xffu) | ((b & 0xffu) << 8) | ((a & 0xff00u) << 8) | ((b & 0xff00u) << 16);
+  uint32_t t = (y ^ (y >> 4)) & 0x00f000f0u;
+  y ^= t ^ (t << 4);
+  t = (y ^ (y >> 2)) & 0x0c0c0c0cu;
+  y ^= t ^ (t << 2);
+  return y;
+}
+
+// register budget: waves per SIMD 4 at d=64 (<= 128 registers; 3 with the QJL operands), 3 at
+// d=128 (<= 168), 2 at d=256 (twice the accumulators)
+template <int D, bool QJL>
+constexpr int attn_wpe() { return D == 256 ? 2 : D == 128 ? 3 : (QJL ? 3 : 4); }
+
+template <int D, int BK, int BV, bool SCORES, int PAGE, bool QJL>
+__global__ void __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(attn_wpe<D, QJL>())))
+attn_kernel(AttnKArgs a) {
+  constexpr int KB = D / 32;            // K blocks of the score MFMA
+  constexpr int TV = D / 16;            // output tiles of the P.V MFMA
+  constexpr int NBK = D * BK / 4;       // bits of a lane's K chunk
+  constexpr int NBV = D * BV / 16;      // bits of a lane's V segment
+  constexpr int NWK = (NBK + 31) / 32, NWV = (NBV + 31) / 32;
+  constexpr int NBS = D / 4;            // bits of a lane's sign chunk (QJL keys)
+  constexpr int NWS = (NBS + 31) / 32;
+  constexpr int ROWK = D * BK / 8, ROWV = D * BV / 8;
+  constexpr int PK = 2 * BK;            // bits of a pair of K codes
+  constexpr int KTAB = 1 << PK;
+  constexpr int VTAB = BV == 2 ? 512 : (1 << (2 * BV));
+  // Code -> operand tables: a pair of K codes -> two bf16 hi (tkh) / lo (tkl) halves; for
+  // 2-bit V a byte of interleaved codes (two coordinates of two tokens) -> two fp16 pairs,
+  // else a pair of V codes (one coordinate of two tokens) -> one fp16 pair.
+  __shared__ uint32_t tkh[KTAB], tkl[KTAB];
+  __shared__ uint32_t tv[SCORES ? 1 : VTAB];
+  __shared__ u32x4 sq[2 * KB * 64];   // query B operands [hi, lo][kb][lane], shared by the waves
+  __shared__ u32x4 ssq[QJL ? 2 * KB * 64 : 1];   // the same for S q (QJL keys)
+  {
+    // centroids straight from the kernel-argument segment (`a` is the only argument)
+    const char* ka = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+    const uint32_t* kk = (const uint32_t*)(ka + offsetof(AttnKArgs, ctk));
+    const uint32_t* kv = (const uint32_t*)(ka + offsetof(AttnKArgs, ctv));
+    constexpr uint32_t MK = (1u << BK) - 1u, MV = (1u << BV) - 1u;
+    for (int j = threadIdx.x; j < KTAB; j += blockDim.x) {
+      const uint32_t c0 = kk[j & MK], c1 = kk[j >> BK];
+      tkh[j] = (c0 & 0xffffu) | (c1 << 16);
+      tkl[j] = (c0 >> 16) | (c1 & 0xffff0000u);
+    }
+    if constexpr (!SCORES) {
+      auto cv = [&](uint32_t k) -> uint32_t { return (kv[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
+      if constexpr (BV == 2) {
+        for (int j = threadIdx.x; j < 256; j += blockDim.x) {
+          tv[2 * j] = cv(j & 3u) | (cv((j >> 2) & 3u) << 16);
+          tv[2 * j + 1] = cv((j >> 4) & 3u) | (cv((uint32_t)j >> 6) << 16);
+        }
+      } else {
+        for (int j = threadIdx.x; j < VTAB; j += blockDim.x) tv[j] = cv(j & MV) | (cv((uint32_t)j >> BV) << 16);
+      }
+    }
+  }
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int sidx = blockIdx.x * kAttnWaves + wave;
+  // compressed tokens: all but the newest min(L, window) of the sequence's L tokens
+  const int total = a.seq_lens ? max(0, min(a.seq_lens[b], a.max_seq_len)) : a.max_seq_len;
+  const int len = total - min(total, a.window);
+  const int nblk = (len + 31) >> 5;
+  const int per = (nblk + a.s_eff - 1) / a.s_eff;
+  const int start = sidx * per * 32;
+  const int end = min(len, start + per * 32);
+  const int last = end - 1;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const bool head_ok = n16 < a.G;
+  const int h = kvh * a.G + (head_ok ? n16 : 0);
+
+  // ---- rotated query as the score MFMA's B operand: lane (head n16, g = q4) holds
+  //      q'[h][q4*d/4 + 8kb + e] / qmax for kb < KB, e < 8, split into bf16 hi + lo. Scores
+  //      take three bf16 passes (q_hi c_hi + q_hi c_lo + q_lo c_hi, ~2^-17 relative): with
+  //      large logits (outlier tokens) softmax turns score errors into weight errors, so fp16
+  //      (2^-11) operands are not enough there. All waves of the workgroup serve the same
+  //      (sequence, KV head); wave 0 leaves the operands in LDS and the loop reads them there.
+  auto query_operands = [&](const float* src, u32x4* dst) -> float {
+    float qv[D / 4];
+    const float* qp = src + ((int64_t)b * a.Hq + h) * D + q4 * (D / 4);
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      qv[i] = head_ok ? qp[i] : 0.f;
+      mx = fmaxf(mx, fabsf(qv[i]));
+    }
+    mx = fmaxf(mx, wave_xor(mx, 16));
+    mx = fmaxf(mx, wave_xor(mx, 32));
+    const float qm = mx > 0.f ? mx : 1.f;
+    const float inv = 1.0f / qm;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float v0 = qv[8 * kb + 2 * c] * inv, v1 = qv[8 * kb + 2 * c + 1] * inv;
+        const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
+        const uint32_t l0 = f32_to_bf16_bits(v0 - bf16_bits_to_f32(h0));
+        const uint32_t l1 = f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1));
+        if (wave == 0) {
+          ((uint32_t*)&dst[kb * 64 + lane])[c] = h0 | (h1 << 16);
+          ((uint32_t*)&dst[(KB + kb) * 64 + lane])[c] = l0 | (l1 << 16);
+        }
+      }
+    return qm;
+  };
+  const float qmax = query_operands(a.qrot, sq);
+  float sqmax = 0.f;
+  if constexpr (QJL) sqmax = query_operands(a.qsk, ssq);
+  __syncthreads();
+  const float sc = qmax * a.scale;
+  const float sc2 = sqmax * a.scale * a.qjl_c;
+
+  float m_run = -INFINITY, l_run = 0.f, n_run = 0.f;
+  f32x4 acc[TV];
+#pragma unroll
+  for (int t = 0; t < TV; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- operands of one 32-token block, fetched one block ahead of their use. This lane
+  //      needs the K codes of token t0 + 16*tile + n16 (score A operand row n16) and, for the
+  //      8 tokens tok(e) = t0 + (e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4) whose scores land in
+  //      it and whose weights it supplies to P.V, their K norms, V norms and V codes. Tokens
+  //      past the end are clamped to the last one (and masked later): every load is issued
+  //      unconditionally, so the in-order memory counter waits only for what is needed.
+  struct KBlk {
+    uint32_t kc[2][NWK];
+    uint32_t sg[QJL ? 2 : 1][NWS];
+  };
+  struct VBlk {
+    float kn[8], vn[SCORES ? 1 : 8], rn[QJL ? 8 : 1];
+    uint32_t seg[SCORES ? 1 : 8][NWV];
+  };
+  const int64_t dense_base = ((int64_t)b * a.Hkv + kvh) * a.max_seq_len;
+  const int32_t* btab = a.block_table + (int64_t)b * a.mbps;
+  auto pages = [&](int t0, int& p0, int& p1) {
+    if constexpr (PAGE == kPagedPow2) {
+      p0 = btab[min(t0, last) >> a.bs_shift];
+      p1 = btab[min(t0 + 31, last) >> a.bs_shift];
+    } else {
+      p0 = p1 = 0;
+    }
+  };
+  auto row_of = [&](int tt, int t0, int p0, int p1) -> int64_t {
+    if constexpr (PAGE == kDense) {
+      return dense_base + tt;
+    } else if constexpr (PAGE == kPagedPow2) {
+      const int phys = ((tt >> a.bs_shift) == (t0 >> a.bs_shift)) ? p0 : p1;
+      return (((int64_t)phys * a.Hkv + kvh) << a.bs_shift) + (tt & (a.block_size - 1));
+    } else {
+      const int blk = tt / a.block_size;
+      return ((int64_t)btab[blk] * a.Hkv + kvh) * a.block_size + (tt - blk * a.block_size);
+    }
+  };
+  auto tok = [&](int t0, int e) { return min(t0 + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4)), last); };
+  auto fetch_k = [&](int t0, int p0, int p1, KBlk& B) {
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      const int tk = min(t0 + 16 * tile + n16, last);
+      const int64_t row = row_of(tk, t0, p0, p1);
+      load_chunk<NBK, ROWK>(a.kp + row * ROWK, q4 * NBK, B.kc[tile]);
+      if constexpr (QJL) load_chunk<NBS, D / 8>(a.ksg + row * (D / 8), q4 * NBS, B.sg[tile]);
+    }
+  };
+  auto fetch_v = [&](int t0, int p0, int p1, VBlk& B) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t row = row_of(tok(t0, e), t0, p0, p1);
+      B.kn[e] = a.kn[row];
+      if constexpr (QJL) B.rn[e] = a.krn[row];
+      if constexpr (!SCORES) {
+        B.vn[e] = a.vn[row];
+        load_chunk<NBV, ROWV>(a.vp + row * ROWV, n16 * NBV, B.seg[e]);
+      }
+    }
+  };
+
+  // Key codes are fetched one block ahead; a block's norms and value codes are fetched at the
+  // start of its own iteration, ahead of the score MFMAs that precede their use.
+  if (start < end) {
+    KBlk cur;
+    int p0, p1, np0, np1;
+    pages(start, p0, p1);
+    fetch_k(start, p0, p1, cur);
+    pages(start + 32, np0, np1);
+    wait_vmem_all();
+    uint32_t qoff = (uint32_t)lane * 16u;
+
+    for (int t0 = start; t0 < end; t0 += 32) {
+      VBlk vb;
+      fetch_v(t0, p0, p1, vb);
+      KBlk nxt;
+      fetch_k(t0 + 32, np0, np1, nxt);
+      int nnp0, nnp1;
+      pages(t0 + 64, nnp0, nnp1);
+      // query operands are re-read from LDS each block rather than held in 8*KB registers
+      asm volatile("" : "+v"(qoff));
+      const char* qbase = (const char*)sq + qoff;
+      const char* sbase = (const char*)ssq + qoff;
+
+      // ---- scores of the block's two 16-token tiles
+      float s[8];
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          u32x4 akh, akl;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t idx = bits_at<PK>(cur.kc[tile], (4 * kb + c) * PK);
+            akh[c] = tkh[idx];
+            akl[c] = tkl[idx];
+          }
+          const u32x4 qh = *(const u32x4*)(qbase + kb * 1024);
+          const u32x4 ql = *(const u32x4*)(qbase + (KB + kb) * 1024);
+          S = mfma16_bf16(akh, qh, S);
+          S = mfma16_bf16(akl, qh, S);
+          S = mfma16_bf16(akh, ql, S);
+        }
+        // QJL term: <S q, signs> with the signs as exact bf16 +-1 (bit 1 -> +1) against S q hi + lo
+        f32x4 S2 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (QJL) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const uint32_t u = bits_at<8>(cur.sg[tile], 8 * kb);
+            u32x4 as;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t w = u >> (2 * c);
+              as[c] = 0xBF80BF80u ^ ((w & 1u) << 15) ^ ((w & 2u) << 30);
+            }
+            const u32x4 sh = *(const u32x4*)(sbase + kb * 1024);
+            const u32x4 sl = *(const u32x4*)(sbase + (KB + kb) * 1024);
+            S2 = mfma16_bf16(as, sh, S2);
+            S2 = mfma16_bf16(as, sl, S2);
+          }
+        }
+        // D layout: lane (head n16, q4) register r = token t0 + 16*tile + 4*q4 + r = tok(4*tile + r)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tt = t0 + 16 * tile + 4 * q4 + r;
+          const bool ok = tt < end;
+          float v = S[r] * sc * vb.kn[4 * tile + r];
+          if constexpr (QJL) v = fmaf(S2[r] * sc2, vb.rn[4 * tile + r], v);
+          v = ok ? v : -INFINITY;
+          if constexpr (SCORES) {
+            float* dst = ok && head_ok ? a.scores + ((int64_t)b * a.Hq + h) * a.max_seq_len + tt : a.sink + lane;
+            *dst = v;
+          }
+          s[4 * tile + r] = v;
+        }
+      }
+      if constexpr (!SCORES) {
+        // ---- online softmax; weights p_t n^v_t / N with N the running max V norm
+        float mb = s[0], nb = vb.vn[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) {
+          mb = fmaxf(mb, s[e]);
+          nb = fmaxf(nb, vb.vn[e]);
+        }
+        mb = fmaxf(mb, wave_xor(mb, 16));
+        mb = fmaxf(mb, wave_xor(mb, 32));
+        nb = fmaxf(nb, wave_xor(nb, 16));
+        nb = fmaxf(nb, wave_xor(nb, 32));
+        const float m_new = fmaxf(m_run, mb);
+        const float n_new = fmaxf(n_run, nb);
+        const float al = __expf(m_run - m_new);
+        const float inv_n = n_new > 0.f ? 1.0f / n_new : 0.f;
+        const float a_acc = al * n_run * inv_n;
+        float lsum = 0.f;
+        u32x4 bw;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float e0 = __expf(s[2 * c] - m_new), e1 = __expf(s[2 * c + 1] - m_new);
+          lsum += e0 + e1;
+          bw[c] = pack_f16x2(e0 * vb.vn[2 * c] * inv_n, e1 * vb.vn[2 * c + 1] * inv_n);
+        }
+        l_run = l_run * al + lsum;
+        m_run = m_new;
+        n_run = n_new;
+        // the running maxima settle after a few blocks: skip the rescale once no lane needs it
+        if (__any(a_acc != 1.0f)) {
+#pragma unroll
+          for (int t = 0; t < TV; ++t) acc[t] = acc[t] * a_acc;
+        }
+
+        // ---- P.V: lane (coordinate group m = n16, token group g = q4), same 8 tokens; tile t
+        //      is coordinate m*d/16 + t, component c the tokens tok(2c), tok(2c+1)
+        if constexpr (BV == 2) {
+#pragma unroll
+          for (int ch = 0; ch < (NBV + 15) / 16; ++ch) {   // 8 codes = 8 tiles per 16-bit chunk
+            uint32_t z[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              z[c] = interleave2((vb.seg[2 * c][0] >> (16 * ch)) & 0xffffu, (vb.seg[2 * c + 1][0] >> (16 * ch)) & 0xffffu);
+#pragma unroll
+            for (int j = 0; j < 4 && 8 * ch + 2 * j < TV; ++j) {
+              u32x4 av0, av1;
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const u32x2 e = *(const u32x2*)&tv[2 * ((z[c] >> (8 * j)) & 255u)];
+                av0[c] = e[0];
+                av1[c] = e[1];
+              }
+              acc[8 * ch + 2 * j] = mfma16_f16(av0, bw, acc[8 * ch + 2 * j]);
+              acc[8 * ch + 2 * j + 1] = mfma16_f16(av1, bw, acc[8 * ch + 2 * j + 1]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < TV; ++t) {
+            u32x4 av;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              av[c] = tv[bits_at<BV>(vb.seg[2 * c], BV * t) | (bits_at<BV>(vb.seg[2 * c + 1], BV * t) << BV)];
+            acc[t] = mfma16_f16(av, bw, acc[t]);
+          }
+        }
+      }
+      cur = nxt;
+      p0 = np0;
+      p1 = np1;
+      np0 = nnp0;
+      np1 = nnp1;
+    }
+  }
+
+  if constexpr (!SCORES) {
+    float lt = l_run;
+    lt += wave_xor(lt, 16);
+    lt += wave_xor(lt, 32);
+    if (head_ok) {
+      float* P = a.part + (((int64_t)sidx * a.B + b) * a.Hq + h) * (D + 2);
+      if (q4 == 0) {
+        P[0] = m_run;
+        P[1] = lt;
+      }
+      // D layout of the P.V MFMA: lane (head n16, q4) register r = coordinate group 4*q4 + r
+#pragma unroll
+      for (int t = 0; t < TV; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P[2 + (4 * q4 + r) * (D / 16) + t] = acc[t][r] * n_run;
+    }
+  }
+}
+
+// ---- recent-token window (KV Cache API page, TurboQuantKVCache.attention_scores / attend: the
+//      buffered newest tokens are scored exactly and their values added at full precision).
+// One workgroup per (sequence, KV head) computes the window's split partial (m, l, acc[d]) for
+// the group's query heads, in the original (unrotated) value domain, into the split slot after
+// the compressed ones; the merge adds it beside the rotated-back compressed accumulator.
+// Token at absolute position t sits at ring slot t mod R. Chunks of kWinChunk tokens: thread i
+// scores token i of the chunk against every head (queries in LDS), then an online softmax per
+// head, then thread k accumulates coordinate k over the chunk.
+struct WinKArgs {
+  const void* q;
+  const void* kw;
+  const void* vw;
+  const int32_t* seq_lens;
+  float* part;
+  int32_t q_dtype, w_dtype, window, max_seq_len;
+  int32_t B, Hq, Hkv, G, slot;   // slot: the split index the window partial is written to
+  float scale;
+};
+
+constexpr int kWinChunk = 256;
+
+__device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
+  if (dt == TQ_F32) return ((const float*)p)[i];
+  const uint32_t bits = ((const uint16_t*)p)[i];
+  return dt == TQ_BF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kWinChunk) window_kernel(WinKArgs a) {
+  constexpr int MAXG = 16;
+  constexpr int NP = kWinChunk / D;   // token parts in the value phase (D <= kWinChunk)
+  __shared__ float qs[MAXG][D];
+  __shared__ float ps[MAXG][kWinChunk];
+  __shared__ float red[MAXG][kWinChunk / 64];
+  __shared__ float mrun[MAXG], lrun[MAXG], alpha[MAXG];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int G = a.G, R = a.window;
+  const int total = a.seq_lens ? max(0, min(a.seq_lens[b], a.max_seq_len)) : a.max_seq_len;
+  const int w = min(total, R), c = total - w;
+  for (int i = tid; i < G * D; i += blockDim.x) {
+    const int g = i / D, k = i - g * D;
+    qs[g][k] = load_elem(a.q, ((int64_t)b * a.Hq + kvh * G + g) * D + k, a.q_dtype);
+  }
+  if (tid < MAXG) {
+    mrun[tid] = -INFINITY;
+    lrun[tid] = 0.f;
+  }
+  float acc[MAXG];
+#pragma unroll
+  for (int g = 0; g < MAXG; ++g) acc[g] = 0.f;
+  __syncthreads();
+  const int64_t ring = ((int64_t)b * a.Hkv + kvh) * R;   // first row of this head's ring
+  for (int i0 = 0; i0 < w; i0 += kWinChunk) {
+    const int n = min(kWinChunk, w - i0);
+    // scores of token i0 + tid against every head
+    float s[MAXG];
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) s[g] = -INFINITY;
+    if (tid < n) {
+      const int64_t row = ring + (c + i0 + tid) % R;
+#pragma unroll
+      for (int g = 0; g < MAXG; ++g)
+        if (g < G) s[g] = 0.f;
+      // the key row in 16-byte pieces, all loads in flight before the arithmetic
+      constexpr int NPIECE = D / 4;   // upper bound (float32); 16-bit rows use half of them
+      const int esz = a.w_dtype == TQ_F32 ? 4 : 2, per = 16 / esz, np = D / per;
+      const u32x4* kr = (const u32x4*)((const uint8_t*)a.kw + row * D * esz);
+      u32x4 pieces[NPIECE];
+#pragma unroll
+      for (int j = 0; j < NPIECE; ++j)
+        if (j < np) pieces[j] = kr[j];
+#pragma unroll
+      for (int j = 0; j < NPIECE; ++j) {
+        if (j >= np) break;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (e >= per) break;
+          const uint32_t w32 = pieces[j][per == 4 ? e : e >> 1];
+          const float kv = a.w_dtype == TQ_F32 ? __uint_as_float(w32)
+                           : a.w_dtype == TQ_BF16 ? ((e & 1) ? bf16_hi_to_f32(w32) : bf16_lo_to_f32(w32))
+                                                  : f16_bits_to_f32((e & 1) ? (w32 >> 16) : w32);
+          const int k = j * per + e;
+#pragma unroll
+          for (int g = 0; g < MAXG; ++g)
+            if (g < G) s[g] = fmaf(kv, qs[g][k], s[g]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < MAXG; ++g)
+        if (g < G) s[g] *= a.scale;
+    }
+    // chunk max per head
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) {
+      if (g >= G) break;
+      float m = s[g];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, wave_xor(m, o));
+      if (lane == 0) red[g][wv] = m;
+    }
+    __syncthreads();
+    if (tid < G) {
+      float m = red[tid][0];
+      for (int j = 1; j < kWinChunk / 64; ++j) m = fmaxf(m, red[tid][j]);
+      const float mn = fmaxf(mrun[tid], m);
+      alpha[tid] = __expf(mrun[tid] - mn);   // 0 when mrun is -inf
+      mrun[tid] = mn;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) {
+      if (g >= G) break;
+      const float p = tid < n ? __expf(s[g] - mrun[g]) : 0.f;
+      ps[g][tid] = p;
+      float l = p;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) l += wave_xor(l, o);
+      if (lane == 0) red[g][wv] = l;
+    }
+    __syncthreads();   // the chunk's weights and per-wave sums are visible from here
+    if (tid < G) {
+      float l = 0.f;
+      for (int j = 0; j < kWinChunk / 64; ++j) l += red[tid][j];
+      lrun[tid] = lrun[tid] * alpha[tid] + l;
+    }
+    // values: thread (k = tid % D, part = tid / D) accumulates coordinate k over the chunk's
+    // tokens i = part, part + NP, ...; the parts are summed once at the end
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g)
+      if (g < G) acc[g] *= alpha[g];
+    {
+      const int k = tid % D, part = tid / D;
+#pragma unroll 8
+      for (int i = part; i < n; i += NP) {
+        const int64_t row = ring + (c + i0 + i) % R;
+        const float vv = load_elem(a.vw, row * D + k, a.w_dtype);
+#pragma unroll
+        for (int g = 0; g < MAXG; ++g)
+          if (g < G) acc[g] = fmaf(ps[g][i], vv, acc[g]);
+      }
+    }
+    __syncthreads();
+  }
+  // sum the parts: part 0 threads collect the others through LDS (reusing ps)
+  float* red2 = &ps[0][0];   // needs NP * G * D floats <= MAXG * kWinChunk
+  const int k = tid % D, part = tid / D;
+  if (part > 0)
+    for (int g = 0; g < G; ++g) red2[((part - 1) * G + g) * D + k] = acc[g];
+  __syncthreads();
+  if (part == 0) {
+    for (int g = 0; g < G; ++g) {
+      float v = acc[g];
+      for (int pp = 1; pp < NP; ++pp) v += red2[((pp - 1) * G + g) * D + k];
+      float* P = a.part + (((int64_t)a.slot * a.B + b) * a.Hq + kvh * G + g) * (D + 2);
+      if (k == 0) {
+        P[0] = mrun[g];
+        P[1] = lrun[g];
+      }
+      P[2 + k] = v;
+    }
+  }
+}
+
+// Query heads handled together by qrot_kernel / merge_kernel (a block reads each rotation entry
+// once for all of them); kept small so that there are enough blocks to hide load latency.
+constexpr int kHeadsPerBlock = 2;
+
+// q' = Pi_K q for up to 8 query heads of one sequence. Thread k owns output coordinate k and
+// walks Pi_K^T row by row (coalesced across threads); the queries sit in LDS.
+template <int D>
+__global__ void __launch_bounds__(D) qrot_kernel(const void* q, int q_dtype, const float* pikt, int64_t rot_stride,
+                                                 int Hq, int bpr, float* out) {
+  constexpr int HB = kHeadsPerBlock;
+  __shared__ float qs[HB][D];
+  const int b = blockIdx.x, h0 = blockIdx.y * HB;
+  const int nh = min(HB, Hq - h0);
+  const int k = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    float v = 0.f;
+    if (h < nh) {
+      const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + k;
+      if (q_dtype == TQ_F32)
+        v = ((const float*)q)[idx];
+      else if (q_dtype == TQ_BF16)
+        v = bf16_bits_to_f32(((const uint16_t*)q)[idx]);
+      else
+        v = f16_bits_to_f32(((const uint16_t*)q)[idx]);
+    }
+    qs[h][k] = v;
+  }
+  __syncthreads();
+  const int r = bpr ? b / bpr : 0;
+  const float* PT = pikt + r * rot_stride + k;   // PT[j*D] = Pi[k][j]
+  float acc[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) acc[h] = 0.f;
+#pragma unroll 16
+  for (int j = 0; j < D; ++j) {
+    const float pv = PT[(int64_t)j * D];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) acc[h] = fmaf(pv, qs[h][j], acc[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < HB; ++h)
+    if (h < nh) out[((int64_t)b * Hq + h0 + h) * D + k] = acc[h];
+}
+
+// Log-sum-exp merge of the token splits for up to 8 query heads of one sequence, then
+// o = Pi_V^T (sum_s acc_s e^(m_s - M)) / L. Thread k owns coordinate k.
+template <int D, int OUT>
+__global__ void __launch_bounds__(D) merge_kernel(const float* part, int s_eff, int has_window, int B, int Hq,
+                                                  int bpr, const float* piv, int64_t rot_stride, void* out,
+                                                  float* lse) {
+  constexpr int HB = kHeadsPerBlock, NW = D / 64;
+  __shared__ float orot[HB][D];
+  __shared__ float red[HB][NW];
+  __shared__ float Ms[HB];
+  const int b = blockIdx.x, h0 = blockIdx.y * HB;
+  const int nh = min(HB, Hq - h0);
+  const int k = threadIdx.x, lane = k & 63, wv = k >> 6;
+  const int64_t sstride = (int64_t)B * Hq * (D + 2);
+  const float* P0 = part + ((int64_t)b * Hq + h0) * (D + 2);   // split s, head h: + s*sstride + h*(D+2)
+
+  // M_h = max over splits of m_s (threads stride over the splits)
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    float m = -INFINITY;
+    if (h < nh)
+      for (int s = k; s < s_eff + has_window; s += D) m = fmaxf(m, P0[(int64_t)s * sstride + h * (D + 2)]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, wave_xor(m, o));
+    if (lane == 0) red[h][wv] = m;
+  }
+  __syncthreads();
+  if (k < HB) {
+    float m = red[k][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, red[k][w]);
+    Ms[k] = m;
+  }
+  __syncthreads();
+
+  float acc[HB], lsum[HB], M[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    acc[h] = 0.f;
+    lsum[h] = 0.f;
+    M[h] = Ms[h];
+  }
+#pragma unroll 4
+  for (int s = 0; s < s_eff; ++s) {
+    const float* Ps = P0 + (int64_t)s * sstride;
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      if (h < nh && M[h] > -INFINITY) {
+        const float ms = Ps[h * (D + 2)];
+        const float w = ms > -INFINITY ? __expf(ms - M[h]) : 0.f;
+        lsum[h] = fmaf(w, Ps[h * (D + 2) + 1], lsum[h]);
+        acc[h] = fmaf(w, Ps[h * (D + 2) + 2 + k], acc[h]);
+      }
+    }
+  }
+  // the window's partial (original value domain) joins after the rotation back
+  float accw[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    accw[h] = 0.f;
+    if (has_window && h < nh && M[h] > -INFINITY) {
+      const float* Pw = P0 + (int64_t)s_eff * sstride + h * (D + 2);
+      const float ms = Pw[0];
+      const float w = ms > -INFINITY ? __expf(ms - M[h]) : 0.f;
+      lsum[h] = fmaf(w, Pw[1], lsum[h]);
+      accw[h] = w * Pw[2 + k];
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < HB; ++h) orot[h][k] = lsum[h] > 0.f ? acc[h] / lsum[h] : 0.f;
+  __syncthreads();
+
+  const float* Pv = piv + (bpr ? b / bpr : 0) * rot_stride + k;   // Pv[kk*D] = Pi[kk][k]
+  float o[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) o[h] = 0.f;
+#pragma unroll 16
+  for (int kk = 0; kk < D; ++kk) {
+    const float pv = Pv[(int64_t)kk * D];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) o[h] = fmaf(pv, orot[h][kk], o[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    if (h >= nh) continue;
+    if (lsum[h] > 0.f) o[h] += accw[h] / lsum[h];
+    const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + k;
+    if constexpr (OUT == TQ_F32)
+      ((float*)out)[idx] = o[h];
+    else if constexpr (OUT == TQ_BF16)
+      ((uint16_t*)out)[idx] = (uint16_t)f32_to_bf16_bits(o[h]);
+    else
+      ((uint16_t*)out)[idx] = (uint16_t)f32_to_f16_bits(o[h]);
+    if (k == 0 && lse) lse[(int64_t)b * Hq + h0 + h] = lsum[h] > 0.f ? M[h] + logf(lsum[h]) : -INFINITY;
+  }
+}
+
+template <int D, int BK, int BV, int PAGE, bool QJL>
+static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
+                                const Rotation& rv, float* scores, bool scores_only, const AttnLayout& lay,
+                                hipStream_t st) {
+  uint8_t* ws = (uint8_t*)p->workspace;
+  float* qrot = (float*)(ws + lay.qrot_off);
+  const int Hq = p->num_q_heads, B = p->batch;
+  const unsigned hblocks = (unsigned)((Hq + kHeadsPerBlock - 1) / kHeadsPerBlock);
+  hipLaunchKernelGGL((qrot_kernel<D>), dim3(B, hblocks), dim3(D), 0, st, p->q, p->q_dtype, rk.f32t(0),
+                     (int64_t)(rk.f32_stride / sizeof(float)), Hq, p->batch_per_rot, qrot);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  float* qsk = (float*)(ws + lay.qsk_off);
+  if constexpr (QJL) {
+    // S q: the same product with S^T in place of Pi^T
+    const Qjl& qj = p->qjl_k->q;
+    hipLaunchKernelGGL((qrot_kernel<D>), dim3(B, hblocks), dim3(D), 0, st, p->q, p->q_dtype, qj.st(0),
+                       (int64_t)(qj.st_stride / sizeof(float)), Hq, p->batch_per_rot, qsk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (p->max_seq_len == 0 && scores_only) return hipSuccess;
+
+  AttnKArgs a;
+  a.qrot = qrot;
+  a.kp = p->k_packed;
+  a.kn = p->k_norms;
+  a.vp = scores_only ? p->k_packed : p->v_packed;
+  a.vn = scores_only ? p->k_norms : p->v_norms;
+  a.seq_lens = p->seq_lens;
+  a.block_table = p->block_table;
+  a.scores = scores;
+  a.part = (float*)(ws + lay.part_off);
+  a.sink = (float*)rk.sink();
+  a.max_seq_len = p->max_seq_len;
+  a.block_size = p->block_table ? p->block_size : 1;
+  a.bs_shift = -1;
+  if (p->block_table && (p->block_size & (p->block_size - 1)) == 0) {
+    int s = 0;
+    while ((1 << s) < p->block_size) ++s;
+    a.bs_shift = s;
+  }
+  a.mbps = p->max_blocks_per_seq;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = p->num_kv_heads;
+  a.G = Hq / p->num_kv_heads;
+  a.s_eff = lay.splits * kAttnWaves;
+  a.window = p->window;
+  a.scale = p->scale;
+  LevelArgs lk = make_levels(ck), lv = make_levels(cv);
+  for (int j = 0; j < 16; ++j) a.ctk[j] = lk.centroid_bf16x2[j];
+  for (int j = 0; j < 8; ++j)
+    a.ctv[j] = (uint32_t)lv.centroid_f16[2 * j] | ((uint32_t)lv.centroid_f16[2 * j + 1] << 16);
+  a.ksg = p->k_signs;
+  a.krn = p->k_rnorms;
+  a.qsk = qsk;
+  a.qjl_c = (float)(std::sqrt(M_PI / 2.0) / D);
+  dim3 grid((unsigned)lay.splits, (unsigned)p->num_kv_heads, (unsigned)B);
+  if (scores_only) {
+    hipLaunchKernelGGL((attn_kernel<D, BK, BV, true, PAGE, QJL>), grid, dim3(kAttnWaves * 64), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((attn_kernel<D, BK, BV, false, PAGE, QJL>), grid, dim3(kAttnWaves * 64), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int has_win = p->window > 0 ? 1 : 0;
+  if (has_win) {
+    WinKArgs w;
+    w.q = p->q;
+    w.kw = p->k_window;
+    w.vw = p->v_window;
+    w.seq_lens = p->seq_lens;
+    w.part = a.part;
+    w.q_dtype = p->q_dtype;
+    w.w_dtype = p->window_dtype;
+    w.window = p->window;
+    w.max_seq_len = p->max_seq_len;
+    w.B = B;
+    w.Hq = Hq;
+    w.Hkv = p->num_kv_heads;
+    w.G = a.G;
+    w.slot = a.s_eff;
+    w.scale = p->scale;
+    hipLaunchKernelGGL((window_kernel<D>), dim3((unsigned)p->num_kv_heads, (unsigned)B), dim3(kWinChunk), 0, st, w);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t rs = (int64_t)(rv.f32_stride / sizeof(float));
+  switch (p->out_dtype) {
+    case TQ_F32:
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F32>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, has_win, B, Hq,
+                         p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
+      break;
+    case TQ_BF16:
+      hipLaunchKernelGGL((merge_kernel<D, TQ_BF16>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, has_win, B, Hq,
+                         p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
+      break;
+    default:
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F16>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, has_win, B, Hq,
+                         p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int BK, int BV, bool QJL>
+static hipError_t launch_attn_t(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
+                                const Rotation& rv, float* scores, bool so, const AttnLayout& lay, hipStream_t st) {
+  if (!p->block_table) return launch_attn_p<D, BK, BV, kDense, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
+  const int bs = p->block_size;
+  if (bs >= 16 && (bs & (bs - 1)) == 0) return launch_attn_p<D, BK, BV, kPagedPow2, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
+  return launch_attn_p<D, BK, BV, kPagedAny, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
+}
+
+template <int D, int BK, bool QJL>
+static hipError_t attn_bv(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
+                          const Rotation& rv, float* scores, bool so, const AttnLayout& lay, hipStream_t st) {
+  // scores-only calls use the K width for the (unused) V side to avoid extra instances
+  const int bv = so ? BK : cv.bits;
+  switch (bv) {
+    case 2: return launch_attn_t<D, BK, 2, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
+    case 3: return launch_attn_t<D, BK, 3, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
+    default: return launch_attn_t<D, BK, 4, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
+  }
+}
+
+template <int D, bool QJL>
+static hipError_t attn_bk(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
+                          const Rotation& rv, float* scores, bool so, const AttnLayout& lay, hipStream_t st) {
+  switch (ck.bits) {
+    case 2: return attn_bv<D, 2, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
+    case 3: return attn_bv<D, 3, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
+    default: return attn_bv<D, 4, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
+  }
+}
+
+}  // namespace tq

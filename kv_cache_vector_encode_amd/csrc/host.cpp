@@ -384,6 +384,57 @@ static int upload_rotation(Rotation& R) {
   return TQ_OK;
 }
 
+// QJL sketch upload: M_r = S_r Pi_r^T (float64 products of the float32 sketch and the float64
+// rotation) as bf16 hi / lo tiles in Pi's encode tile order, and S_r^T in float32 for the
+// query projection S q.
+static int upload_qjl(Qjl& Q, const float* sketch) {
+  const int d = Q.d;
+  const size_t dd = (size_t)d * d;
+  Q.frag_stride = 4 * dd;
+  Q.st_stride = 4 * dd;
+  Q.frag_off = 0;
+  Q.st_off = Q.frag_stride * Q.n_rot;
+  const size_t total = Q.st_off + Q.st_stride * Q.n_rot;
+  std::vector<uint8_t> host(total);
+  std::vector<double> m(dd);
+  for (int r = 0; r < Q.n_rot; ++r) {
+    const float* S = sketch + (size_t)r * dd;
+    const double* P = Q.rot->pi.data() + (size_t)r * dd;
+    for (int i = 0; i < d; ++i)
+      for (int k = 0; k < d; ++k) {
+        double acc = 0.0;
+        for (int j = 0; j < d; ++j) acc += (double)S[(size_t)i * d + j] * P[(size_t)k * d + j];
+        m[(size_t)i * d + k] = acc;
+      }
+    uint16_t* hi = (uint16_t*)(host.data() + Q.frag_off + r * Q.frag_stride);
+    uint16_t* lo = hi + dd;
+    build_tiles(d, [&](int row, int col) { return to_bf16((float)m[(size_t)row * d + col]); }, hi);
+    build_tiles(d, [&](int row, int col) {
+      double v = m[(size_t)row * d + col];
+      float h = from_bf16(to_bf16((float)v));
+      return to_bf16((float)(v - (double)h));
+    }, lo);
+    float* st = (float*)(host.data() + Q.st_off + r * Q.st_stride);
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) st[(size_t)j * d + i] = S[(size_t)i * d + j];
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(TQ_ERR_NO_DEVICE, "tq_qjl_create: hipGetDevice failed");
+  if (dev != Q.rot->device)
+    return fail(TQ_ERR_NO_DEVICE, "tq_qjl_create: the rotation lives on device " + std::to_string(Q.rot->device) +
+                                      " but device " + std::to_string(dev) + " is current");
+  hipError_t e = hipMalloc(&Q.dev, total);
+  if (e != hipSuccess) return fail(TQ_ERR_HIP, std::string("tq_qjl_create: hipMalloc: ") + hipGetErrorString(e));
+  e = hipMemcpy(Q.dev, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(Q.dev);
+    Q.dev = nullptr;
+    return fail(TQ_ERR_HIP, std::string("tq_qjl_create: hipMemcpy: ") + hipGetErrorString(e));
+  }
+  Q.device = dev;
+  return TQ_OK;
+}
+
 int device_cu_count(int device) {
   static int cached[64] = {0};
   if (device >= 0 && device < 64 && cached[device]) return cached[device];
@@ -660,6 +711,99 @@ int tq_encode_norm_corrected(const tq_codebook_t* cb, const tq_rotation_t* rot, 
                      packed, norms, slot_mapping, stream);
 }
 
+tq_qjl_t* tq_qjl_create(const tq_rotation_t* rot, const float* sketch) {
+  if (!rot) {
+    set_error("tq_qjl_create: rot is NULL");
+    return nullptr;
+  }
+  if (!sketch) {
+    set_error("tq_qjl_create: sketch is NULL");
+    return nullptr;
+  }
+  if (!gpu_dim_ok(rot->rot.d)) {
+    set_error("tq_qjl_create: d = " + std::to_string(rot->rot.d) + " is not supported; accepted 64, 128, 256");
+    return nullptr;
+  }
+  const size_t dd = (size_t)rot->rot.d * rot->rot.d;
+  for (size_t i = 0; i < dd * rot->rot.n_rot; ++i)
+    if (!std::isfinite(sketch[i])) {
+      set_error("tq_qjl_create: sketch has a non-finite entry at index " + std::to_string(i));
+      return nullptr;
+    }
+  tq_qjl_t* h = new tq_qjl_t;
+  h->q.rot = &rot->rot;
+  h->q.d = rot->rot.d;
+  h->q.n_rot = rot->rot.n_rot;
+  if (upload_qjl(h->q, sketch) != TQ_OK) {
+    delete h;
+    return nullptr;
+  }
+  set_error("");
+  return h;
+}
+
+void tq_qjl_free(tq_qjl_t* qjl) {
+  if (!qjl) return;
+  if (qjl->q.dev) (void)hipFree(qjl->q.dev);
+  delete qjl;
+}
+
+int tq_qjl_encode(const tq_codebook_t* cb, const tq_qjl_t* qjl, int64_t vectors_per_rot, const void* x,
+                  int x_dtype, int64_t n, int64_t x_row_stride, uint8_t* packed, float* norms, uint8_t* signs,
+                  float* rnorms, const int64_t* slot_mapping, tq_stream_t stream) {
+  const char* who = "tq_qjl_encode";
+  const std::string W(who);
+  if (!qjl) return fail(TQ_ERR_NULL, W + ": qjl is NULL");
+  const Rotation& R = *qjl->q.rot;
+  if (!cb) return fail(TQ_ERR_NULL, W + ": cb is NULL");
+  if (!gpu_bits_ok(cb->cb.bits))
+    return fail(TQ_ERR_INVALID_ARG, W + ": codebook bits = " + std::to_string(cb->cb.bits) +
+                                        " is not supported on the GPU; accepted 2, 3, 4 (keys of 3..5 bits)");
+  if (cb->cb.d != R.d)
+    return fail(TQ_ERR_INVALID_ARG, W + ": codebook d = " + std::to_string(cb->cb.d) + " does not match d = " +
+                                        std::to_string(R.d));
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, W + ": n must be >= 0");
+  const int es = dtype_size(x_dtype);
+  if (!es) return fail(TQ_ERR_INVALID_ARG, W + ": x_dtype = " + std::to_string(x_dtype) +
+                                               " is not supported; accepted TQ_F32 (0), TQ_BF16 (1), TQ_F16 (2)");
+  if (x_row_stride < R.d)
+    return fail(TQ_ERR_INVALID_ARG, W + ": x_row_stride = " + std::to_string(x_row_stride) +
+                                        " is smaller than d = " + std::to_string(R.d));
+  int s = check_rot_index(n, vectors_per_rot, R.n_rot, who);
+  if (s) return s;
+  if (n == 0) return TQ_OK;
+  if (!x) return fail(TQ_ERR_NULL, W + ": x is NULL");
+  if (!packed || !norms || !signs || !rnorms) return fail(TQ_ERR_NULL, W + ": an output pointer is NULL");
+  if (!aligned(x, 16)) return fail(TQ_ERR_ALIGN, W + ": x must be 16-byte aligned");
+  if ((x_row_stride * es) % 16) return fail(TQ_ERR_ALIGN, W + ": x_row_stride * element size must be a multiple of 16 bytes");
+  if (!aligned(packed, 8)) return fail(TQ_ERR_ALIGN, W + ": packed must be 8-byte aligned");
+  if (!aligned(norms, 4) || !aligned(rnorms, 4)) return fail(TQ_ERR_ALIGN, W + ": norms / rnorms must be 4-byte aligned");
+  if (!aligned(signs, 16)) return fail(TQ_ERR_ALIGN, W + ": signs must be 16-byte aligned");
+  if (slot_mapping && !aligned(slot_mapping, 8)) return fail(TQ_ERR_ALIGN, W + ": slot_mapping must be 8-byte aligned");
+  if ((s = check_device(R, who))) return s;
+  QjlEncodeLaunch q;
+  EncodeLaunch& a = q.enc;
+  a.rot = &R;
+  a.lv = make_levels(cb->cb);
+  if (!lut_covers_unit_range(a.lv))
+    return fail(TQ_ERR_INVALID_ARG, W + ": the codebook's boundaries are too close for the quantization table");
+  a.bits = cb->cb.bits;
+  a.x_dtype = x_dtype;
+  a.vectors_per_rot = vectors_per_rot;
+  a.n = n;
+  a.x_row_stride = x_row_stride;
+  a.x = x;
+  a.packed = packed;
+  a.norms = norms;
+  a.slot_mapping = slot_mapping;
+  a.norm_correct = false;
+  a.stream = (hipStream_t)stream;
+  q.qjl = &qjl->q;
+  q.signs = signs;
+  q.rnorms = rnorms;
+  return hip_status(launch_qjl_encode(q), who);
+}
+
 int tq_decode(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors_per_rot, const uint8_t* packed,
               const float* norms, const int64_t* slot_mapping, int64_t n, void* out, int out_dtype,
               tq_stream_t stream) {
@@ -742,6 +886,8 @@ static int check_attn(const tq_attn_params* p, bool scores_only, const char* who
     if (!aligned(p->k_window, es) || !aligned(p->v_window, es))
       return fail(TQ_ERR_ALIGN, std::string(who) + ": k_window / v_window must be aligned to the element size");
   }
+  if (p->qjl_k && p->qjl_k->q.rot != &p->rot_k->rot)
+    return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": qjl_k was not created on rot_k");
   return TQ_OK;
 }
 
@@ -764,6 +910,11 @@ static int attn_common(const tq_attn_params* p, float* scores, bool scores_only,
     if (!p->k_packed || !p->k_norms) return fail(TQ_ERR_NULL, std::string(who) + ": k_packed / k_norms is NULL");
     if (!aligned(p->k_packed, 8) || !aligned(p->k_norms, 4))
       return fail(TQ_ERR_ALIGN, std::string(who) + ": k_packed must be 8-byte and k_norms 4-byte aligned");
+    if (p->qjl_k) {
+      if (!p->k_signs || !p->k_rnorms) return fail(TQ_ERR_NULL, std::string(who) + ": qjl_k needs k_signs and k_rnorms");
+      if (!aligned(p->k_signs, 16) || !aligned(p->k_rnorms, 4))
+        return fail(TQ_ERR_ALIGN, std::string(who) + ": k_signs must be 16-byte and k_rnorms 4-byte aligned");
+    }
     if (!scores_only) {
       if (!p->v_packed || !p->v_norms) return fail(TQ_ERR_NULL, std::string(who) + ": v_packed / v_norms is NULL");
       if (!aligned(p->v_packed, 8) || !aligned(p->v_norms, 4))

@@ -46,6 +46,17 @@ struct Rotation {
   static constexpr size_t kZeroBytes = 256, kSinkBytes = 8192;
 };
 
+// QJL sketch of a rotation stack: per rotation r, M_r = S_r Pi_r^T as bf16 hi / lo MFMA tiles
+// (same tile order as Pi's encode tiles, 4*d*d bytes) and S_r^T in float32 (4*d*d bytes).
+struct Qjl {
+  const Rotation* rot = nullptr;
+  int d = 0, n_rot = 0, device = -1;
+  void* dev = nullptr;
+  size_t frag_stride = 0, st_stride = 0, frag_off = 0, st_off = 0;
+  const uint8_t* frag(int r) const { return (const uint8_t*)dev + frag_off + (size_t)r * frag_stride; }
+  const float* st(int r) const { return (const float*)((const uint8_t*)dev + st_off + (size_t)r * st_stride); }
+};
+
 // Quantization table for the encode. With f = y * scale + offset (y the rotated, normalized
 // coordinate), bin = floor(f) holds at most one decision boundary: code = base[bin] + (f > thr[bin]),
 // which equals #{k : t_k < y}. Bins cover f in [0, kLutBins) for |y| <= 1. An entry is the
@@ -86,6 +97,16 @@ struct EncodeLaunch {
   hipStream_t stream;
 };
 hipError_t launch_encode(const EncodeLaunch& a);
+
+// QJL key encode: the MSE encode of `enc` (codebook at the MSE width, no norm correction) plus
+// the residual's sign sketch and norm.
+struct QjlEncodeLaunch {
+  EncodeLaunch enc;
+  const Qjl* qjl;
+  uint8_t* signs;
+  float* rnorms;
+};
+hipError_t launch_qjl_encode(const QjlEncodeLaunch& a);
 
 // Recent-token window append: stage the flushed rows, encode them (K and V), fill the rings.
 struct WindowAppendLaunch {
@@ -136,6 +157,7 @@ hipError_t launch_decode(const DecodeLaunch& a);
 struct AttnLayout {
   int splits;            // token splits per (b, kv head)
   size_t qrot_off;       // float [B, Hq, d]: Pi_K q
+  size_t qsk_off;        // float [B, Hq, d]: S q (QJL keys only; else == part_off, unused)
   size_t part_off;       // float [splits, B, Hq, d + 2]: (m, l, acc[d])
   size_t total;
 };
@@ -143,6 +165,10 @@ AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu);
 hipError_t launch_attention(const tq_attn_params* p, const Codebook& ck, const Codebook& cv,
                             const Rotation& rk, const Rotation& rv, float* scores_out,
                             bool scores_only, const AttnLayout& lay, hipStream_t stream);
+// The same with QJL keys (p->qjl_k set), in its own translation unit.
+hipError_t launch_attention_qjl(const tq_attn_params* p, const Codebook& ck, const Codebook& cv,
+                                const Rotation& rk, const Rotation& rv, float* scores_out,
+                                bool scores_only, const AttnLayout& lay, hipStream_t stream);
 
 int device_cu_count(int device);
 
@@ -153,4 +179,7 @@ struct tq_codebook {
 };
 struct tq_rotation {
   tq::Rotation rot;
+};
+struct tq_qjl {
+  tq::Qjl q;
 };

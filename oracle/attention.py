@@ -58,18 +58,17 @@ def scores(q, k_hat, scale: float, seq_lens=None):
     return out
 
 
-def attention(q, k_hat, v_hat, scale: float, seq_lens=None):
-    """o[b, h] = sum_t softmax(s[b, h])_t v_hat[b, h // G, t]; also lse = log sum_t exp(s)."""
-    q = np.asarray(q, dtype=np.float64)
+def attend(s, v_hat, seq_lens=None):
+    """o[b, h] = sum_t softmax(s[b, h, :L])_t v_hat[b, h // G, t]; lse = log sum_t exp(s[b, h, :L])."""
+    s = np.asarray(s, dtype=np.float64)
     v_hat = np.asarray(v_hat, dtype=np.float64)
-    s = scores(q, k_hat, scale, seq_lens)
-    B, Hq, d = q.shape
-    Hkv = v_hat.shape[1]
+    B, Hq, T = s.shape
+    Hkv, d = v_hat.shape[1], v_hat.shape[3]
     G = _group(Hq, Hkv)
     o = np.zeros((B, Hq, d))
     lse = np.full((B, Hq), -np.inf)
     for b in range(B):
-        L = s.shape[2] if seq_lens is None else int(seq_lens[b])
+        L = T if seq_lens is None else int(seq_lens[b])
         if L == 0:
             continue
         for h in range(Hq):
@@ -80,6 +79,11 @@ def attention(q, k_hat, v_hat, scale: float, seq_lens=None):
             o[b, h] = (e / tot) @ v_hat[b, h // G, :L]
             lse[b, h] = m + math.log(tot)
     return o, lse
+
+
+def attention(q, k_hat, v_hat, scale: float, seq_lens=None):
+    """o[b, h] = sum_t softmax(s[b, h])_t v_hat[b, h // G, t]; also lse = log sum_t exp(s)."""
+    return attend(scores(q, k_hat, scale, seq_lens), v_hat, seq_lens)
 
 
 def gather_paged(pool, block_table, seq_lens, block_size: int):

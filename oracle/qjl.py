@@ -10,6 +10,8 @@ KV Cache API page (ginkgoq.github.io/TurboQuant/api/kv), TurboQuantCompressorV2:
   asymmetric_attention_scores: <q, k> ~ <q, k_mse> + ||r|| sqrt(pi/2) / m <S q, signs>, m the
     number of sketch rows (d); the attention scale multiplies the sum (TurboQuantKVCache).
 The module's header on the same page states the estimator is unbiased with variance O(1/d).
+Decode attention over QJL keys takes the softmax of these scores and the weighted sum of the
+decompressed values, as TurboQuantKVCache.attend does with its scores.
 
 Readings: norms and residual norms are kept in float32 (the page stores float16; the MSE
 codec here keeps float32 norms, reading 1 of the codec); k_mse uses the exact norm, as the
@@ -22,6 +24,7 @@ import math
 
 import numpy as np
 
+from . import attention as _att
 from . import codec
 
 
@@ -67,3 +70,29 @@ def scores(q, codes, norms, signs, rnorms, pi, S, centroids_mse, scale: float):
     term1 = q @ k_mse.T
     term2 = (q @ S.T) @ np.asarray(signs, dtype=np.float64).T
     return scale * (term1 + math.sqrt(math.pi / 2) / m * term2 * np.asarray(rnorms, dtype=np.float64)[None, :])
+
+
+def cache_scores(q, codes, norms, signs, rnorms, pi, S, centroids_mse, scale: float, seq_lens=None):
+    """QJL scores over a cache: q [B, Hq, d]; codes / signs [B, Hkv, T, d], norms / rnorms
+    [B, Hkv, T]; query head h reads KV head h // (Hq / Hkv). Returns [B, Hq, T], -inf past len_b."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv, T = np.asarray(norms).shape[1:3]
+    G = Hq // Hkv
+    out = np.full((B, Hq, T), -np.inf)
+    for b in range(B):
+        L = T if seq_lens is None else int(seq_lens[b])
+        if L == 0:
+            continue
+        for g in range(Hkv):
+            hs = slice(g * G, (g + 1) * G)
+            out[b, hs, :L] = scores(q[b, hs], codes[b, g, :L], norms[b, g, :L], signs[b, g, :L],
+                                    rnorms[b, g, :L], pi, S, centroids_mse, scale)
+    return out
+
+
+def attention(q, codes, norms, signs, rnorms, pi, S, centroids_mse, v_hat, scale: float, seq_lens=None):
+    """Decode attention with QJL keys: softmax of cache_scores, then the weighted sum of v_hat
+    [B, Hkv, T, d] (the plain attention's second half). Returns (o [B, Hq, d], lse [B, Hq])."""
+    s = cache_scores(q, codes, norms, signs, rnorms, pi, S, centroids_mse, scale, seq_lens)
+    return _att.attend(s, v_hat, seq_lens)

@@ -114,3 +114,12 @@ def test_hadamard_rejects_bad_arguments():
     bad = (C.c_int8 * 64)(*([1] * 63 + [0]))
     assert not L.tq_rotation_hadamard(64, 1, C.cast(bad, C.c_void_p))
     assert b"signs[63]" in L.tq_last_error()
+
+
+def test_qjl_calls_validate_before_any_launch(L):
+    assert not L.tq_qjl_create(None, None)
+    assert "rot is NULL" in _lib.last_error()
+    cb = tq.Codebook(128, 3)
+    assert L.tq_qjl_encode(cb.handle, None, 0, None, 1, 1, 128, None, None, None, None, None, None) == -2
+    assert "qjl is NULL" in _lib.last_error()
+    L.tq_qjl_free(None)   # freeing NULL is a no-op

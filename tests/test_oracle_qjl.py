@@ -152,3 +152,28 @@ def test_variance_shrinks_like_one_over_m():
         est = _estimates(q, x, pi, cb, rng.standard_normal((1500, m, d)))
         v.append(est.var(ddof=1))
     assert 5.0 <= v[0] / v[1] <= 12.8            # 8 in expectation
+
+
+def test_cache_attention_reduces_to_plain_attention_without_residual():
+    # ||r|| = 0 removes the sketch term: QJL attention is the plain attention of the MSE keys
+    from oracle import attention as oatt
+    d, B, Hq, Hkv, T = 16, 2, 4, 2, 9
+    rng = np.random.default_rng(11)
+    pi = _pi(d, 13)
+    cb = codebook.codebook(d, 2)
+    codes = rng.integers(0, 4, size=(B, Hkv, T, d)).astype(np.uint8)
+    norms = rng.uniform(0.5, 3.0, size=(B, Hkv, T)).astype(np.float32)
+    signs = np.where(rng.random((B, Hkv, T, d)) < 0.5, -1, 1).astype(np.int8)
+    S = rng.standard_normal((d, d))
+    q = rng.standard_normal((B, Hq, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    lens = [9, 4]
+    o, lse = qjl.attention(q, codes, norms, signs, np.zeros((B, Hkv, T), np.float32), pi, S, cb.centroids, v,
+                           0.25, lens)
+    khat = (cb.centroids[codes.astype(np.int64)] @ pi) * norms.astype(np.float64)[..., None]
+    o2, lse2 = oatt.attention(q, khat, v, 0.25, seq_lens=lens)
+    assert np.allclose(o, o2, rtol=0, atol=1e-12) and np.allclose(lse, lse2, rtol=0, atol=1e-12)
+    # one token: the softmax weight is 1 and the output is that token's value
+    o1, _ = qjl.attention(q, codes, norms, signs, norms, pi, S, cb.centroids, v, 0.25, [1, 1])
+    for h in range(Hq):
+        assert np.allclose(o1[:, h], v[:, h // (Hq // Hkv), 0], rtol=0, atol=1e-14)

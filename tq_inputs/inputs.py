@@ -17,7 +17,7 @@ __all__ = [
     "example_keys", "codec_check_inputs", "LlamaCacheShape", "llama_layer_kv",
     "LongCacheShape", "long_cache_layer_kv", "AttnShape", "attn_inputs",
     "PagedShape", "paged_layout", "paged_layer_bits", "paged_layer_tokens", "paged_queries",
-    "generator",
+    "generator", "random_bytes", "random_norms",
 ]
 
 
@@ -256,3 +256,20 @@ def paged_queries(shape: PagedShape, sequences: int, head_dim: int, layer: int,
     base = 200000 + 1000 * head_dim + 10 * layer
     return torch.randn(sequences, shape.q_heads, head_dim, generator=generator(device, base),
                        device=device).to(dtype)
+
+
+# --- compressed-cache stand-ins ----------------------------------------------------------
+# A packed code row is any byte string (every bit pattern decodes to valid codes), so uniform
+# random bytes stand in for a compressed cache; norms are log-normal around a typical key norm.
+
+def random_bytes(shape, seed: int, device="cpu") -> torch.Tensor:
+    """Uniform random uint8 tensor of the given shape."""
+    g = generator("cpu", seed)
+    return torch.randint(0, 256, tuple(shape), generator=g, dtype=torch.uint8).to(device)
+
+
+def random_norms(shape, seed: int, median: float = 16.0, sigma: float = 0.4, device="cpu") -> torch.Tensor:
+    """Positive float32 tensor: median * exp(sigma * N(0, 1))."""
+    g = generator("cpu", seed)
+    z = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    return (median * torch.exp(sigma * z)).to(device)
