@@ -298,8 +298,8 @@ def next_rows(tq, ti, torch, dev, K, V, kp, kn, vp, vn, rot, ck, cv, q, kp4, kn4
     """Figures for the rows beside the hot path, on the same Llama-3-8B-shaped cache:
     the recent-token window (attention over 8064 compressed + 128 full-precision tokens per
     sequence, and a one-token append that flushes one token per (layer, KV head)), the Hadamard
-    rotation and the norm-corrected encode (keys, 4 bits), and affine group quantization of the
-    values (2 bits, groups of 32)."""
+    rotation and the norm-corrected encode (keys, 4 bits), QJL keys at 4 bits (encode and decode
+    attention), and affine group quantization of the values (2 bits, groups of 32)."""
     N = L * H * T
     out = {}
     # Hadamard rotation: same encode kernel, a different Pi
@@ -315,6 +315,33 @@ def next_rows(tq, ti, torch, dev, K, V, kp, kn, vp, vn, rot, ck, cv, q, kp4, kn4
     out["norm_corrected_encode_k"] = {"ms": round(ms, 4), "GB/s": round(alg / (ms * 1e-3) / 1e9, 1),
                                       "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     tq.encode(ck, rot, K, vectors_per_rot=H * T, packed=kp, norms=kn)   # restore the keys' cache
+    # QJL keys at 4 bits: 3-bit MSE codes + sign sketch of the residual + residual norm, then
+    # decode attention over them (values as in the hot path)
+    cq = tq.Codebook(d, 3)
+    sk = tq.QJLSketch(rot, torch.stack([ti.qjl_sketch_gaussian(d, ti.key_seed(l)) for l in range(L)]))
+    qp = torch.empty(N, d * 3 // 8, dtype=torch.uint8, device=dev)
+    qn = torch.empty(N, device=dev)
+    qs = torch.empty(N, d // 8, dtype=torch.uint8, device=dev)
+    qr = torch.empty(N, device=dev)
+    ms = _time(torch, lambda: tq.qjl_encode(cq, sk, K, vectors_per_rot=H * T, packed=qp, norms=qn, signs=qs,
+                                            rnorms=qr))
+    alg = N * (d * 2 + d * 3 // 8 + 4 + d // 8 + 4)
+    flops = N * 5 * 2 * d * d    # MFMA work: rotation (2 bf16 passes) + sketch product (3 passes)
+    out["qjl_encode_k4"] = {"ms": round(ms, 4), "GB/s": round(alg / (ms * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "mfma_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                            "mfma_frac_bf16": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4)}
+    ao_q = torch.empty(L, q.shape[1], d, dtype=torch.bfloat16, device=dev)
+    qv = dict(qjl=sk, k_signs=qs.view(L, H, T, -1), k_rnorms=qr.view(L, H, T))
+    tq.attn_decode(cq, rot, cv, rot, q, qp.view(L, H, T, -1), qn.view(L, H, T), vp4, vn4, batch_per_rot=1, out=ao_q, **qv)
+    wsq = ao_q._tq_workspace
+    ms = _time(torch, lambda: tq.attn_decode(cq, rot, cv, rot, q, qp.view(L, H, T, -1), qn.view(L, H, T), vp4, vn4,
+                                             batch_per_rot=1, out=ao_q, workspace=wsq, **qv))
+    alg = N * (d * 3 // 8 + 4 + d // 8 + 4) + N * (d * cv.bits // 8 + 4) + 2 * L * q.shape[1] * d * 2
+    out["qjl_attention_k4v2"] = {"ms": round(ms, 4), "context_tokens_per_s": round(L * T / (ms * 1e-3), 1),
+                                 "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "plain_k4_attention_ms": round(attn_ms, 4)}
+    del qp, qn, qs, qr, ao_q, wsq
     # group-quantized values, 2 bits
     gp = torch.empty(N, d // 4, dtype=torch.uint8, device=dev)
     gs = torch.empty(N, d // 32, dtype=torch.float16, device=dev)

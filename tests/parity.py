@@ -6,11 +6,15 @@ Bars:
   * norms: |n_gpu - n| <= (d/4 + 4) * 2^-24 * n, the rounding bound of the kernel's float32
     sum of squares (two chains of d/4 fused multiply-adds per lane, two adds, a square root);
   * decode: per vector ||x_gpu - x_ref|| <= (2e-3 + u_out) ||x_ref||, x_ref = float64 oracle
-    decode of the GPU's own codes and norms, u_out the output dtype's unit roundoff (0 for
+    decode of the same codes and norms, u_out the output dtype's unit roundoff (0 for
     float32, 2^-8 bfloat16, 2^-11 float16);
   * scores: |s_gpu - s_ref| <= 2e-3 * scale * n_t * ||q|| * ||c[idx_t]|| (Cauchy-Schwarz scale);
   * attention: ||o_gpu - o_ref|| <= 2e-3 * sum_t p_t ||v_hat_t||; |lse_gpu - lse_ref| <= the
     largest score bound of the row.
+
+Provenance: the oracle never takes a GPU output as input. A decode, score or attention test
+feeds the GPU a compressed cache made by the oracle's own encode of seeded inputs
+(oracle_encoded) or by tq_inputs' random bytes and norms, and gives the oracle the same bytes.
 """
 
 from __future__ import annotations
@@ -40,7 +44,7 @@ def check_encode(x: np.ndarray, packed: np.ndarray, norms: np.ndarray, pi: np.nd
     """x float64 [N, d] (the exact input values), packed/norms from the GPU. Returns flip count."""
     cb = ocb.codebook(d, bits)
     codes_ref, n_ref, y = occ.encode_codes(x, pi, cb.centroids)
-    codes = occ.unpack_codes(packed, bits, d)
+    codes = unpack(packed, bits, d)
     delta = occ.boundary_distance(y, cb.thresholds)
     diff = codes != codes_ref
     bad = diff & (delta >= WINDOW)
@@ -58,6 +62,28 @@ def check_encode(x: np.ndarray, packed: np.ndarray, norms: np.ndarray, pi: np.nd
     inside = int((delta < WINDOW).sum())
     log("%s: %d vectors, %d flips among %d coordinates inside the window" % (what, x.shape[0], flips, inside))
     return flips
+
+
+def unpack(packed: np.ndarray, bits: int, d: int) -> np.ndarray:
+    """Codes of GPU-written rows for comparison (LSB-first bitstream, code j in stream bits
+    [j*bits, (j+1)*bits)); the tests' own vectorized reader, so no GPU output enters the oracle."""
+    p = np.asarray(packed, dtype=np.uint8).reshape(-1, np.asarray(packed).shape[-1])
+    stream = np.unpackbits(p, axis=1, bitorder="little")[:, : d * bits].reshape(-1, d, bits).astype(np.int64)
+    return (stream << np.arange(bits)).sum(axis=2).astype(np.uint8)
+
+
+def oracle_encoded(x64: np.ndarray, pi: np.ndarray, bits: int):
+    """The oracle's encode of x [..., d] (float64 values of a seeded input): packed uint8
+    [..., (d*bits)/8] and norms float32 [...], to be uploaded as a GPU test input."""
+    d = x64.shape[-1]
+    lead = x64.shape[:-1]
+    cb = ocb.codebook(d, bits)
+    packed, norms = occ.encode(x64.reshape(-1, d), pi, cb.centroids, bits)
+    return packed.reshape(*lead, -1), norms.reshape(lead)
+
+
+def upload(a: np.ndarray, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
 def check_decode(out: torch.Tensor, packed: np.ndarray, norms: np.ndarray, pi: np.ndarray, d: int, bits: int,

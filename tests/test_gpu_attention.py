@@ -1,4 +1,8 @@
-"""GPU parity of tq_scores_compressed / tq_attn_decode against the float64 oracle."""
+"""GPU parity of tq_scores_compressed / tq_attn_decode against the float64 oracle.
+
+The compressed cache both sides read is the oracle's encode of the seeded K and V (small
+cases), or, at the full sizes, tq_inputs' random code bytes with norms taken from the seeded
+tokens; the oracle never decodes a GPU-written row."""
 
 import math
 
@@ -8,7 +12,8 @@ import torch
 
 import tq_inputs as ti
 from oracle import attention as oatt, codebook as ocb, codec as occ
-from parity import check_attention, check_decode, check_encode, log, rotation_pair, score_bounds, to64
+from parity import (check_attention, check_decode, check_encode, log, oracle_encoded, rotation_pair, score_bounds,
+                    to64, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,18 +32,15 @@ def _dense_cache(dev, B, Hq, Hkv, T, d, bk, bv, seed=11, kseed=42, vseed=542, qd
     rk, pk = rotation_pair(d, [kseed])
     rv, pv = rotation_pair(d, [vseed])
     ck, cv = tq.Codebook(d, bk), tq.Codebook(d, bv)
-    kp, kn = tq.encode(ck, rk, k)
-    vp, vn = tq.encode(cv, rv, v)
-    kp, kn = kp.view(B, Hkv, T, -1), kn.view(B, Hkv, T)
-    vp, vn = vp.view(B, Hkv, T, -1), vn.view(B, Hkv, T)
-    return dict(q=q, k=k, v=v, rk=rk, rv=rv, pk=pk[0], pv=pv[0], ck=ck, cv=cv, kp=kp, kn=kn, vp=vp, vn=vn)
+    kpn, knn = oracle_encoded(to64(k), pk[0], bk)      # [B, Hkv, T, row], [B, Hkv, T]
+    vpn, vnn = oracle_encoded(to64(v), pv[0], bv)
+    return dict(q=q, k=k, v=v, rk=rk, rv=rv, pk=pk[0], pv=pv[0], ck=ck, cv=cv, kpn=kpn, knn=knn, vpn=vpn, vnn=vnn,
+                kp=upload(kpn, dev), kn=upload(knn, dev), vp=upload(vpn, dev), vn=upload(vnn, dev))
 
 
 def _oracle_cache(c, d, bk, bv):
-    khat = oatt.decode_cache(c["kp"].cpu().numpy(), c["kn"].cpu().numpy(), c["pk"], ocb.codebook(d, bk).centroids,
-                             bk, d)
-    vhat = oatt.decode_cache(c["vp"].cpu().numpy(), c["vn"].cpu().numpy(), c["pv"], ocb.codebook(d, bv).centroids,
-                             bv, d)
+    khat = oatt.decode_cache(c["kpn"], c["knn"], c["pk"], ocb.codebook(d, bk).centroids, bk, d)
+    vhat = oatt.decode_cache(c["vpn"], c["vnn"], c["pv"], ocb.codebook(d, bv).centroids, bv, d)
     return khat, vhat
 
 
@@ -55,8 +57,8 @@ def test_scores(dev, d, bk):
     q64 = to64(c["q"])
     scale = 1 / math.sqrt(d)
     ref = oatt.scores(q64, khat, scale, seq_lens=lens.cpu().numpy())
-    codes = occ.unpack_codes(c["kp"].cpu().numpy().reshape(-1, c["kp"].shape[-1]), bk, d).reshape(B, Hkv, T, d)
-    bound = score_bounds(q64, c["kn"].cpu().numpy(), codes, ocb.codebook(d, bk), scale)
+    codes = occ.unpack_codes(c["kpn"].reshape(-1, c["kpn"].shape[-1]), bk, d).reshape(B, Hkv, T, d)
+    bound = score_bounds(q64, c["knn"], codes, ocb.codebook(d, bk), scale)
     got = s.cpu().numpy().astype(np.float64)
     for b, L in enumerate(lens.tolist()):
         err = np.abs(got[b, :, :L] - ref[b, :, :L])
@@ -107,7 +109,11 @@ def test_attention_bf16_output_and_scale(dev):
                     [T] * B, "bf16 out, scale 0.3")
 
 
-def _paged(dev, S, max_len, Hkv, Hq, d, bk, bv, seed=7):
+def _paged(dev, S, max_len, Hkv, Hq, d, bk, bv, seed=7, oracle_rows=None):
+    """Paged pool [num_blocks, Hkv, 16, row] of one layer's tokens, written by tq_encode through a
+    slot mapping. oracle_rows: sequences whose rows are then replaced by oracle-side inputs
+    (all sequences: the oracle's encode of their tokens; a list: random code bytes with the
+    tokens' own norms, cheap at full size) so that the attention check reads no GPU-written row."""
     shape = ti.PagedShape(sequences=S, max_len=max_len, kv_heads=Hkv, q_heads=Hq)
     lay = ti.paged_layout(shape, seed=seed)
     total = int(lay.seq_starts[-1])
@@ -125,9 +131,34 @@ def _paged(dev, S, max_len, Hkv, Hq, d, bk, bv, seed=7):
     kp, kn = tq.encode(ck, rk, k, slot_mapping=slot, num_slots=nslots)
     vp, vn = tq.encode(cv, rv, v, slot_mapping=slot, num_slots=nslots)
     q = ti.paged_queries(shape, S, d, seed, device=dev)
-    return dict(shape=shape, lay=lay, k=k, v=v, slot=slot, rk=rk, rv=rv, pk=pk[0], pv=pv[0], ck=ck, cv=cv,
-                kp=kp.view(lay.num_blocks, Hkv, bs, -1), kn=kn.view(lay.num_blocks, Hkv, bs),
-                vp=vp.view(lay.num_blocks, Hkv, bs, -1), vn=vn.view(lay.num_blocks, Hkv, bs), q=q)
+    c = dict(shape=shape, lay=lay, k=k, v=v, slot=slot, rk=rk, rv=rv, pk=pk[0], pv=pv[0], ck=ck, cv=cv, q=q,
+             gkp=kp, gkn=kn)
+    if oracle_rows is not None:
+        seqs = range(S) if oracle_rows == "all" else oracle_rows
+        starts = lay.seq_starts
+        tok = torch.cat([torch.arange(int(starts[s_]), int(starts[s_ + 1])) for s_ in seqs])
+        rows = (tok[:, None] * Hkv + heads[None, :]).reshape(-1)          # rows of k.view(-1, d)
+        dst = slot[rows.to(dev)]
+        if oracle_rows == "all":
+            kr, knr = oracle_encoded(to64(k.view(-1, d)[rows.to(dev)]), pk[0], bk)
+            vr, vnr = oracle_encoded(to64(v.view(-1, d)[rows.to(dev)]), pv[0], bv)
+        else:
+            n = rows.numel()
+            kr = ti.random_bytes((n, d * bk // 8), 900 + seed, "cpu").numpy()
+            vr = ti.random_bytes((n, d * bv // 8), 901 + seed, "cpu").numpy()
+            knr = np.linalg.norm(to64(k.view(-1, d)[rows.to(dev)]), axis=1).astype(np.float32)
+            vnr = np.linalg.norm(to64(v.view(-1, d)[rows.to(dev)]), axis=1).astype(np.float32)
+        kp, kn, vp, vn = kp.clone(), kn.clone(), vp.clone(), vn.clone()
+        kp[dst], kn[dst], vp[dst], vn[dst] = upload(kr, dev), upload(knr, dev), upload(vr, dev), upload(vnr, dev)
+        pool = {}
+        for name, arr, src in (("kp", kp, kr), ("kn", kn, knr), ("vp", vp, vr), ("vn", vn, vnr)):
+            host = np.zeros(tuple(arr.shape), dtype=src.dtype)
+            host[dst.cpu().numpy()] = src
+            pool[name + "_host"] = host.reshape((lay.num_blocks, Hkv, bs) + tuple(arr.shape[1:]))
+        c.update(pool)
+    c.update(kp=kp.view(lay.num_blocks, Hkv, bs, -1), kn=kn.view(lay.num_blocks, Hkv, bs),
+             vp=vp.view(lay.num_blocks, Hkv, bs, -1), vn=vn.view(lay.num_blocks, Hkv, bs))
+    return c
 
 
 def _check_paged(c, d, bk, bv, o, lse, seqs, what):
@@ -136,8 +167,7 @@ def _check_paged(c, d, bk, bv, o, lse, seqs, what):
     lens = lay.seq_lens.numpy()
     ck, cv = ocb.codebook(d, bk).centroids, ocb.codebook(d, bv).centroids
     q64 = to64(c["q"])
-    kpn, knn = c["kp"].cpu().numpy(), c["kn"].cpu().numpy()
-    vpn, vnn = c["vp"].cpu().numpy(), c["vn"].cpu().numpy()
+    kpn, knn, vpn, vnn = c["kp_host"], c["kn_host"], c["vp_host"], c["vn_host"]
     table = lay.block_table.numpy()
     worst = 0
     for s in seqs:
@@ -158,8 +188,11 @@ def _check_paged(c, d, bk, bv, o, lse, seqs, what):
 def test_attention_paged_small(dev, d, bk, bv):
     S, Hkv, Hq = 6, 2, 8
     log("case: paged small d%d K%dV%d" % (d, bk, bv))
-    c = _paged(dev, S, 700, Hkv, Hq, d, bk, bv)
+    c = _paged(dev, S, 700, Hkv, Hq, d, bk, bv, oracle_rows="all")
     lay = c["lay"]
+    # the slot-mapped GPU encode of every token meets the codec bar
+    check_encode(to64(c["k"].view(-1, d)), c["gkp"][c["slot"]].cpu().numpy(), c["gkn"][c["slot"]].cpu().numpy(),
+                 c["pk"], d, bk, "paged small K d%d" % d)
     o, lse = tq.attn_decode(c["ck"], c["rk"], c["cv"], c["rv"], c["q"], c["kp"], c["kn"], c["vp"], c["vn"],
                             seq_lens=lay.seq_lens.to(dev), max_seq_len=int(lay.seq_lens.max()),
                             block_table=lay.block_table.to(dev), block_size=16,
@@ -175,26 +208,34 @@ def test_attention_paged_small(dev, d, bk, bv):
 
 
 def test_fused_attention_workload_full(dev):
-    """Batch 32, 32 query heads over 8 KV heads, context 32768, d=128, K4/V2, bf16 queries;
-    oracle attention over the decoded cache for 2 batch rows (all heads)."""
+    """Batch 32, 32 query heads over 8 KV heads, context 32768, d=128, K4/V2, bf16 queries, in the
+    launch configuration the bench times. The cache is random code bytes with log-normal norms
+    (tq_inputs); oracle attention over the same bytes for 2 batch rows (all heads). The encode of
+    the seeded K at this size is checked on 2048 sampled rows."""
     shape = ti.AttnShape()
     B, Hq, Hkv, T, d = shape.batch, shape.q_heads, shape.kv_heads, shape.tokens, shape.head_dim
     log("case: fused attention workload B%d Hq%d Hkv%d T%d" % (B, Hq, Hkv, T))
-    c = _dense_cache(dev, B, Hq, Hkv, T, d, 4, 2)
-    o, lse = tq.attn_decode(c["ck"], c["rk"], c["cv"], c["rv"], c["q"], c["kp"], c["kn"], c["vp"], c["vn"],
+    q, k, _ = ti.attn_inputs(shape, device=dev, seed=11)
+    rk, pk = rotation_pair(d, [42])
+    rv, pv = rotation_pair(d, [542])
+    ck, cv = tq.Codebook(d, 4), tq.Codebook(d, 2)
+    gkp, gkn = tq.encode(ck, rk, k)
+    torch.cuda.synchronize()
+    rows = torch.randperm(B * Hkv * T, generator=ti.generator("cpu", 3))[:2048].to(dev)
+    check_encode(to64(k.view(-1, d)[rows]), gkp[rows].cpu().numpy(), gkn[rows].cpu().numpy(), pk[0], d, 4,
+                 "attn workload K")
+    del k, gkp, gkn
+    kp = ti.random_bytes((B, Hkv, T, d * 4 // 8), 31)
+    vp = ti.random_bytes((B, Hkv, T, d * 2 // 8), 32)
+    kn = ti.random_norms((B, Hkv, T), 33)
+    vn = ti.random_norms((B, Hkv, T), 34, median=11.0)
+    o, lse = tq.attn_decode(ck, rk, cv, rv, q, kp.to(dev), kn.to(dev), vp.to(dev), vn.to(dev),
                             out_dtype=torch.float32, return_lse=True)
     torch.cuda.synchronize()
-    # sampled encode parity on the cache itself
-    rows = torch.randperm(B * Hkv * T, generator=torch.Generator().manual_seed(3))[:2048].to(dev)
-    check_encode(to64(c["k"].view(-1, d)[rows]), c["kp"].view(-1, 64)[rows].cpu().numpy(),
-                 c["kn"].view(-1)[rows].cpu().numpy(), c["pk"], d, 4, "attn workload K")
     rowsb = [0, 31]
-    sub = lambda t: t[rowsb]
-    khat = oatt.decode_cache(sub(c["kp"]).cpu().numpy(), sub(c["kn"]).cpu().numpy(), c["pk"],
-                             ocb.codebook(d, 4).centroids, 4, d)
-    vhat = oatt.decode_cache(sub(c["vp"]).cpu().numpy(), sub(c["vn"]).cpu().numpy(), c["pv"],
-                             ocb.codebook(d, 2).centroids, 2, d)
-    check_attention(sub(o).cpu().numpy().astype(np.float64), sub(lse).cpu().numpy(), to64(sub(c["q"])), khat, vhat,
+    khat = oatt.decode_cache(kp[rowsb].numpy(), kn[rowsb].numpy(), pk[0], ocb.codebook(d, 4).centroids, 4, d)
+    vhat = oatt.decode_cache(vp[rowsb].numpy(), vn[rowsb].numpy(), pv[0], ocb.codebook(d, 2).centroids, 2, d)
+    check_attention(o[rowsb].cpu().numpy().astype(np.float64), lse[rowsb].cpu().numpy(), to64(q[rowsb]), khat, vhat,
                     1 / math.sqrt(d), [T, T], "attn workload")
 
 
@@ -206,24 +247,32 @@ def test_paged_ragged_workload(dev, d):
     bk, bv = ti.paged_layer_bits(layer)
     log("case: paged ragged workload d%d layer %d K%dV%d" % (d, layer, bk, bv))
     shape = ti.PagedShape()
-    c = _paged(dev, shape.sequences, shape.max_len, shape.kv_heads, shape.q_heads, d, bk, bv, seed=layer)
+    lay0 = ti.paged_layout(shape, seed=layer)
+    lens = lay0.seq_lens.numpy()
+    seqs = [int(np.argmin(lens)), int(np.argmax(lens)), 17, 100]
+    c = _paged(dev, shape.sequences, shape.max_len, shape.kv_heads, shape.q_heads, d, bk, bv, seed=layer,
+               oracle_rows=seqs)
     lay = c["lay"]
     o = tq.attn_decode(c["ck"], c["rk"], c["cv"], c["rv"], c["q"], c["kp"], c["kn"], c["vp"], c["vn"],
                        seq_lens=lay.seq_lens.to(dev), max_seq_len=int(lay.seq_lens.max()),
                        block_table=lay.block_table.to(dev), block_size=16, out_dtype=torch.float32,
                        num_kv_heads=shape.kv_heads)
     torch.cuda.synchronize()
-    # codec parity on sampled (token, head) vectors, read back through the slot gather
+    # codec parity on sampled (token, head) vectors of the GPU-written pool
     n = c["slot"].numel()
-    idx = torch.randperm(n, generator=torch.Generator().manual_seed(d))[:2048].to(dev)
+    idx = torch.randperm(n, generator=ti.generator("cpu", d))[:2048].to(dev)
     slots = c["slot"][idx]
     kflat = c["k"].view(-1, d)
-    check_encode(to64(kflat[idx]), c["kp"].view(-1, c["kp"].shape[-1])[slots].cpu().numpy(),
-                 c["kn"].view(-1)[slots].cpu().numpy(), c["pk"], d, bk, "paged K d%d" % d)
-    dec = tq.decode(c["ck"], c["rk"], c["kp"].view(-1, c["kp"].shape[-1]), c["kn"].view(-1), slot_mapping=slots,
-                    out_dtype=torch.bfloat16)
-    check_decode(dec, c["kp"].view(-1, c["kp"].shape[-1])[slots].cpu().numpy(), c["kn"].view(-1)[slots].cpu().numpy(),
-                 c["pk"], d, bk, "paged K decode d%d" % d)
-    lens = lay.seq_lens.numpy()
-    seqs = [int(np.argmin(lens)), int(np.argmax(lens)), 17, 100]
+    check_encode(to64(kflat[idx]), c["gkp"][slots].cpu().numpy(), c["gkn"][slots].cpu().numpy(), c["pk"], d, bk,
+                 "paged K d%d" % d)
+    # gather decode through a slot mapping, over the rows of the checked sequences (random bytes)
+    kp_h = c["kp_host"].reshape(-1, c["kp_host"].shape[-1])
+    kn_h = c["kn_host"].reshape(-1)
+    lay_slots = torch.cat([c["slot"].view(-1, shape.kv_heads)[int(lay.seq_starts[s_]):int(lay.seq_starts[s_ + 1])]
+                           .reshape(-1) for s_ in seqs[2:]])
+    dec = tq.decode(c["ck"], c["rk"], c["kp"].view(-1, c["kp"].shape[-1]), c["kn"].view(-1),
+                    slot_mapping=lay_slots, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ls = lay_slots.cpu().numpy()
+    check_decode(dec, kp_h[ls], kn_h[ls], c["pk"], d, bk, "paged K gather decode d%d" % d)
     _check_paged(c, d, bk, bv, o.cpu().numpy().astype(np.float64), None, seqs, "paged ragged d%d" % d)

@@ -1,4 +1,8 @@
-"""GPU parity of tq_encode / tq_decode against the float64 oracle (through the C ABI)."""
+"""GPU parity of tq_encode / tq_decode against the float64 oracle (through the C ABI).
+
+Encode: the GPU and the oracle encode the same seeded x. Decode: the GPU decodes the oracle's
+own encode of x (or, at full size, tq_inputs' random code bytes and norms) and the oracle
+decodes the same bytes; no GPU output is an oracle input."""
 
 import ctypes as C
 
@@ -7,7 +11,7 @@ import pytest
 import torch
 
 import tq_inputs as ti
-from parity import check_decode, check_encode, log, rotation_pair, to64
+from parity import check_decode, check_encode, log, oracle_encoded, rotation_pair, to64, unpack, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -26,12 +30,13 @@ def _run(x_dev, d, bits, seed=42, out_dtype=None, what=""):
     cb = tq.Codebook(d, bits)
     log("case:", what, "shape", tuple(x_dev.shape), x_dev.dtype, "bits", bits)
     packed, norms = tq.encode(cb, rot, x_dev)
-    out = tq.decode(cb, rot, packed, norms, out_dtype=out_dtype or x_dev.dtype)
     torch.cuda.synchronize()
     x64 = to64(x_dev.reshape(-1, d))
-    pk, nm = packed.cpu().numpy(), norms.cpu().numpy()
-    flips = check_encode(x64, pk, nm, pis[0], d, bits, what)
-    check_decode(out, pk, nm, pis[0], d, bits, what)
+    flips = check_encode(x64, packed.cpu().numpy(), norms.cpu().numpy(), pis[0], d, bits, what)
+    pr, nr = oracle_encoded(x64, pis[0], bits)
+    out = tq.decode(cb, rot, upload(pr, x_dev.device), upload(nr, x_dev.device), out_dtype=out_dtype or x_dev.dtype)
+    torch.cuda.synchronize()
+    check_decode(out, pr, nr, pis[0], d, bits, what)
     return packed, norms, out, flips
 
 
@@ -50,8 +55,7 @@ def test_codec_check_workload(dev):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_shapes_and_dtypes(dev, d, bits, dtype):
     n = 1000   # 31 full 32-vector tiles and a ragged tail of 8
-    g = torch.Generator(device="cpu").manual_seed(d * 10 + bits)
-    x = torch.randn(n, d, generator=g) * torch.exp(torch.randn(n, 1, generator=g))
+    x = ti.normal((n, d), d * 10 + bits) * torch.exp(ti.normal((n, 1), d * 10 + bits + 1))
     _run(x.to(dtype).to(dev), d, bits, seed=7 + d, what="d%d b%d %s" % (d, bits, dtype))
 
 
@@ -71,8 +75,7 @@ def test_zero_and_small_vectors(dev):
     x[32:] = ti.codec_check_inputs(32, d, seed=11) * 1e-10
     for bits in (2, 3, 4):
         packed, norms, out, _ = _run(x.to(dev), d, bits, out_dtype=torch.float32, what="zero/small b%d" % bits)
-        from oracle import codec as occ
-        codes = occ.unpack_codes(packed[:32].cpu().numpy(), bits, d)
+        codes = unpack(packed[:32].cpu().numpy(), bits, d)
         assert np.all(codes == 2 ** (bits - 1) - 1)
         assert torch.all(norms[:32] == 0) and torch.all(out[:32] == 0)
 
@@ -93,8 +96,7 @@ def test_slot_mapping_scatter_and_gather(dev):
     rot, pis = rotation_pair(d, [42])
     cb = tq.Codebook(d, bits)
     x = ti.codec_check_inputs(n, d, seed=21).to(torch.bfloat16).to(dev)
-    g = torch.Generator(device="cpu").manual_seed(4)
-    slots = torch.randperm(800, generator=g)[:n]
+    slots = torch.randperm(800, generator=ti.generator("cpu", 4))[:n]
     slots[::7] = -1                                     # skipped vectors
     slots_d = slots.to(dev)
     row = tq.packed_row_bytes(d, bits)
@@ -121,12 +123,15 @@ def test_rotation_stack(dev):
     cb = tq.Codebook(d, bits)
     x = ti.codec_check_inputs(n, d, seed=8).to(torch.bfloat16).to(dev)
     packed, norms = tq.encode(cb, rot, x, vectors_per_rot=vpr)
-    out = tq.decode(cb, rot, packed, norms, vectors_per_rot=vpr, out_dtype=torch.float32)
     x64 = to64(x)
+    enc = [oracle_encoded(x64[r * vpr:(r + 1) * vpr], pis[r], bits) for r in range(3)]
+    pr, nr = np.concatenate([e[0] for e in enc]), np.concatenate([e[1] for e in enc])
+    out = tq.decode(cb, rot, upload(pr, dev), upload(nr, dev), vectors_per_rot=vpr, out_dtype=torch.float32)
+    torch.cuda.synchronize()
     for r in range(3):
         sl = slice(r * vpr, min(n, (r + 1) * vpr))
         check_encode(x64[sl], packed[sl].cpu().numpy(), norms[sl].cpu().numpy(), pis[r], d, bits, "stack r%d" % r)
-        check_decode(out[sl], packed[sl].cpu().numpy(), norms[sl].cpu().numpy(), pis[r], d, bits, "stack r%d" % r)
+        check_decode(out[sl], pr[sl], nr[sl], pis[r], d, bits, "stack r%d" % r)
 
 
 def test_deterministic(dev):
@@ -148,9 +153,8 @@ def test_power_of_two_scale_invariance(dev):
     p1, n1 = tq.encode(cb, rot, x)
     p2, n2 = tq.encode(cb, rot, x * 64)
     assert torch.equal(n2, n1 * 64)
-    from oracle import codec as occ
-    c1 = occ.unpack_codes(p1.cpu().numpy(), bits, d)
-    c2 = occ.unpack_codes(p2.cpu().numpy(), bits, d)
+    c1 = unpack(p1.cpu().numpy(), bits, d)
+    c2 = unpack(p2.cpu().numpy(), bits, d)
     assert np.mean(c1 != c2) < 1e-5
 
 
@@ -179,13 +183,13 @@ def test_error_paths_on_device(dev):
 
 
 def _sample_rows(n_total, k, seed):
-    g = torch.Generator(device="cpu").manual_seed(seed)
-    return torch.randperm(n_total, generator=g)[:k].sort().values
+    return torch.randperm(n_total, generator=ti.generator("cpu", seed))[:k].sort().values
 
 
 def test_llama_shaped_cache_full(dev):
     """32 layers x 8 KV heads x 8192 tokens x d=128 bf16, K4/V2, one launch per tensor over
-    the 32-rotation stack (one shared rotation per layer); sampled oracle parity."""
+    the 32-rotation stack (one shared rotation per layer); sampled oracle parity. The decode
+    runs at the same size on random code bytes and norms (every code value occurs)."""
     shape = ti.LlamaCacheShape()
     L_, H, T, d = shape.layers, shape.kv_heads, shape.tokens, shape.head_dim
     K = torch.empty(L_, H, T, d, dtype=torch.bfloat16, device=dev)
@@ -198,18 +202,21 @@ def test_llama_shaped_cache_full(dev):
     log("case: llama-shaped cache, encode K4 and V2 over 32 layers")
     kp, kn = tq.encode(ck, rot, K, vectors_per_rot=vpr)
     vp, vn = tq.encode(cv, rot, V, vectors_per_rot=vpr)
-    ko = tq.decode(ck, rot, kp, kn, vectors_per_rot=vpr)
-    vo = tq.decode(cv, rot, vp, vn, vectors_per_rot=vpr)
+    N_ = L_ * vpr
+    rkp, rvp = ti.random_bytes((N_, d * 4 // 8), 61, dev), ti.random_bytes((N_, d * 2 // 8), 62, dev)
+    rkn, rvn = ti.random_norms((N_,), 63, device=dev), ti.random_norms((N_,), 64, device=dev)
+    ko = tq.decode(ck, rot, rkp, rkn, vectors_per_rot=vpr)
+    vo = tq.decode(cv, rot, rvp, rvn, vectors_per_rot=vpr)
     torch.cuda.synchronize()
-    rows = _sample_rows(L_ * vpr, 4096, 0)
+    rows = _sample_rows(N_, 4096, 0)
     layer = (rows // vpr).numpy()
     Kf, Vf = K.view(-1, d), V.view(-1, d)
     for l in np.unique(layer)[:8]:
         sel = rows[layer == l].to(dev)
-        for name, X, P, N, O, bits in (("K", Kf, kp, kn, ko, 4), ("V", Vf, vp, vn, vo, 2)):
+        for name, X, P, N, RP, RN, O, bits in (("K", Kf, kp, kn, rkp, rkn, ko, 4), ("V", Vf, vp, vn, rvp, rvn, vo, 2)):
             check_encode(to64(X[sel]), P[sel].cpu().numpy(), N[sel].cpu().numpy(), pis[l], d, bits,
                          "llama %s layer %d" % (name, l))
-            check_decode(O[sel], P[sel].cpu().numpy(), N[sel].cpu().numpy(), pis[l], d, bits,
+            check_decode(O[sel], RP[sel].cpu().numpy(), RN[sel].cpu().numpy(), pis[l], d, bits,
                          "llama %s layer %d" % (name, l))
 
 
@@ -225,13 +232,15 @@ def test_long_cache_layer_full(dev, layer):
     log("case: long cache layer %d" % layer)
     kp, kn = tq.encode(cb, rk, K)
     vp, vn = tq.encode(cb, rv, V)
-    ko = tq.decode(cb, rk, kp, kn)
+    n = K.numel() // d
+    rkp, rkn = ti.random_bytes((n, d * 3 // 8), 70 + layer, dev), ti.random_norms((n,), 71 + layer, device=dev)
+    ko = tq.decode(cb, rk, rkp, rkn)
     torch.cuda.synchronize()
-    rows = _sample_rows(K.numel() // d, 4096, layer).to(dev)
+    rows = _sample_rows(n, 4096, layer).to(dev)
     Kf, Vf = K.view(-1, d), V.view(-1, d)
     check_encode(to64(Kf[rows]), kp[rows].cpu().numpy(), kn[rows].cpu().numpy(), pk[0], d, 3, "long K l%d" % layer)
     check_encode(to64(Vf[rows]), vp[rows].cpu().numpy(), vn[rows].cpu().numpy(), pv[0], d, 3, "long V l%d" % layer)
-    check_decode(ko[rows], kp[rows].cpu().numpy(), kn[rows].cpu().numpy(), pk[0], d, 3, "long K l%d" % layer)
+    check_decode(ko[rows], rkp[rows].cpu().numpy(), rkn[rows].cpu().numpy(), pk[0], d, 3, "long K l%d" % layer)
 
 
 def test_gpu_codes_reach_the_distortion_integral(dev):
@@ -244,7 +253,7 @@ def test_gpu_codes_reach_the_distortion_integral(dev):
         rot, pis = rotation_pair(d, [42])
         cb = tq.Codebook(d, bits)
         packed, _ = tq.encode(cb, rot, x.to(dev))
-        codes = occ.unpack_codes(packed.cpu().numpy(), bits, d).astype(np.int64)
+        codes = unpack(packed.cpu().numpy(), bits, d).astype(np.int64)
         _, _, y = occ.encode_codes(x.numpy(), pis[0], ocb.codebook(d, bits).centroids)
         err = ((y - ocb.codebook(d, bits).centroids[codes]) ** 2).mean(axis=1)
         se = err.std(ddof=1) / math.sqrt(err.size)

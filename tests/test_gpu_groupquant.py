@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import tq_inputs as ti
 from oracle import groupquant as ogq
 from parity import log
 
@@ -24,8 +25,7 @@ def dev():
 
 
 def _inputs(n, d, dtype, seed):
-    g = torch.Generator().manual_seed(seed)
-    x = torch.randn(n, d, generator=g) * torch.exp(torch.randn(n, 1, generator=g))
+    x = ti.normal((n, d), seed) * torch.exp(ti.normal((n, 1), seed + 1))
     x[0] = 1.25                                   # constant row: the scale floor
     if n > 1:
         x[1, :32] = torch.tensor([0.0, 3.0, 0.5, 1.5, 2.5] + [1.0] * 27)   # ties at 2 bits

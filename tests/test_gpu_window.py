@@ -2,7 +2,8 @@
 and the append / flush that maintains the rings (through the C ABI).
 
 Attention with a window must match oracle/window.py (the newest min(L, R) tokens exact, the
-older ones decoded from the GPU's own codes) to the usual bar ||do|| <= 2e-3 sum_t p_t ||v_t||.
+older ones decoded from a compressed cache the oracle's encode made of the same tokens) to the
+usual bar ||do|| <= 2e-3 sum_t p_t ||v_t||.
 Append: a prefill (one call with the whole prompt) and token-by-token appends must leave the
 same state, bit for bit; the flushed rows must equal tq_encode of the same tokens (same
 kernel) and meet the oracle's code parity; the rings must hold the newest tokens verbatim.
@@ -15,7 +16,8 @@ import pytest
 import torch
 
 from oracle import attention as oatt, codebook as ocb, window as ow
-from parity import REL, check_encode, log, rotation_pair, to64
+import tq_inputs as ti
+from parity import REL, check_encode, log, oracle_encoded, rotation_pair, to64, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -60,26 +62,26 @@ def _check(o_gpu, lse_gpu, q64, khat, vhat, kw, vw, lens, R, scale, what):
                                             (256, 2, 4, 40, torch.float32), (128, 3, 2, 300, torch.bfloat16)])
 def test_attention_with_window(dev, d, bk, bv, R, wdt):
     B, Hq, Hkv, T = 5, 8, 2, 600
-    g = torch.Generator().manual_seed(d + R)
-    q = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16).to(dev)
-    k = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16).to(dev)
-    v = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16).to(dev)
-    kw = (torch.randn(B, Hkv, R, d, generator=g) * 1.5).to(wdt).to(dev)
-    vw = torch.randn(B, Hkv, R, d, generator=g).to(wdt).to(dev)
+    sd = 10 * (d + R)
+    q = ti.normal((B, Hq, d), sd, dtype=torch.bfloat16, device=dev)
+    k = ti.normal((B, Hkv, T, d), sd + 1, dtype=torch.bfloat16)
+    v = ti.normal((B, Hkv, T, d), sd + 2, dtype=torch.bfloat16)
+    kw = ti.normal((B, Hkv, R, d), sd + 3, scale=1.5, dtype=wdt, device=dev)
+    vw = ti.normal((B, Hkv, R, d), sd + 4, dtype=wdt, device=dev)
     rk, pk = rotation_pair(d, [42])
     rv, pv = rotation_pair(d, [542])
     ck, cv = tq.Codebook(d, bk), tq.Codebook(d, bv)
-    kp, kn = tq.encode(ck, rk, k)
-    vp, vn = tq.encode(cv, rv, v)
-    kp, kn, vp, vn = kp.view(B, Hkv, T, -1), kn.view(B, Hkv, T), vp.view(B, Hkv, T, -1), vn.view(B, Hkv, T)
+    kpn, knn = oracle_encoded(to64(k), pk[0], bk)
+    vpn, vnn = oracle_encoded(to64(v), pv[0], bv)
+    kp, kn, vp, vn = upload(kpn, dev), upload(knn, dev), upload(vpn, dev), upload(vnn, dev)
     lens = torch.tensor([600, 0, min(R, 600) // 2 + 1, R, R + 1], dtype=torch.int32, device=dev)
     what = "window d%d K%dV%d R%d %s" % (d, bk, bv, R, wdt)
     log("case:", what)
     o, lse = tq.attn_decode(ck, rk, cv, rv, q, kp, kn, vp, vn, seq_lens=lens, out_dtype=torch.float32,
                             return_lse=True, k_window=kw, v_window=vw)
     torch.cuda.synchronize()
-    khat = oatt.decode_cache(kp.cpu().numpy(), kn.cpu().numpy(), pk[0], ocb.codebook(d, bk).centroids, bk, d)
-    vhat = oatt.decode_cache(vp.cpu().numpy(), vn.cpu().numpy(), pv[0], ocb.codebook(d, bv).centroids, bv, d)
+    khat = oatt.decode_cache(kpn, knn, pk[0], ocb.codebook(d, bk).centroids, bk, d)
+    vhat = oatt.decode_cache(vpn, vnn, pv[0], ocb.codebook(d, bv).centroids, bv, d)
     _check(o.cpu().numpy().astype(np.float64), lse.cpu().numpy(), to64(q), khat, vhat, to64(kw), to64(vw),
            lens.cpu().numpy(), R, 1 / math.sqrt(d), what)
 
@@ -114,9 +116,8 @@ def _append(st, k_new, v_new, S, block_table=None, block_size=0):
                                       (64, [3, 3, 44]), (16, [16, 1, 33])])
 def test_append_streaming_equals_prefill(dev, R, chunks):
     B, Hkv, S, d, bk, bv = 3, 2, 50, 128, 4, 2
-    g = torch.Generator().manual_seed(R + 1)
-    K = torch.randn(B, Hkv, S, d, generator=g).to(torch.bfloat16).to(dev)
-    V = torch.randn(B, Hkv, S, d, generator=g).to(torch.bfloat16).to(dev)
+    K = ti.normal((B, Hkv, S, d), 100 + R, dtype=torch.bfloat16, device=dev)
+    V = ti.normal((B, Hkv, S, d), 200 + R, dtype=torch.bfloat16, device=dev)
     if chunks == "prefill":
         chunks = [S]
     elif chunks == "ones":
@@ -150,14 +151,15 @@ def test_append_streaming_equals_prefill(dev, R, chunks):
 def test_append_ragged_lengths_paged_then_attention(dev):
     """Sequences at different lengths in a paged compressed cache: per-sequence prefills of
     0, 5 and 11 tokens (one-sequence sub-batches), then 60 batched single-token appends, then
-    attention over compressed + window against the oracle."""
+    attention over compressed + window against the oracle. The append's compressed rows are
+    checked bit for bit against tq_encode of the same tokens; for the attention check they are
+    then replaced by the oracle's encode of those tokens, which both sides read."""
     B, Hkv, Hq, S, R, d, bk, bv, bs = 3, 2, 8, 96, 24, 64, 3, 2, 16
     nblk = B * (S // bs)
-    perm = torch.randperm(nblk, generator=torch.Generator().manual_seed(4)).to(torch.int32)
+    perm = torch.randperm(nblk, generator=ti.generator("cpu", 4)).to(torch.int32)
     table = perm.view(B, S // bs).to(dev)
-    g = torch.Generator().manual_seed(9)
-    K = torch.randn(B, Hkv, S, d, generator=g).to(torch.bfloat16).to(dev)
-    V = torch.randn(B, Hkv, S, d, generator=g).to(torch.bfloat16).to(dev)
+    K = ti.normal((B, Hkv, S, d), 9, dtype=torch.bfloat16, device=dev)
+    V = ti.normal((B, Hkv, S, d), 10, dtype=torch.bfloat16, device=dev)
     st = _state(dev, B, Hkv, S, R, d, bk, bv, paged=(nblk, bs))
     L0 = [0, 5, 11]
     for b, n in enumerate(L0):
@@ -175,27 +177,41 @@ def test_append_ragged_lengths_paged_then_attention(dev):
     torch.cuda.synchronize()
     final = [L0[b] + steps for b in range(B)]
     assert st["lens"].tolist() == final
-    q = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16).to(dev)
+    q = ti.normal((B, Hq, d), 11, dtype=torch.bfloat16, device=dev)
     lens = torch.tensor(final, dtype=torch.int32, device=dev)
-    o, lse = tq.attn_decode(st["ck"], st["rk"], st["cv"], st["rv"], q, st["kp"], st["kn"], st["vp"], st["vn"],
-                            seq_lens=lens, max_seq_len=S, block_table=table, block_size=bs, out_dtype=torch.float32,
-                            return_lse=True, num_kv_heads=Hkv, k_window=st["kw"], v_window=st["vw"])
-    torch.cuda.synchronize()
-    # oracle: gather the paged codes back into positions, decode, exact window
+    # the append's state: compressed rows = tq_encode of the tokens at those positions, rings verbatim
     tb = table.cpu().numpy()
-    kp = st["kp"].cpu().numpy()[tb].transpose(0, 2, 1, 3, 4).reshape(B, Hkv, S, -1)
-    kn = st["kn"].cpu().numpy()[tb].transpose(0, 2, 1, 3).reshape(B, Hkv, S)
-    vp = st["vp"].cpu().numpy()[tb].transpose(0, 2, 1, 3, 4).reshape(B, Hkv, S, -1)
-    vn = st["vn"].cpu().numpy()[tb].transpose(0, 2, 1, 3).reshape(B, Hkv, S)
-    khat = oatt.decode_cache(kp, kn, st["pk"], ocb.codebook(d, bk).centroids, bk, d)
-    vhat = oatt.decode_cache(vp, vn, st["pv"], ocb.codebook(d, bv).centroids, bv, d)
+    gkp = st["kp"].cpu().numpy()[tb].transpose(0, 2, 1, 3, 4).reshape(B, Hkv, S, -1)
+    gkn = st["kn"].cpu().numpy()[tb].transpose(0, 2, 1, 3).reshape(B, Hkv, S)
     for b in range(B):
         c, _ = ow.split(final[b], R)
-        # the flushed rows are the encode of the very tokens appended at those positions
         kp_b, kn_b = tq.encode(st["ck"], st["rk"], K[b, :, :c])
-        assert np.array_equal(kp[b, :, :c].reshape(-1, kp.shape[-1]), kp_b.cpu().numpy())
-        assert np.array_equal(kn[b, :, :c].reshape(-1), kn_b.cpu().numpy())
+        assert np.array_equal(gkp[b, :, :c].reshape(-1, gkp.shape[-1]), kp_b.cpu().numpy())
+        assert np.array_equal(gkn[b, :, :c].reshape(-1), kn_b.cpu().numpy())
         for t in range(c, final[b]):
             assert torch.equal(st["kw"][b, :, t % R], K[b, :, t])
-    _check(o.cpu().numpy().astype(np.float64), lse.cpu().numpy(), to64(q), khat, vhat, to64(st["kw"]),
-           to64(st["vw"]), final, R, 1 / math.sqrt(d), "append+paged attention")
+    # attention input: the oracle's encode of every position, scattered into the same pages
+    kpn, knn = oracle_encoded(to64(K), st["pk"], bk)           # [B, Hkv, S, row]
+    vpn, vnn = oracle_encoded(to64(V), st["pv"], bv)
+    def pages(a):   # [B, Hkv, S, ...] -> pool [nblk, Hkv, bs, ...] through the block table
+        pool = np.zeros((nblk, Hkv, bs) + a.shape[3:], dtype=a.dtype)
+        for b in range(B):
+            for j in range(S // bs):
+                pool[tb[b, j]] = a[b, :, j * bs:(j + 1) * bs]
+        return upload(pool, dev)
+    o, lse = tq.attn_decode(st["ck"], st["rk"], st["cv"], st["rv"], q, pages(kpn), pages(knn), pages(vpn),
+                            pages(vnn), seq_lens=lens, max_seq_len=S, block_table=table, block_size=bs,
+                            out_dtype=torch.float32, return_lse=True, num_kv_heads=Hkv, k_window=st["kw"],
+                            v_window=st["vw"])
+    torch.cuda.synchronize()
+    khat = oatt.decode_cache(kpn, knn, st["pk"], ocb.codebook(d, bk).centroids, bk, d)
+    vhat = oatt.decode_cache(vpn, vnn, st["pv"], ocb.codebook(d, bv).centroids, bv, d)
+    # the oracle's rings are built from the appended tokens themselves (token t at slot t mod R)
+    K64, V64 = to64(K), to64(V)
+    kw_ref, vw_ref = np.zeros((B, Hkv, R, d)), np.zeros((B, Hkv, R, d))
+    for b in range(B):
+        c, _ = ow.split(final[b], R)
+        for t in range(c, final[b]):
+            kw_ref[b, :, t % R], vw_ref[b, :, t % R] = K64[b, :, t], V64[b, :, t]
+    _check(o.cpu().numpy().astype(np.float64), lse.cpu().numpy(), to64(q), khat, vhat, kw_ref, vw_ref, final, R,
+           1 / math.sqrt(d), "append+paged attention")

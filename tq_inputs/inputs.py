@@ -10,6 +10,7 @@ from __future__ import annotations
 import math
 from dataclasses import dataclass, field
 
+import numpy as np
 import torch
 
 __all__ = [
@@ -17,7 +18,7 @@ __all__ = [
     "example_keys", "codec_check_inputs", "LlamaCacheShape", "llama_layer_kv",
     "LongCacheShape", "long_cache_layer_kv", "AttnShape", "attn_inputs",
     "PagedShape", "paged_layout", "paged_layer_bits", "paged_layer_tokens", "paged_queries",
-    "generator", "random_bytes", "random_norms",
+    "generator", "random_bytes", "random_norms", "normal", "random_signs",
 ]
 
 
@@ -49,6 +50,13 @@ def rotation_gaussians(d: int, seeds) -> torch.Tensor:
     return torch.stack([rotation_gaussian(d, s) for s in seeds])
 
 
+def random_signs(n_rot: int, d: int, seed: int) -> np.ndarray:
+    """The random +-1 diagonal of a Hadamard rotation (Turbo Attention PyPI page, "The codec"):
+    int8 [n_rot, d], each sign a fair coin from a CPU generator."""
+    g = generator("cpu", seed)
+    return (torch.randint(0, 2, (n_rot, d), generator=g) * 2 - 1).to(torch.int8).numpy()
+
+
 def qjl_sketch_gaussian(d: int, seed: int) -> torch.Tensor:
     """The float32 d x d standard-normal sketch matrix of the QJL stage for a key compressor
     seeded `seed`: a CPU generator seeded seed + 10000 (the key compressor's second draw)."""
@@ -56,6 +64,12 @@ def qjl_sketch_gaussian(d: int, seed: int) -> torch.Tensor:
 
 
 # --- small codec workloads ----------------------------------------------------------
+
+def normal(shape, seed: int, scale: float = 1.0, dtype=torch.float32, device="cpu") -> torch.Tensor:
+    """scale * N(0, 1) of the given shape from a CPU generator, rounded to dtype, on device."""
+    z = torch.randn(tuple(shape), generator=generator("cpu", seed), dtype=torch.float32)
+    return (z * scale).to(dtype).to(device)
+
 
 def example_keys() -> torch.Tensor:
     """8 key vectors of dimension 128, N(0,1), drawn as torch.randn(8, 128) after manual_seed(0)."""
