@@ -77,7 +77,7 @@ def traffic_from_profile(kernel: str, src_hash: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(sample_vectors: int = 65536, attn_tokens: int = 8192):
+def cpu_baseline(sample_vectors: int = 327680, attn_tokens: int = 8192):
     """The oracle as it stands, one thread, on a bounded sample of the same workload."""
     import numpy as np
     import torch
@@ -107,7 +107,7 @@ def cpu_baseline(sample_vectors: int = 65536, attn_tokens: int = 8192):
         # attention (the oracle's definition: decode the cache, then attend): one layer's 32
         # query heads over its 8 KV heads, T tokens each
         T = min(attn_tokens, sample_vectors // shape.kv_heads)
-        q = torch.randn(1, 32, d, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).float().numpy()
+        q = ti.normal((1, 32, d), 5, dtype=torch.bfloat16).float().numpy()
         t0 = time.perf_counter()
         khat = oatt.decode_cache(pk.reshape(shape.kv_heads, -1, pk.shape[-1])[:, :T],
                                  nk.reshape(shape.kv_heads, -1)[:, :T], pi, cbk.centroids, shape.key_bits, d)[None]
@@ -159,7 +159,7 @@ def main():
     vn = torch.empty(N, device=dev)
     ko = torch.empty(N, d, dtype=torch.bfloat16, device=dev)
     vo = torch.empty_like(ko)
-    q = torch.randn(L, Hq, d, generator=torch.Generator(device=dev).manual_seed(7), device=dev).to(torch.bfloat16)
+    q = ti.normal((L, Hq, d), 7, dtype=torch.bfloat16, device=dev)
     ao = torch.empty(L, Hq, d, dtype=torch.bfloat16, device=dev)
     kp4, kn4 = kp.view(L, H, T, -1), kn.view(L, H, T)
     vp4, vn4 = vp.view(L, H, T, -1), vn.view(L, H, T)
@@ -303,9 +303,7 @@ def next_rows(tq, ti, torch, dev, K, V, kp, kn, vp, vn, rot, ck, cv, q, kp4, kn4
     N = L * H * T
     out = {}
     # Hadamard rotation: same encode kernel, a different Pi
-    g = torch.Generator().manual_seed(1)
-    signs = (torch.randint(0, 2, (L, d), generator=g) * 2 - 1).to(torch.int8).numpy()
-    rh = tq.Rotation.hadamard(d, signs)
+    rh = tq.Rotation.hadamard(d, ti.random_signs(L, d, 1))
     ms = _time(torch, lambda: tq.encode(ck, rh, K, vectors_per_rot=H * T, packed=kp, norms=kn))
     alg = N * (d * 2 + d // 2 + 4)
     out["hadamard_encode_k"] = {"ms": round(ms, 4), "GB/s": round(alg / (ms * 1e-3) / 1e9, 1),

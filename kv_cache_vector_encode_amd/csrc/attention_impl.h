@@ -492,101 +492,126 @@ __device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
   return dt == TQ_BF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
 }
 
-template <int D>
+// One 16-byte piece of a full-precision row as floats (4 float32 or 8 bfloat16 / float16).
+template <int WDT>
+struct WinPiece {
+  static constexpr int PER = WDT == TQ_F32 ? 4 : 8;
+  static constexpr int ESZ = WDT == TQ_F32 ? 4 : 2;
+};
+template <int WDT>
+__device__ __forceinline__ void unpack_piece(const u32x4& p, float (&f)[WinPiece<WDT>::PER]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if constexpr (WDT == TQ_F32) {
+      f[c] = __uint_as_float(p[c]);
+    } else if constexpr (WDT == TQ_BF16) {
+      f[2 * c] = bf16_lo_to_f32(p[c]);
+      f[2 * c + 1] = bf16_hi_to_f32(p[c]);
+    } else {
+      f[2 * c] = f16_bits_to_f32(p[c]);
+      f[2 * c + 1] = f16_bits_to_f32(p[c] >> 16);
+    }
+  }
+}
+
+template <int WDT>
+__device__ __forceinline__ float win_elem(const void* p, int64_t i) {
+  if constexpr (WDT == TQ_F32) {
+    return ((const float*)p)[i];
+  } else {
+    const uint32_t bits = ((const uint16_t*)p)[i];
+    return WDT == TQ_BF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+  }
+}
+
+// GC = the head count G rounded up to 4, 8 or 16: every per-head loop runs GC times without a
+// branch (heads >= G get a zero query and are never written), so the loads of a loop can all
+// be in flight together.
+template <int D, int WDT, int GC>
 __global__ void __launch_bounds__(kWinChunk) window_kernel(WinKArgs a) {
-  constexpr int MAXG = 16;
   constexpr int NP = kWinChunk / D;   // token parts in the value phase (D <= kWinChunk)
-  __shared__ float qs[MAXG][D];
-  __shared__ float ps[MAXG][kWinChunk];
-  __shared__ float red[MAXG][kWinChunk / 64];
-  __shared__ float mrun[MAXG], lrun[MAXG], alpha[MAXG];
+  constexpr int PER = WinPiece<WDT>::PER, ESZ = WinPiece<WDT>::ESZ;
+  constexpr int NPIECE = D / PER;     // 16-byte pieces of a row
+  __shared__ f32x4 qs[D][GC / 4];     // query coordinate k of head g at qs[k][g / 4][g % 4]
+  __shared__ f32x4 ps[kWinChunk][GC / 4];   // softmax weight of chunk token i for head g
+  __shared__ float red[GC][kWinChunk / 64];
+  __shared__ float mrun[GC], lrun[GC], alpha[GC];
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int G = a.G, R = a.window;
   const int total = a.seq_lens ? max(0, min(a.seq_lens[b], a.max_seq_len)) : a.max_seq_len;
   const int w = min(total, R), c = total - w;
-  for (int i = tid; i < G * D; i += blockDim.x) {
+  for (int i = tid; i < GC * D; i += blockDim.x) {
     const int g = i / D, k = i - g * D;
-    qs[g][k] = load_elem(a.q, ((int64_t)b * a.Hq + kvh * G + g) * D + k, a.q_dtype);
+    ((float*)&qs[k][0])[g] = g < G ? load_elem(a.q, ((int64_t)b * a.Hq + kvh * G + g) * D + k, a.q_dtype) : 0.f;
   }
-  if (tid < MAXG) {
+  if (tid < GC) {
     mrun[tid] = -INFINITY;
     lrun[tid] = 0.f;
   }
-  float acc[MAXG];
+  float acc[GC];
 #pragma unroll
-  for (int g = 0; g < MAXG; ++g) acc[g] = 0.f;
+  for (int g = 0; g < GC; ++g) acc[g] = 0.f;
   __syncthreads();
   const int64_t ring = ((int64_t)b * a.Hkv + kvh) * R;   // first row of this head's ring
   for (int i0 = 0; i0 < w; i0 += kWinChunk) {
     const int n = min(kWinChunk, w - i0);
-    // scores of token i0 + tid against every head
-    float s[MAXG];
+    // scores of token i0 + tid against every head, the key row read piece by piece
+    float s[GC];
 #pragma unroll
-    for (int g = 0; g < MAXG; ++g) s[g] = -INFINITY;
+    for (int g = 0; g < GC; ++g) s[g] = 0.f;
     if (tid < n) {
       const int64_t row = ring + (c + i0 + tid) % R;
-#pragma unroll
-      for (int g = 0; g < MAXG; ++g)
-        if (g < G) s[g] = 0.f;
-      // the key row in 16-byte pieces, all loads in flight before the arithmetic
-      constexpr int NPIECE = D / 4;   // upper bound (float32); 16-bit rows use half of them
-      const int esz = a.w_dtype == TQ_F32 ? 4 : 2, per = 16 / esz, np = D / per;
-      const u32x4* kr = (const u32x4*)((const uint8_t*)a.kw + row * D * esz);
-      u32x4 pieces[NPIECE];
-#pragma unroll
-      for (int j = 0; j < NPIECE; ++j)
-        if (j < np) pieces[j] = kr[j];
-#pragma unroll
+      const u32x4* kr = (const u32x4*)((const uint8_t*)a.kw + row * D * ESZ);
+#pragma unroll 4
       for (int j = 0; j < NPIECE; ++j) {
-        if (j >= np) break;
+        float f[PER];
+        unpack_piece<WDT>(kr[j], f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (e >= per) break;
-          const uint32_t w32 = pieces[j][per == 4 ? e : e >> 1];
-          const float kv = a.w_dtype == TQ_F32 ? __uint_as_float(w32)
-                           : a.w_dtype == TQ_BF16 ? ((e & 1) ? bf16_hi_to_f32(w32) : bf16_lo_to_f32(w32))
-                                                  : f16_bits_to_f32((e & 1) ? (w32 >> 16) : w32);
-          const int k = j * per + e;
+        for (int e = 0; e < PER; ++e) {
 #pragma unroll
-          for (int g = 0; g < MAXG; ++g)
-            if (g < G) s[g] = fmaf(kv, qs[g][k], s[g]);
+          for (int g4 = 0; g4 < GC / 4; ++g4) {
+            const f32x4 qv = qs[j * PER + e][g4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[4 * g4 + r] = fmaf(f[e], qv[r], s[4 * g4 + r]);
+          }
         }
       }
-#pragma unroll
-      for (int g = 0; g < MAXG; ++g)
-        if (g < G) s[g] *= a.scale;
     }
+#pragma unroll
+    for (int g = 0; g < GC; ++g) s[g] = tid < n ? s[g] * a.scale : -INFINITY;
     // chunk max per head
 #pragma unroll
-    for (int g = 0; g < MAXG; ++g) {
-      if (g >= G) break;
+    for (int g = 0; g < GC; ++g) {
       float m = s[g];
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, wave_xor(m, o));
       if (lane == 0) red[g][wv] = m;
     }
     __syncthreads();
-    if (tid < G) {
+    if (tid < GC) {
       float m = red[tid][0];
       for (int j = 1; j < kWinChunk / 64; ++j) m = fmaxf(m, red[tid][j]);
       const float mn = fmaxf(mrun[tid], m);
-      alpha[tid] = __expf(mrun[tid] - mn);   // 0 when mrun is -inf
+      alpha[tid] = mn == -INFINITY ? 1.f : __expf(mrun[tid] - mn);   // 0 when mrun is -inf
       mrun[tid] = mn;
     }
     __syncthreads();
+    {
+      float pw[GC];
 #pragma unroll
-    for (int g = 0; g < MAXG; ++g) {
-      if (g >= G) break;
-      const float p = tid < n ? __expf(s[g] - mrun[g]) : 0.f;
-      ps[g][tid] = p;
-      float l = p;
+      for (int g = 0; g < GC; ++g) {
+        pw[g] = tid < n ? __expf(s[g] - mrun[g]) : 0.f;
+        float l = pw[g];
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) l += wave_xor(l, o);
-      if (lane == 0) red[g][wv] = l;
+        for (int o = 32; o >= 1; o >>= 1) l += wave_xor(l, o);
+        if (lane == 0) red[g][wv] = l;
+      }
+#pragma unroll
+      for (int g4 = 0; g4 < GC / 4; ++g4) ps[tid][g4] = f32x4{pw[4 * g4], pw[4 * g4 + 1], pw[4 * g4 + 2], pw[4 * g4 + 3]};
     }
     __syncthreads();   // the chunk's weights and per-wave sums are visible from here
-    if (tid < G) {
+    if (tid < GC) {
       float l = 0.f;
       for (int j = 0; j < kWinChunk / 64; ++j) l += red[tid][j];
       lrun[tid] = lrun[tid] * alpha[tid] + l;
@@ -594,23 +619,27 @@ __global__ void __launch_bounds__(kWinChunk) window_kernel(WinKArgs a) {
     // values: thread (k = tid % D, part = tid / D) accumulates coordinate k over the chunk's
     // tokens i = part, part + NP, ...; the parts are summed once at the end
 #pragma unroll
-    for (int g = 0; g < MAXG; ++g)
-      if (g < G) acc[g] *= alpha[g];
+    for (int g = 0; g < GC; ++g) acc[g] *= alpha[g];
     {
       const int k = tid % D, part = tid / D;
+      int pos = (c + i0 + part) % R;
 #pragma unroll 8
       for (int i = part; i < n; i += NP) {
-        const int64_t row = ring + (c + i0 + i) % R;
-        const float vv = load_elem(a.vw, row * D + k, a.w_dtype);
+        const float vv = win_elem<WDT>(a.vw, (ring + pos) * D + k);
+        pos += NP;
+        if (pos >= R) pos -= R;
 #pragma unroll
-        for (int g = 0; g < MAXG; ++g)
-          if (g < G) acc[g] = fmaf(ps[g][i], vv, acc[g]);
+        for (int g4 = 0; g4 < GC / 4; ++g4) {
+          const f32x4 pv = ps[i][g4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[4 * g4 + r] = fmaf(pv[r], vv, acc[4 * g4 + r]);
+        }
       }
     }
     __syncthreads();
   }
   // sum the parts: part 0 threads collect the others through LDS (reusing ps)
-  float* red2 = &ps[0][0];   // needs NP * G * D floats <= MAXG * kWinChunk
+  float* red2 = (float*)&ps[0][0];   // needs (NP - 1) * G * D floats <= kWinChunk * GC
   const int k = tid % D, part = tid / D;
   if (part > 0)
     for (int g = 0; g < G; ++g) red2[((part - 1) * G + g) * D + k] = acc[g];
@@ -627,6 +656,16 @@ __global__ void __launch_bounds__(kWinChunk) window_kernel(WinKArgs a) {
       P[2 + k] = v;
     }
   }
+}
+
+template <int D, int WDT>
+static void launch_window(const WinKArgs& w, dim3 grid, hipStream_t st) {
+  if (w.G <= 4)
+    hipLaunchKernelGGL((window_kernel<D, WDT, 4>), grid, dim3(kWinChunk), 0, st, w);
+  else if (w.G <= 8)
+    hipLaunchKernelGGL((window_kernel<D, WDT, 8>), grid, dim3(kWinChunk), 0, st, w);
+  else
+    hipLaunchKernelGGL((window_kernel<D, WDT, 16>), grid, dim3(kWinChunk), 0, st, w);
 }
 
 // Query heads handled together by qrot_kernel / merge_kernel (a block reads each rotation entry
@@ -853,7 +892,13 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
     w.G = a.G;
     w.slot = a.s_eff;
     w.scale = p->scale;
-    hipLaunchKernelGGL((window_kernel<D>), dim3((unsigned)p->num_kv_heads, (unsigned)B), dim3(kWinChunk), 0, st, w);
+    const dim3 wg((unsigned)p->num_kv_heads, (unsigned)B);
+    if (p->window_dtype == TQ_F32)
+      launch_window<D, TQ_F32>(w, wg, st);
+    else if (p->window_dtype == TQ_BF16)
+      launch_window<D, TQ_BF16>(w, wg, st);
+    else
+      launch_window<D, TQ_F16>(w, wg, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t rs = (int64_t)(rv.f32_stride / sizeof(float));
