@@ -7,7 +7,8 @@
 // of rotated coordinates hh*d/2 .. +d/2 of vector v, turns 8 codes at a time into an fp16
 // MFMA B operand, and one 32x32x16 fp16 MFMA per (output tile, K block) against prebuilt
 // tiles of Pi^T (resident in LDS) leaves output coordinates hh*d/2 + 16t + i in accumulator
-// register i, which are scaled by n and stored 16 at a time. fp16 operands (2^-11 relative)
+// register i, which are scaled by n, staged in LDS and stored with the wave's other rows as
+// one contiguous block. fp16 operands (2^-11 relative)
 // keep the decode within ~2e-4 of the float64 result, well inside the 2e-3 parity bound.
 #include "device_common.h"
 #include "tq_internal.h"
@@ -27,12 +28,14 @@ struct DecodeKArgs {
   uint32_t ctab[8];   // 16 fp16 centroids, two per word
 };
 
-// Four waves per workgroup and one workgroup per CU: the decode is bound by its output
-// stores, and HBM write throughput drops when more waves keep stores in flight at once
-// (fewer writers with a smaller address window sustain more bytes/s). Latency within a wave
-// is hidden by computing two output tiles at a time instead.
+// Four waves per workgroup, two workgroups per CU (one where LDS allows only one: float32
+// outputs at d = 128, every output type at d = 256). The decode is bound by its output
+// stores; HBM write throughput drops when many waves keep scattered stores in flight, so each
+// wave stages its 32 output rows in LDS and writes them as one contiguous block, 1 KiB per
+// store instruction, and latency within a wave is hidden by computing two output tiles at a
+// time.
 constexpr int kDecWaves = 4;
-constexpr int kStageBytes = 4096;   // per-wave output staging buffer
+constexpr int kDecWgPerCu = 2;
 
 template <int D, int BITS>
 struct DecGeo {
@@ -47,17 +50,16 @@ struct DecGeo {
   static constexpr int PER_LOOKUP = BITS == 2 ? 4 : 2;
   static constexpr int TAB_N = 1 << (PER_LOOKUP * BITS);
   static constexpr int TAB_WORDS = TAB_N * PER_LOOKUP / 2;
-  // Outputs are staged through LDS so that stores go out as 64-byte runs (d <= 128; at d=256
-  // the Pi^T tiles fill LDS and lanes store their own 16-byte pieces).
+  // Outputs are staged through LDS so that a wave's 32 output rows, one contiguous block, go
+  // out as 1 KiB per store instruction (d <= 128; at d=256 the Pi^T tiles fill LDS and lanes
+  // store their own 16-byte pieces).
   static constexpr bool STAGE = D <= 128;
-  static constexpr size_t lds_bytes() {
-    return (size_t)FRAG_U4 * 16 + (STAGE ? (size_t)kDecWaves * kStageBytes : 0);
+  static constexpr size_t stage_bytes(int out_elem) { return STAGE ? (size_t)32 * D * out_elem : 0; }
+  static constexpr size_t lds_bytes(int out_elem) {
+    return (size_t)FRAG_U4 * 16 + (size_t)kDecWaves * stage_bytes(out_elem);
   }
 };
 
-// 16-byte chunk c of a wave's staging buffer lives at chunk c ^ ((c >> 4) & 7): the 16 lanes
-// that write (chunk stride 8) or read (stride 1) together then hit 16 distinct bank groups.
-__device__ __forceinline__ uint32_t stage_swizzle(uint32_t c) { return c ^ ((c >> 4) & 7u); }
 
 template <int D, int BITS, int OUT, bool SLOT>
 __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
@@ -93,7 +95,8 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
   if (ntile <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vl = lane & 31, hh = lane >> 5;
-  uint8_t* stg = (uint8_t*)(smem + Geo::FRAG_U4) + wave * kStageBytes;
+  constexpr int OE = OUT == TQ_F32 ? 4 : 2;
+  uint8_t* stg = (uint8_t*)(smem + Geo::FRAG_U4) + wave * Geo::stage_bytes(OE);
 
   // Two-stage prefetch: the packed row of the next tile is loaded while this tile is decoded,
   // and with a slot gather the slot index is read one tile earlier still. Every load and store
@@ -215,29 +218,32 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
         ch[1] = u32x4{w[4], w[5], w[6], w[7]};
       }
       if constexpr (Geo::STAGE) {
-        // piece p = 2 v + hh holds 64 bytes of one half vector: tiles t0 .. t0+S-1
-        const uint32_t c0 = 4u * (2u * vl + hh) + (t % S) * CPT;
+        // staged in row-major order (row v = the wave's vector v), 16-byte chunks XOR-swizzled
+        // within a row by the row index so that the 32 rows written together spread over banks
+        constexpr uint32_t RC = D * E / 16;                  // 16-byte chunks per output row
+        constexpr uint32_t SW = RC >= 16 ? 15u : RC - 1u;
+        const uint32_t c0 = hh * (HALF * E / 16) + t * CPT;
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) *(u32x4*)(stg + 16 * stage_swizzle(c0 + k)) = ch[k];
-        if (t % S == S - 1) {
-          // the wave's LDS operations run in order, so its own writes above are visible here;
-          // each group of 4 lanes then writes one 64-byte run
-          const int t0 = t - (S - 1);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t c = 64u * j + lane;
-            const u32x4 q = *(const u32x4*)(stg + 16 * stage_swizzle(c));
-            const uint32_t p = c >> 2;
-            const int64_t pv = vbase + (p >> 1);
-            uint8_t* dst = pv < v_end ? (uint8_t*)a.out + (pv * D + (p & 1) * HALF + 16 * t0) * E + (c & 3) * 16
-                                      : a.sink + 16 * lane;
-            *(u32x4*)dst = q;
-          }
-        }
+        for (int k = 0; k < CPT; ++k)
+          *(u32x4*)(stg + 16 * (vl * RC + ((c0 + k) ^ (vl & SW)))) = ch[k];
       } else {
         uint8_t* dst = vec < v_end ? (uint8_t*)a.out + (vec * D + hh * HALF + 16 * t) * E : a.sink + 64 * lane;
 #pragma unroll
         for (int k = 0; k < CPT; ++k) *(u32x4*)(dst + 16 * k) = ch[k];
+      }
+    }
+    if constexpr (Geo::STAGE) {
+      // the tile's 32 output rows are one contiguous block: 1 KiB per store instruction
+      constexpr uint32_t RB = D * E, RC = RB / 16;
+      constexpr uint32_t SW = RC >= 16 ? 15u : RC - 1u;
+      uint8_t* tbase = (uint8_t*)a.out + vbase * RB;
+#pragma unroll
+      for (uint32_t j = 0; j < 32 * RB / 1024; ++j) {
+        const uint32_t off = 1024u * j + 16u * lane;
+        const uint32_t rowi = off / RB, c = (off % RB) / 16;
+        const u32x4 q = *(const u32x4*)(stg + 16 * (rowi * RC + (c ^ (rowi & SW))));
+        uint8_t* dst = vbase + rowi < v_end ? tbase + off : a.sink + 16 * lane;
+        *(u32x4*)dst = q;
       }
     }
   }
@@ -262,7 +268,7 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
   const int64_t per_rot = L.vectors_per_rot ? L.vectors_per_rot : L.n;
   const int nrot = L.vectors_per_rot ? (int)((L.n + L.vectors_per_rot - 1) / L.vectors_per_rot) : 1;
   const int64_t tiles = (per_rot + 31) / 32;
-  const size_t lds = Geo::lds_bytes();
+  const size_t lds = Geo::lds_bytes(OUT == TQ_F32 ? 4 : 2);
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<D, BITS, OUT, SLOT>,
@@ -271,7 +277,7 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
     attr_done = true;
   }
   const int cu = device_cu_count(L.rot->device);
-  const int64_t want = cu;   // one workgroup per CU (see kDecWaves)
+  const int64_t want = (int64_t)cu * kDecWgPerCu;
   int64_t bx = (want + nrot - 1) / nrot;
   const int64_t need = (tiles + kDecWaves - 1) / kDecWaves;
   if (bx > need) bx = need;
