@@ -32,6 +32,7 @@
 #include <math.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "device_common.h"
 #include "tq_internal.h"
@@ -103,6 +104,45 @@ __device__ __forceinline__ void load_chunk(const uint8_t* row, int bitoff, uint3
   }
 }
 
+// The same through a buffer resource: `row` is the row's byte offset from the resource base.
+// Buffer loads take a 32-bit offset next to a uniform base, so a lane's address costs no 64-bit
+// arithmetic.
+template <int NB, int ROWB>
+__device__ __forceinline__ void load_chunk_buf(__amdgpu_buffer_rsrc_t rs, uint32_t row, int bitoff,
+                                               uint32_t (&out)[(NB + 31) / 32]) {
+  constexpr int NW = (NB + 31) / 32;
+  if constexpr (NB % 32 == 0) {
+    const uint32_t o = row + (uint32_t)bitoff / 8;
+    if constexpr (NW == 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0);
+      out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+    } else if constexpr (NW == 2) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0);
+      out[0] = v[0]; out[1] = v[1];
+    } else {
+#pragma unroll
+      for (int k = 0; k < NW; ++k) out[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, o + 4 * k, 0, 0);
+    }
+  } else if constexpr (NB == 16) {
+    out[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, row + (uint32_t)bitoff / 8, 0, 0);
+  } else if constexpr (NB == 8) {
+    out[0] = __builtin_amdgcn_raw_buffer_load_b8(rs, row + (uint32_t)bitoff / 8, 0, 0);
+  } else {
+    constexpr int ROW_DW = ROWB / 4;
+    const int idx = bitoff >> 5;
+    const uint32_t sh = (uint32_t)bitoff & 31u;
+    uint32_t w[NW + 1];
+#pragma unroll
+    for (int k = 0; k <= NW; ++k) w[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, row + 4u * min(idx + k, ROW_DW - 1), 0, 0);
+#pragma unroll
+    for (int k = 0; k < NW; ++k) out[k] = funnel(w[k + 1], w[k], sh);
+  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
 // PB bits at bit `pos` of w (pos is a compile-time constant after unrolling)
 template <int PB, int NW>
 __device__ __forceinline__ uint32_t bits_at(const uint32_t (&w)[NW], int pos) {
@@ -126,10 +166,10 @@ __device__ __forceinline__ uint32_t interleave2(uint32_t a, uint32_t b) {
   return y;
 }
 
-// register budget: waves per SIMD 4 at d=64 (<= 128 registers; 3 with the QJL operands), 3 at
-// d=128 (<= 168), 2 at d=256 (twice the accumulators)
+// register budget: waves per SIMD 3 at d=64 (<= 168 registers), 3 at d=128 (2 with the QJL
+// operands), 2 at d=256 (twice the accumulators)
 template <int D, bool QJL>
-constexpr int attn_wpe() { return D == 256 ? 2 : D == 128 ? 3 : (QJL ? 3 : 4); }
+constexpr int attn_wpe() { return D == 256 ? 2 : D == 128 ? (QJL ? 2 : 3) : 3; }
 
 template <int D, int BK, int BV, bool SCORES, int PAGE, bool QJL>
 __global__ void __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(attn_wpe<D, QJL>())))
@@ -252,6 +292,17 @@ attn_kernel(AttnKArgs a) {
     uint32_t seg[SCORES ? 1 : 8][NWV];
   };
   const int64_t dense_base = ((int64_t)b * a.Hkv + kvh) * a.max_seq_len;
+  // Dense caches are addressed from this (sequence, KV head)'s first row with 32-bit offsets
+  // (a uniform base plus a per-lane offset needs no 64-bit arithmetic per token); paged pools
+  // from their first row with 64-bit rows.
+  const int64_t base_row = PAGE == kDense ? dense_base : 0;
+  const uint8_t* kp0 = a.kp + base_row * ROWK;
+  const uint8_t* vp0 = a.vp + base_row * ROWV;
+  const float* kn0 = a.kn + base_row;
+  const float* vn0 = a.vn + base_row;
+  const uint8_t* ks0 = QJL ? a.ksg + base_row * (D / 8) : nullptr;
+  const float* kr0 = QJL ? a.krn + base_row : nullptr;
+  using Row = typename std::conditional<PAGE == kDense, uint32_t, int64_t>::type;
   const int32_t* btab = a.block_table + (int64_t)b * a.mbps;
   auto pages = [&](int t0, int& p0, int& p1) {
     if constexpr (PAGE == kPagedPow2) {
@@ -261,9 +312,9 @@ attn_kernel(AttnKArgs a) {
       p0 = p1 = 0;
     }
   };
-  auto row_of = [&](int tt, int t0, int p0, int p1) -> int64_t {
+  auto row_of = [&](int tt, int t0, int p0, int p1) -> Row {
     if constexpr (PAGE == kDense) {
-      return dense_base + tt;
+      return (uint32_t)tt;
     } else if constexpr (PAGE == kPagedPow2) {
       const int phys = ((tt >> a.bs_shift) == (t0 >> a.bs_shift)) ? p0 : p1;
       return (((int64_t)phys * a.Hkv + kvh) << a.bs_shift) + (tt & (a.block_size - 1));
@@ -273,46 +324,64 @@ attn_kernel(AttnKArgs a) {
     }
   };
   auto tok = [&](int t0, int e) { return min(t0 + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4)), last); };
+  // dense: buffer resources over this (sequence, KV head)'s rows (max_seq_len rows each)
+  const uint32_t nrows = PAGE == kDense ? (uint32_t)a.max_seq_len : 0u;
+  const __amdgpu_buffer_rsrc_t r_kp = buffer_rsrc(kp0, nrows * ROWK), r_vp = buffer_rsrc(vp0, nrows * ROWV);
+  const __amdgpu_buffer_rsrc_t r_kn = buffer_rsrc(kn0, nrows * 4), r_vn = buffer_rsrc(vn0, nrows * 4);
+  const __amdgpu_buffer_rsrc_t r_ks = buffer_rsrc(ks0, QJL ? nrows * (D / 8) : 0u);
+  const __amdgpu_buffer_rsrc_t r_kr = buffer_rsrc(kr0, QJL ? nrows * 4 : 0u);
   auto fetch_k = [&](int t0, int p0, int p1, KBlk& B) {
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
       const int tk = min(t0 + 16 * tile + n16, last);
-      const int64_t row = row_of(tk, t0, p0, p1);
-      load_chunk<NBK, ROWK>(a.kp + row * ROWK, q4 * NBK, B.kc[tile]);
-      if constexpr (QJL) load_chunk<NBS, D / 8>(a.ksg + row * (D / 8), q4 * NBS, B.sg[tile]);
+      const Row row = row_of(tk, t0, p0, p1);
+      if constexpr (PAGE == kDense) {
+        load_chunk_buf<NBK, ROWK>(r_kp, row * ROWK, q4 * NBK, B.kc[tile]);
+        if constexpr (QJL) load_chunk_buf<NBS, D / 8>(r_ks, row * (D / 8), q4 * NBS, B.sg[tile]);
+      } else {
+        load_chunk<NBK, ROWK>(kp0 + row * (Row)ROWK, q4 * NBK, B.kc[tile]);
+        if constexpr (QJL) load_chunk<NBS, D / 8>(ks0 + row * (Row)(D / 8), q4 * NBS, B.sg[tile]);
+      }
     }
   };
   auto fetch_v = [&](int t0, int p0, int p1, VBlk& B) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int64_t row = row_of(tok(t0, e), t0, p0, p1);
-      B.kn[e] = a.kn[row];
-      if constexpr (QJL) B.rn[e] = a.krn[row];
-      if constexpr (!SCORES) {
-        B.vn[e] = a.vn[row];
-        load_chunk<NBV, ROWV>(a.vp + row * ROWV, n16 * NBV, B.seg[e]);
+      const Row row = row_of(tok(t0, e), t0, p0, p1);
+      if constexpr (PAGE == kDense) {
+        B.kn[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_kn, row * 4, 0, 0));
+        if constexpr (QJL) B.rn[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_kr, row * 4, 0, 0));
+        if constexpr (!SCORES) {
+          B.vn[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_vn, row * 4, 0, 0));
+          load_chunk_buf<NBV, ROWV>(r_vp, row * ROWV, n16 * NBV, B.seg[e]);
+        }
+      } else {
+        B.kn[e] = kn0[row];
+        if constexpr (QJL) B.rn[e] = kr0[row];
+        if constexpr (!SCORES) {
+          B.vn[e] = vn0[row];
+          load_chunk<NBV, ROWV>(vp0 + row * (Row)ROWV, n16 * NBV, B.seg[e]);
+        }
       }
     }
   };
 
-  // Key codes are fetched one block ahead; a block's norms and value codes are fetched at the
-  // start of its own iteration, ahead of the score MFMAs that precede their use.
+  // Loads run one block ahead without a second buffer set: the next block's key codes are
+  // loaded into the current ones' registers as soon as the scores have been formed, and its
+  // norms and value codes into theirs after the P.V products. The first use of each
+  // register set then waits only for loads issued most of a block earlier (copying a
+  // prefetch buffer at the end of an iteration would drain every load in flight instead).
   if (start < end) {
-    KBlk cur;
-    int p0, p1, np0, np1;
-    pages(start, p0, p1);
-    fetch_k(start, p0, p1, cur);
-    pages(start + 32, np0, np1);
-    wait_vmem_all();
     uint32_t qoff = (uint32_t)lane * 16u;
-
+    KBlk cur;
+    VBlk vb;
+    int q0, q1;   // pages of the next block to fetch
+    pages(start, q0, q1);
+    fetch_k(start, q0, q1, cur);
+    fetch_v(start, q0, q1, vb);
+    pages(start + 32, q0, q1);
+    wait_vmem_all();
     for (int t0 = start; t0 < end; t0 += 32) {
-      VBlk vb;
-      fetch_v(t0, p0, p1, vb);
-      KBlk nxt;
-      fetch_k(t0 + 32, np0, np1, nxt);
-      int nnp0, nnp1;
-      pages(t0 + 64, nnp0, nnp1);
       // query operands are re-read from LDS each block rather than held in 8*KB registers
       asm volatile("" : "+v"(qoff));
       const char* qbase = (const char*)sq + qoff;
@@ -371,6 +440,8 @@ attn_kernel(AttnKArgs a) {
           s[4 * tile + r] = v;
         }
       }
+      // this block's key codes are consumed: their registers now take the next block's
+      fetch_k(t0 + 32, q0, q1, cur);
       if constexpr (!SCORES) {
         // ---- online softmax; weights p_t n^v_t / N with N the running max V norm
         float mb = s[0], nb = vb.vn[0];
@@ -438,11 +509,9 @@ attn_kernel(AttnKArgs a) {
           }
         }
       }
-      cur = nxt;
-      p0 = np0;
-      p1 = np1;
-      np0 = nnp0;
-      np1 = nnp1;
+      // this block's norms and value codes are consumed: load the next block's
+      fetch_v(t0 + 32, q0, q1, vb);
+      pages(t0 + 64, q0, q1);
     }
   }
 
@@ -672,21 +741,28 @@ static void launch_window(const WinKArgs& w, dim3 grid, hipStream_t st) {
 // once for all of them); kept small so that there are enough blocks to hide load latency.
 constexpr int kHeadsPerBlock = 2;
 
-// q' = Pi_K q for up to 8 query heads of one sequence. Thread k owns output coordinate k and
-// walks Pi_K^T row by row (coalesced across threads); the queries sit in LDS.
+// Parts per output coordinate in qrot_kernel / merge_kernel: thread (k, part) covers 1/kParts
+// of a length-D (or length-s_eff) sum, so a thread's chain of dependent loads is kParts times
+// shorter; the parts meet in LDS.
+constexpr int kParts = 4;
+
+// q' = Pi_K q for kHeadsPerBlock query heads of one sequence. Thread (k, part) owns output
+// coordinate k over the rows j of its part, reading Pi_K^T row by row (coalesced across k);
+// the queries sit in LDS.
 template <int D>
-__global__ void __launch_bounds__(D) qrot_kernel(const void* q, int q_dtype, const float* pikt, int64_t rot_stride,
-                                                 int Hq, int bpr, float* out) {
-  constexpr int HB = kHeadsPerBlock;
+__global__ void __launch_bounds__(D * kParts) qrot_kernel(const void* q, int q_dtype, const float* pikt,
+                                                          int64_t rot_stride, int Hq, int bpr, float* out) {
+  constexpr int HB = kHeadsPerBlock, JP = D / kParts;
   __shared__ float qs[HB][D];
+  __shared__ float red[kParts][HB][D];
   const int b = blockIdx.x, h0 = blockIdx.y * HB;
   const int nh = min(HB, Hq - h0);
-  const int k = threadIdx.x;
-#pragma unroll
-  for (int h = 0; h < HB; ++h) {
+  const int k = threadIdx.x % D, part = threadIdx.x / D;
+  for (int i = threadIdx.x; i < HB * D; i += blockDim.x) {
+    const int h = i / D, kk = i - h * D;
     float v = 0.f;
     if (h < nh) {
-      const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + k;
+      const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + kk;
       if (q_dtype == TQ_F32)
         v = ((const float*)q)[idx];
       else if (q_dtype == TQ_BF16)
@@ -694,119 +770,157 @@ __global__ void __launch_bounds__(D) qrot_kernel(const void* q, int q_dtype, con
       else
         v = f16_bits_to_f32(((const uint16_t*)q)[idx]);
     }
-    qs[h][k] = v;
+    qs[h][kk] = v;
   }
   __syncthreads();
   const int r = bpr ? b / bpr : 0;
-  const float* PT = pikt + r * rot_stride + k;   // PT[j*D] = Pi[k][j]
+  const float* PT = pikt + r * rot_stride + (int64_t)part * JP * D + k;   // PT[j*D] = Pi[k][part*JP + j]
   float acc[HB];
 #pragma unroll
   for (int h = 0; h < HB; ++h) acc[h] = 0.f;
 #pragma unroll 16
-  for (int j = 0; j < D; ++j) {
+  for (int j = 0; j < JP; ++j) {
     const float pv = PT[(int64_t)j * D];
 #pragma unroll
-    for (int h = 0; h < HB; ++h) acc[h] = fmaf(pv, qs[h][j], acc[h]);
+    for (int h = 0; h < HB; ++h) acc[h] = fmaf(pv, qs[h][part * JP + j], acc[h]);
   }
 #pragma unroll
-  for (int h = 0; h < HB; ++h)
-    if (h < nh) out[((int64_t)b * Hq + h0 + h) * D + k] = acc[h];
+  for (int h = 0; h < HB; ++h) red[part][h][k] = acc[h];
+  __syncthreads();
+  if (part == 0) {
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      if (h >= nh) continue;
+      float v = red[0][h][k];
+#pragma unroll
+      for (int pp = 1; pp < kParts; ++pp) v += red[pp][h][k];
+      out[((int64_t)b * Hq + h0 + h) * D + k] = v;
+    }
+  }
 }
 
-// Log-sum-exp merge of the token splits for up to 8 query heads of one sequence, then
-// o = Pi_V^T (sum_s acc_s e^(m_s - M)) / L. Thread k owns coordinate k.
+// Log-sum-exp merge of the token splits for kHeadsPerBlock query heads of one sequence, then
+// o = Pi_V^T (sum_s acc_s e^(m_s - M)) / L (+ the window's partial, already unrotated).
+// Thread (k, part) owns coordinate k over splits s = part, part + kParts, ... and over the
+// rows of its part in the final product.
 template <int D, int OUT>
-__global__ void __launch_bounds__(D) merge_kernel(const float* part, int s_eff, int has_window, int B, int Hq,
-                                                  int bpr, const float* piv, int64_t rot_stride, void* out,
-                                                  float* lse) {
-  constexpr int HB = kHeadsPerBlock, NW = D / 64;
+__global__ void __launch_bounds__(D * kParts) merge_kernel(const float* part, int s_eff, int has_window, int B,
+                                                           int Hq, int bpr, const float* piv, int64_t rot_stride,
+                                                           void* out, float* lse) {
+  constexpr int HB = kHeadsPerBlock, NW = D * kParts / 64, JP = D / kParts;
   __shared__ float orot[HB][D];
-  __shared__ float red[HB][NW];
-  __shared__ float Ms[HB];
+  __shared__ float red[kParts][HB][D];
+  __shared__ float redm[HB][NW];
+  __shared__ float lred[kParts][HB];
+  __shared__ float Ms[HB], Ls[HB];
   const int b = blockIdx.x, h0 = blockIdx.y * HB;
   const int nh = min(HB, Hq - h0);
-  const int k = threadIdx.x, lane = k & 63, wv = k >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int k = tid % D, pt = tid / D;
   const int64_t sstride = (int64_t)B * Hq * (D + 2);
   const float* P0 = part + ((int64_t)b * Hq + h0) * (D + 2);   // split s, head h: + s*sstride + h*(D+2)
+  const int ns = s_eff + has_window;
 
-  // M_h = max over splits of m_s (threads stride over the splits)
+  // M_h = max over splits (and the window) of m_s
 #pragma unroll
   for (int h = 0; h < HB; ++h) {
     float m = -INFINITY;
     if (h < nh)
-      for (int s = k; s < s_eff + has_window; s += D) m = fmaxf(m, P0[(int64_t)s * sstride + h * (D + 2)]);
+      for (int s = tid; s < ns; s += blockDim.x) m = fmaxf(m, P0[(int64_t)s * sstride + h * (D + 2)]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, wave_xor(m, o));
-    if (lane == 0) red[h][wv] = m;
+    if (lane == 0) redm[h][wv] = m;
   }
   __syncthreads();
-  if (k < HB) {
-    float m = red[k][0];
+  if (tid < HB) {
+    float m = redm[tid][0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) m = fmaxf(m, red[k][w]);
-    Ms[k] = m;
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, redm[tid][w]);
+    Ms[tid] = m;
   }
   __syncthreads();
 
-  float acc[HB], lsum[HB], M[HB];
+  // this part's splits
+  float acc[HB], lsum[HB];
 #pragma unroll
   for (int h = 0; h < HB; ++h) {
     acc[h] = 0.f;
     lsum[h] = 0.f;
-    M[h] = Ms[h];
-  }
+    const float M = Ms[h];
+    if (h < nh && M > -INFINITY) {
 #pragma unroll 4
-  for (int s = 0; s < s_eff; ++s) {
-    const float* Ps = P0 + (int64_t)s * sstride;
-#pragma unroll
-    for (int h = 0; h < HB; ++h) {
-      if (h < nh && M[h] > -INFINITY) {
-        const float ms = Ps[h * (D + 2)];
-        const float w = ms > -INFINITY ? __expf(ms - M[h]) : 0.f;
-        lsum[h] = fmaf(w, Ps[h * (D + 2) + 1], lsum[h]);
-        acc[h] = fmaf(w, Ps[h * (D + 2) + 2 + k], acc[h]);
+      for (int s = pt; s < s_eff; s += kParts) {
+        const float* Ps = P0 + (int64_t)s * sstride + h * (D + 2);
+        const float ms = Ps[0];
+        const float w = ms > -INFINITY ? __expf(ms - M) : 0.f;
+        lsum[h] = fmaf(w, Ps[1], lsum[h]);
+        acc[h] = fmaf(w, Ps[2 + k], acc[h]);
       }
     }
+    red[pt][h][k] = acc[h];
+    if (k == 0) lred[pt][h] = lsum[h];
   }
-  // the window's partial (original value domain) joins after the rotation back
-  float accw[HB];
+  __syncthreads();
+  if (tid < HB) {
+    float l = 0.f;
 #pragma unroll
-  for (int h = 0; h < HB; ++h) {
-    accw[h] = 0.f;
-    if (has_window && h < nh && M[h] > -INFINITY) {
-      const float* Pw = P0 + (int64_t)s_eff * sstride + h * (D + 2);
+    for (int pp = 0; pp < kParts; ++pp) l += lred[pp][tid];
+    // the window's partial joins the normalizer here and the output after the rotation back
+    if (has_window && tid < nh && Ms[tid] > -INFINITY) {
+      const float* Pw = P0 + (int64_t)s_eff * sstride + tid * (D + 2);
       const float ms = Pw[0];
-      const float w = ms > -INFINITY ? __expf(ms - M[h]) : 0.f;
-      lsum[h] = fmaf(w, Pw[1], lsum[h]);
-      accw[h] = w * Pw[2 + k];
+      if (ms > -INFINITY) l = fmaf(__expf(ms - Ms[tid]), Pw[1], l);
+    }
+    Ls[tid] = l;
+  }
+  __syncthreads();
+  if (pt == 0) {
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      float v = red[0][h][k];
+#pragma unroll
+      for (int pp = 1; pp < kParts; ++pp) v += red[pp][h][k];
+      orot[h][k] = Ls[h] > 0.f ? v / Ls[h] : 0.f;
     }
   }
-#pragma unroll
-  for (int h = 0; h < HB; ++h) orot[h][k] = lsum[h] > 0.f ? acc[h] / lsum[h] : 0.f;
   __syncthreads();
 
-  const float* Pv = piv + (bpr ? b / bpr : 0) * rot_stride + k;   // Pv[kk*D] = Pi[kk][k]
+  // o = Pi_V^T orot, this part's rows
+  const float* Pv = piv + (bpr ? b / bpr : 0) * rot_stride + (int64_t)pt * JP * D + k;   // Pv[j*D] = Pi[pt*JP + j][k]
   float o[HB];
 #pragma unroll
   for (int h = 0; h < HB; ++h) o[h] = 0.f;
 #pragma unroll 16
-  for (int kk = 0; kk < D; ++kk) {
-    const float pv = Pv[(int64_t)kk * D];
+  for (int j = 0; j < JP; ++j) {
+    const float pv = Pv[(int64_t)j * D];
 #pragma unroll
-    for (int h = 0; h < HB; ++h) o[h] = fmaf(pv, orot[h][kk], o[h]);
+    for (int h = 0; h < HB; ++h) o[h] = fmaf(pv, orot[h][pt * JP + j], o[h]);
   }
 #pragma unroll
-  for (int h = 0; h < HB; ++h) {
-    if (h >= nh) continue;
-    if (lsum[h] > 0.f) o[h] += accw[h] / lsum[h];
-    const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + k;
-    if constexpr (OUT == TQ_F32)
-      ((float*)out)[idx] = o[h];
-    else if constexpr (OUT == TQ_BF16)
-      ((uint16_t*)out)[idx] = (uint16_t)f32_to_bf16_bits(o[h]);
-    else
-      ((uint16_t*)out)[idx] = (uint16_t)f32_to_f16_bits(o[h]);
-    if (k == 0 && lse) lse[(int64_t)b * Hq + h0 + h] = lsum[h] > 0.f ? M[h] + logf(lsum[h]) : -INFINITY;
+  for (int h = 0; h < HB; ++h) red[pt][h][k] = o[h];
+  __syncthreads();
+  if (pt == 0) {
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      if (h >= nh) continue;
+      float v = red[0][h][k];
+#pragma unroll
+      for (int pp = 1; pp < kParts; ++pp) v += red[pp][h][k];
+      const float L = Ls[h];
+      if (has_window && L > 0.f && Ms[h] > -INFINITY) {
+        const float* Pw = P0 + (int64_t)s_eff * sstride + h * (D + 2);
+        const float ms = Pw[0];
+        if (ms > -INFINITY) v += __expf(ms - Ms[h]) * Pw[2 + k] / L;
+      }
+      const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + k;
+      if constexpr (OUT == TQ_F32)
+        ((float*)out)[idx] = v;
+      else if constexpr (OUT == TQ_BF16)
+        ((uint16_t*)out)[idx] = (uint16_t)f32_to_bf16_bits(v);
+      else
+        ((uint16_t*)out)[idx] = (uint16_t)f32_to_f16_bits(v);
+      if (k == 0 && lse) lse[(int64_t)b * Hq + h0 + h] = L > 0.f ? Ms[h] + logf(L) : -INFINITY;
+    }
   }
 }
 
@@ -818,7 +932,7 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   float* qrot = (float*)(ws + lay.qrot_off);
   const int Hq = p->num_q_heads, B = p->batch;
   const unsigned hblocks = (unsigned)((Hq + kHeadsPerBlock - 1) / kHeadsPerBlock);
-  hipLaunchKernelGGL((qrot_kernel<D>), dim3(B, hblocks), dim3(D), 0, st, p->q, p->q_dtype, rk.f32t(0),
+  hipLaunchKernelGGL((qrot_kernel<D>), dim3(B, hblocks), dim3(D * kParts), 0, st, p->q, p->q_dtype, rk.f32t(0),
                      (int64_t)(rk.f32_stride / sizeof(float)), Hq, p->batch_per_rot, qrot);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -826,7 +940,7 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   if constexpr (QJL) {
     // S q: the same product with S^T in place of Pi^T
     const Qjl& qj = p->qjl_k->q;
-    hipLaunchKernelGGL((qrot_kernel<D>), dim3(B, hblocks), dim3(D), 0, st, p->q, p->q_dtype, qj.st(0),
+    hipLaunchKernelGGL((qrot_kernel<D>), dim3(B, hblocks), dim3(D * kParts), 0, st, p->q, p->q_dtype, qj.st(0),
                        (int64_t)(qj.st_stride / sizeof(float)), Hq, p->batch_per_rot, qsk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -904,15 +1018,15 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   const int64_t rs = (int64_t)(rv.f32_stride / sizeof(float));
   switch (p->out_dtype) {
     case TQ_F32:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_F32>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, has_win, B, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F32>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, a.s_eff, has_win, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
       break;
     case TQ_BF16:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_BF16>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, has_win, B, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_BF16>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, a.s_eff, has_win, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
       break;
     default:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_F16>), dim3(B, hblocks), dim3(D), 0, st, a.part, a.s_eff, has_win, B, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F16>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, a.s_eff, has_win, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
   }
   return hipGetLastError();
