@@ -15,9 +15,16 @@ AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu) {
     if (pairs < 1) pairs = 1;
     int64_t nblk = ((int64_t)p->max_seq_len + 31) / 32;
     if (nblk < 1) nblk = 1;
-    int64_t target = (int64_t)num_cu * 16;
+    // one full round of resident waves (waves per SIMD x 4 SIMDs x CUs): a partial last round
+    // would run the chip at a fraction of its occupancy, and every extra wave pays the
+    // prologue (operand tables, query operands) and one more partial for the merge; at least
+    // 4 blocks of 32 tokens per wave
+    const int wpe = d == 256 ? attn_wpe<256, false>() : d == 128 ? (p->qjl_k ? attn_wpe<128, true>() : attn_wpe<128, false>())
+                                                                 : attn_wpe<64, false>();
+    const int64_t target = (int64_t)wpe * 4 * num_cu;
     int64_t s_eff = (target + pairs - 1) / pairs;
-    if (s_eff > nblk) s_eff = nblk;
+    const int64_t cap = nblk >= 8 ? nblk / 4 : 1;
+    if (s_eff > cap) s_eff = cap;
     if (s_eff < 1) s_eff = 1;
     splits = (int)((s_eff + kAttnWaves - 1) / kAttnWaves);
   }

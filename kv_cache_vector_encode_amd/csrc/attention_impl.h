@@ -166,13 +166,16 @@ __device__ __forceinline__ uint32_t interleave2(uint32_t a, uint32_t b) {
   return y;
 }
 
-// register budget: waves per SIMD 3 at d=64 (<= 168 registers), 3 at d=128 (2 with the QJL
-// operands), 2 at d=256 (twice the accumulators)
+// register budget (two buffer sets of block operands): waves per SIMD 3 at d <= 128 (<= 168
+// registers), 2 at d=256 (twice the accumulators); one step lower with the QJL operands or
+// 3-bit values (their 24-bit code segments take more registers)
 template <int D, bool QJL>
-constexpr int attn_wpe() { return D == 256 ? 2 : D == 128 ? (QJL ? 2 : 3) : 3; }
+constexpr int attn_wpe() { return D == 256 ? 2 : D == 128 ? (QJL ? 2 : 3) : (QJL ? 2 : 3); }
+template <int D, int BV, bool QJL>
+constexpr int attn_wpe_bv() { return (BV == 3 && !QJL) ? (D == 256 ? 1 : 2) : (D == 256 && QJL ? 1 : attn_wpe<D, QJL>()); }
 
 template <int D, int BK, int BV, bool SCORES, int PAGE, bool QJL>
-__global__ void __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(attn_wpe<D, QJL>())))
+__global__ void __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(attn_wpe_bv<D, BV, QJL>())))
 attn_kernel(AttnKArgs a) {
   constexpr int KB = D / 32;            // K blocks of the score MFMA
   constexpr int TV = D / 16;            // output tiles of the P.V MFMA
@@ -288,9 +291,9 @@ attn_kernel(AttnKArgs a) {
     uint32_t sg[QJL ? 2 : 1][NWS];
   };
   struct VBlk {
-    float kn[8], vn[SCORES ? 1 : 8], rn[QJL ? 8 : 1];
     uint32_t seg[SCORES ? 1 : 8][NWV];
   };
+  constexpr int NR = QJL ? 2 : 1;   // norm values a lane loads per block
   const int64_t dense_base = ((int64_t)b * a.Hkv + kvh) * a.max_seq_len;
   // Dense caches are addressed from this (sequence, KV head)'s first row with 32-bit offsets
   // (a uniform base plus a per-lane offset needs no 64-bit arithmetic per token); paged pools
@@ -327,9 +330,7 @@ attn_kernel(AttnKArgs a) {
   // dense: buffer resources over this (sequence, KV head)'s rows (max_seq_len rows each)
   const uint32_t nrows = PAGE == kDense ? (uint32_t)a.max_seq_len : 0u;
   const __amdgpu_buffer_rsrc_t r_kp = buffer_rsrc(kp0, nrows * ROWK), r_vp = buffer_rsrc(vp0, nrows * ROWV);
-  const __amdgpu_buffer_rsrc_t r_kn = buffer_rsrc(kn0, nrows * 4), r_vn = buffer_rsrc(vn0, nrows * 4);
   const __amdgpu_buffer_rsrc_t r_ks = buffer_rsrc(ks0, QJL ? nrows * (D / 8) : 0u);
-  const __amdgpu_buffer_rsrc_t r_kr = buffer_rsrc(kr0, QJL ? nrows * 4 : 0u);
   auto fetch_k = [&](int t0, int p0, int p1, KBlk& B) {
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
@@ -345,43 +346,72 @@ attn_kernel(AttnKArgs a) {
     }
   };
   auto fetch_v = [&](int t0, int p0, int p1, VBlk& B) {
+    if constexpr (!SCORES) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const Row row = row_of(tok(t0, e), t0, p0, p1);
-      if constexpr (PAGE == kDense) {
-        B.kn[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_kn, row * 4, 0, 0));
-        if constexpr (QJL) B.rn[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_kr, row * 4, 0, 0));
-        if constexpr (!SCORES) {
-          B.vn[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_vn, row * 4, 0, 0));
+      for (int e = 0; e < 8; ++e) {
+        const Row row = row_of(tok(t0, e), t0, p0, p1);
+        if constexpr (PAGE == kDense)
           load_chunk_buf<NBV, ROWV>(r_vp, row * ROWV, n16 * NBV, B.seg[e]);
-        }
-      } else {
-        B.kn[e] = kn0[row];
-        if constexpr (QJL) B.rn[e] = kr0[row];
-        if constexpr (!SCORES) {
-          B.vn[e] = vn0[row];
+        else
           load_chunk<NBV, ROWV>(vp0 + row * (Row)ROWV, n16 * NBV, B.seg[e]);
-        }
       }
     }
   };
+  // The block's norms come in one load per value kind: lane l < 32 reads the K norm of token
+  // t0 + l, lane l >= 32 the V norm of token t0 + l - 32 (the K norm again for scores), and
+  // with QJL keys every lane the residual norm of token t0 + l % 32. They are staged in LDS
+  // and read back as the 8 values of the lane's tokens (two runs of 4 consecutive tokens).
+  auto fetch_norms = [&](int t0, int p0, int p1, float (&nr)[NR]) {
+    const int tt = min(t0 + (lane & 31), last);
+    const Row row = row_of(tt, t0, p0, p1);
+    const float* np = (SCORES || lane < 32) ? kn0 : vn0;
+    nr[0] = np[row];
+    if constexpr (QJL) nr[1] = kr0[row];
+  };
+  __shared__ f32x4 nstage[kAttnWaves][QJL ? 24 : 16];
+  float* const nst = (float*)&nstage[wave][0];
 
-  // Loads run one block ahead without a second buffer set: the next block's key codes are
-  // loaded into the current ones' registers as soon as the scores have been formed, and its
-  // norms and value codes into theirs after the P.V products. The first use of each
-  // register set then waits only for loads issued most of a block earlier (copying a
-  // prefetch buffer at the end of an iteration would drain every load in flight instead).
+  // Double-buffered walk: at the top of a block every load of the next block (norms, key codes,
+  // value codes) is issued into the other buffer set, so each load has a whole block of work to
+  // arrive before its first use. The two sets alternate by unrolling the walk by two; copying a
+  // prefetch buffer instead would make the wave wait for every load in flight.
   if (start < end) {
     uint32_t qoff = (uint32_t)lane * 16u;
-    KBlk cur;
-    VBlk vb;
     int q0, q1;   // pages of the next block to fetch
-    pages(start, q0, q1);
-    fetch_k(start, q0, q1, cur);
-    fetch_v(start, q0, q1, vb);
-    pages(start + 32, q0, q1);
-    wait_vmem_all();
-    for (int t0 = start; t0 < end; t0 += 32) {
+    auto block = [&](int t0, const KBlk& cur, const VBlk& vb, const float (&nr)[NR], KBlk& kN, VBlk& vN,
+                     float (&nN)[NR]) {
+      fetch_norms(t0 + 32, q0, q1, nN);
+      fetch_k(t0 + 32, q0, q1, kN);
+      fetch_v(t0 + 32, q0, q1, vN);
+      pages(t0 + 64, q0, q1);
+      // this block's norms through LDS into the lane's 8 tokens
+      float kn[8], vn[SCORES ? 1 : 8], rn[QJL ? 8 : 1];
+      {
+        nst[lane] = nr[0];
+        if constexpr (QJL) nst[64 + (lane & 31)] = nr[1];
+        const f32x4 a0 = *(const f32x4*)&nst[4 * q4], a1 = *(const f32x4*)&nst[16 + 4 * q4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kn[i] = a0[i];
+          kn[4 + i] = a1[i];
+        }
+        if constexpr (!SCORES) {
+          const f32x4 b0 = *(const f32x4*)&nst[32 + 4 * q4], b1 = *(const f32x4*)&nst[48 + 4 * q4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vn[i] = b0[i];
+            vn[4 + i] = b1[i];
+          }
+        }
+        if constexpr (QJL) {
+          const f32x4 c0 = *(const f32x4*)&nst[64 + 4 * q4], c1 = *(const f32x4*)&nst[80 + 4 * q4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            rn[i] = c0[i];
+            rn[4 + i] = c1[i];
+          }
+        }
+      }
       // query operands are re-read from LDS each block rather than held in 8*KB registers
       asm volatile("" : "+v"(qoff));
       const char* qbase = (const char*)sq + qoff;
@@ -430,8 +460,8 @@ attn_kernel(AttnKArgs a) {
         for (int r = 0; r < 4; ++r) {
           const int tt = t0 + 16 * tile + 4 * q4 + r;
           const bool ok = tt < end;
-          float v = S[r] * sc * vb.kn[4 * tile + r];
-          if constexpr (QJL) v = fmaf(S2[r] * sc2, vb.rn[4 * tile + r], v);
+          float v = S[r] * sc * kn[4 * tile + r];
+          if constexpr (QJL) v = fmaf(S2[r] * sc2, rn[4 * tile + r], v);
           v = ok ? v : -INFINITY;
           if constexpr (SCORES) {
             float* dst = ok && head_ok ? a.scores + ((int64_t)b * a.Hq + h) * a.max_seq_len + tt : a.sink + lane;
@@ -440,15 +470,13 @@ attn_kernel(AttnKArgs a) {
           s[4 * tile + r] = v;
         }
       }
-      // this block's key codes are consumed: their registers now take the next block's
-      fetch_k(t0 + 32, q0, q1, cur);
       if constexpr (!SCORES) {
         // ---- online softmax; weights p_t n^v_t / N with N the running max V norm
-        float mb = s[0], nb = vb.vn[0];
+        float mb = s[0], nb = vn[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) {
           mb = fmaxf(mb, s[e]);
-          nb = fmaxf(nb, vb.vn[e]);
+          nb = fmaxf(nb, vn[e]);
         }
         mb = fmaxf(mb, wave_xor(mb, 16));
         mb = fmaxf(mb, wave_xor(mb, 32));
@@ -465,7 +493,7 @@ attn_kernel(AttnKArgs a) {
         for (int c = 0; c < 4; ++c) {
           const float e0 = __expf(s[2 * c] - m_new), e1 = __expf(s[2 * c + 1] - m_new);
           lsum += e0 + e1;
-          bw[c] = pack_f16x2(e0 * vb.vn[2 * c] * inv_n, e1 * vb.vn[2 * c + 1] * inv_n);
+          bw[c] = pack_f16x2(e0 * vn[2 * c] * inv_n, e1 * vn[2 * c + 1] * inv_n);
         }
         l_run = l_run * al + lsum;
         m_run = m_new;
@@ -509,9 +537,21 @@ attn_kernel(AttnKArgs a) {
           }
         }
       }
-      // this block's norms and value codes are consumed: load the next block's
-      fetch_v(t0 + 32, q0, q1, vb);
-      pages(t0 + 64, q0, q1);
+    };
+    KBlk kA, kB;
+    VBlk vA, vB;
+    float nA[NR], nB[NR];
+    pages(start, q0, q1);
+    fetch_norms(start, q0, q1, nA);
+    fetch_k(start, q0, q1, kA);
+    fetch_v(start, q0, q1, vA);
+    pages(start + 32, q0, q1);
+    wait_vmem_all();
+    for (int t0 = start;;) {
+      block(t0, kA, vA, nA, kB, vB, nB);
+      if ((t0 += 32) >= end) break;
+      block(t0, kB, vB, nB, kA, vA, nA);
+      if ((t0 += 32) >= end) break;
     }
   }
 
