@@ -293,3 +293,54 @@ def test_qjl_error_paths(dev):
     with pytest.raises(tq.TQError, match="not created on rot_k"):
         tq.scores_compressed(cb, other, q, kp, kn, qjl=sk, k_signs=torch.zeros(1, 2, 8, 16, dtype=torch.uint8,
                                                                              device=dev), k_rnorms=kn)
+
+
+def test_qjl_attention_with_window(dev):
+    # QJL keys in the compressed part, the newest min(L, R) tokens exact in the rings: one softmax
+    # over both (the window partial joins the merge like with plain keys)
+    from oracle import window as ow
+    d, mbits, bv, Hq, Hkv, B, T, R = 128, 3, 2, 8, 2, 3, 300, 40
+    log("case: qjl attention with a %d-token window" % R)
+    q = ti.attn_inputs(ti.AttnShape(B, Hq, Hkv, 1, d, mbits, bv), device=dev, seed=12)[0]
+    rk, pk = rotation_pair(d, [42])
+    rv, pv = rotation_pair(d, [542])
+    S = _sketches(d, [42])
+    sk = tq.QJLSketch(rk, S)
+    ck, cv = tq.Codebook(d, mbits), tq.Codebook(d, bv)
+    c = _qjl_cache(dev, B, Hkv, T, d, mbits, 500)
+    vp = ti.random_bytes((B, Hkv, T, d * bv // 8), 510, dev)
+    vn = ti.random_norms((B, Hkv, T), 511, device=dev)
+    kw = ti.normal((B, Hkv, R, d), 512, scale=4.0, dtype=torch.bfloat16, device=dev)
+    vw = ti.normal((B, Hkv, R, d), 513, scale=4.0, dtype=torch.bfloat16, device=dev)
+    lens = [300, 25, 41]
+    o, lse = tq.attn_decode(ck, rk, cv, rv, q, c["kp"], c["kn"], vp, vn,
+                            seq_lens=torch.tensor(lens, dtype=torch.int32, device=dev), out_dtype=torch.float32,
+                            return_lse=True, qjl=sk, k_signs=c["ks"], k_rnorms=c["kr"], k_window=kw, v_window=vw)
+    torch.cuda.synchronize()
+    codes, norms, signs, rnorms = _oracle_keys(c, d, mbits)
+    vhat = oatt.decode_cache(vp.cpu().numpy(), vn.cpu().numpy(), pv[0], ocb.codebook(d, bv).centroids, bv, d)
+    q64, S64, scale = to64(q), S[0].double().numpy(), 1 / math.sqrt(d)
+    kw64, vw64 = to64(kw), to64(vw)
+    cb = ocb.codebook(d, mbits)
+    G = Hq // Hkv
+    worst = 0.0
+    for b, L in enumerate(lens):
+        cpos, w = ow.split(L, R)
+        for h in range(Hq):
+            g = h // G
+            s_c = oqjl.scores(q64[b, h][None], codes[b, g, :cpos], norms[b, g, :cpos], signs[b, g, :cpos],
+                              rnorms[b, g, :cpos], pk[0], S64, cb.centroids, scale)[0] if cpos else np.zeros(0)
+            kwin = np.stack([kw64[b, g, t % R] for t in range(cpos, L)])
+            vwin = np.stack([vw64[b, g, t % R] for t in range(cpos, L)])
+            s_all = np.concatenate([s_c, scale * (kwin @ q64[b, h])])
+            vals = np.concatenate([vhat[b, g, :cpos], vwin])
+            m = s_all.max()
+            p = np.exp(s_all - m)
+            o_ref = (p / p.sum()) @ vals
+            lse_ref = m + math.log(p.sum())
+            bound = REL * float((p / p.sum()) @ np.linalg.norm(vals, axis=1))
+            err = float(np.linalg.norm(o[b, h].cpu().numpy().astype(np.float64) - o_ref))
+            worst = max(worst, err / bound)
+            assert err <= bound, (b, h, err, bound)
+            assert abs(float(lse[b, h]) - lse_ref) <= 1e-3 * max(1.0, abs(lse_ref))
+    log("qjl + window: worst error / bound %.3g" % worst)
