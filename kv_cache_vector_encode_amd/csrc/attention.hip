@@ -18,9 +18,9 @@ AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu) {
     // one full round of resident waves (waves per SIMD x 4 SIMDs x CUs): a partial last round
     // would run the chip at a fraction of its occupancy, and every extra wave pays the
     // prologue (operand tables, query operands) and one more partial for the merge; at least
-    // 4 blocks of 32 tokens per wave
-    const int wpe = d == 256 ? attn_wpe<256, false>() : d == 128 ? (p->qjl_k ? attn_wpe<128, true>() : attn_wpe<128, false>())
-                                                                 : attn_wpe<64, false>();
+    // 4 blocks of 32 tokens per wave. The round is counted for 2-bit values (other value widths
+    // run a fraction of a round more or less).
+    const int wpe = attn_wpe(d, p->cb_k->cb.bits, 2, p->qjl_k != nullptr, p->block_table != nullptr);
     const int64_t target = (int64_t)wpe * 4 * num_cu;
     int64_t s_eff = (target + pairs - 1) / pairs;
     const int64_t cap = nblk >= 8 ? nblk / 4 : 1;

@@ -139,6 +139,14 @@ __device__ __forceinline__ void load_chunk_buf(__amdgpu_buffer_rsrc_t rs, uint32
   }
 }
 
+// 2^x by the hardware instruction (x = -inf gives 0)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// the LDS word at byte offset `off` of table t
+__device__ __forceinline__ uint32_t lds_word(const uint32_t* t, uint32_t off) {
+  return *(const uint32_t*)((const char*)t + off);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
@@ -166,16 +174,31 @@ __device__ __forceinline__ uint32_t interleave2(uint32_t a, uint32_t b) {
   return y;
 }
 
-// register budget (two buffer sets of block operands): waves per SIMD 3 at d <= 128 (<= 168
-// registers), 2 at d=256 (twice the accumulators); one step lower with the QJL operands or
-// 3-bit values (their 24-bit code segments take more registers)
-template <int D, bool QJL>
-constexpr int attn_wpe() { return D == 256 ? 2 : D == 128 ? (QJL ? 2 : 3) : (QJL ? 2 : 3); }
-template <int D, int BV, bool QJL>
-constexpr int attn_wpe_bv() { return (BV == 3 && !QJL) ? (D == 256 ? 1 : 2) : (D == 256 && QJL ? 1 : attn_wpe<D, QJL>()); }
+// the same with a and b packed as a | b << 16: the byte interleave is one byte permute
+__device__ __forceinline__ uint32_t interleave2_packed(uint32_t x) {
+  uint32_t y = __builtin_amdgcn_perm(x, x, 0x03010200u);   // bytes a0, b0, a1, b1
+  uint32_t t = (y ^ (y >> 4)) & 0x00f000f0u;
+  y ^= t ^ (t << 4);
+  t = (y ^ (y >> 2)) & 0x0c0c0c0cu;
+  y ^= t ^ (t << 2);
+  return y;
+}
+
+// Waves per SIMD an attention kernel is built for (its register budget with two buffer sets
+// of block operands): 3 at d <= 128 (<= 168 registers), 4 for dense caches at d = 128 with
+// 4-bit keys and 2-bit values (their operands fit 128 registers), 2 at d = 256 (twice the
+// accumulators); one step lower with the QJL operands or 3-bit values (their 24-bit code
+// segments take more registers).
+constexpr int attn_wpe(int d, int bk, int bv, bool qjl, bool paged) {
+  return (bv == 3 && !qjl) ? (d == 256 ? 1 : 2)
+         : d == 256        ? (qjl ? 1 : 2)
+         : qjl             ? 2
+         : (d == 128 && bk == 4 && bv == 2 && !paged) ? 4
+                                                      : 3;
+}
 
 template <int D, int BK, int BV, bool SCORES, int PAGE, bool QJL>
-__global__ void __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(attn_wpe_bv<D, BV, QJL>())))
+__global__ void __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(attn_wpe(D, BK, BV, QJL, PAGE != kDense))))
 attn_kernel(AttnKArgs a) {
   constexpr int KB = D / 32;            // K blocks of the score MFMA
   constexpr int TV = D / 16;            // output tiles of the P.V MFMA
@@ -186,14 +209,24 @@ attn_kernel(AttnKArgs a) {
   constexpr int NWS = (NBS + 31) / 32;
   constexpr int ROWK = D * BK / 8, ROWV = D * BV / 8;
   constexpr int PK = 2 * BK;            // bits of a pair of K codes
-  constexpr int KTAB = 1 << PK;
-  constexpr int VTAB = BV == 2 ? 512 : (1 << (2 * BV));
-  // Code -> operand tables: a pair of K codes -> two bf16 hi (tkh) / lo (tkl) halves; for
-  // 2-bit V a byte of interleaved codes (two coordinates of two tokens) -> two fp16 pairs,
-  // else a pair of V codes (one coordinate of two tokens) -> one fp16 pair.
-  __shared__ uint32_t tkh[KTAB], tkl[KTAB];
+  // Code -> operand tables in LDS. A table of at most 16 words is read without bank conflicts
+  // (lanes that pick the same entry share one read); random picks from a 256-entry table cost
+  // several times that. So:
+  //   4-bit keys (K1): one lookup per code, word = the centroid's bf16 hi | lo << 16, and the
+  //     score MFMA's K dimension runs over (coordinate, hi / lo) with the query duplicated,
+  //     so one product takes (c_hi + c_lo) q_hi and a second one (c_hi + c_lo) q_lo;
+  //   2/3-bit keys: a pair of codes (at most 64 entries) -> two bf16 hi (tkh) / lo (tkl)
+  //     halves, three products per K block (c_hi q_hi + c_lo q_hi + c_hi q_lo);
+  //   values: a pair of V codes (one coordinate of two tokens) -> one fp16 pair; 2-bit codes
+  //     are first interleaved so that each nibble is such a pair.
+  constexpr bool K1 = BK == 4;
+  constexpr int KB1 = D / 16;           // score MFMAs per pass with one code per operand word
+  constexpr int KTAB = K1 ? 16 : 1 << PK;
+  constexpr int VTAB = 1 << (2 * BV);
+  __shared__ uint32_t tkh[KTAB], tkl[K1 ? 1 : KTAB];
   __shared__ uint32_t tv[SCORES ? 1 : VTAB];
-  __shared__ u32x4 sq[2 * KB * 64];   // query B operands [hi, lo][kb][lane], shared by the waves
+  constexpr int NQB = K1 ? KB1 : KB;    // query operand words per pass and lane
+  __shared__ u32x4 sq[2 * NQB * 64];   // query B operands [hi, lo][kb][lane], shared by the waves
   __shared__ u32x4 ssq[QJL ? 2 * KB * 64 : 1];   // the same for S q (QJL keys)
   {
     // centroids straight from the kernel-argument segment (`a` is the only argument)
@@ -202,24 +235,21 @@ attn_kernel(AttnKArgs a) {
     const uint32_t* kv = (const uint32_t*)(ka + offsetof(AttnKArgs, ctv));
     constexpr uint32_t MK = (1u << BK) - 1u, MV = (1u << BV) - 1u;
     for (int j = threadIdx.x; j < KTAB; j += blockDim.x) {
-      const uint32_t c0 = kk[j & MK], c1 = kk[j >> BK];
-      tkh[j] = (c0 & 0xffffu) | (c1 << 16);
-      tkl[j] = (c0 >> 16) | (c1 & 0xffff0000u);
+      if constexpr (K1) {
+        tkh[j] = kk[j];
+      } else {
+        const uint32_t c0 = kk[j & MK], c1 = kk[j >> BK];
+        tkh[j] = (c0 & 0xffffu) | (c1 << 16);
+        tkl[j] = (c0 >> 16) | (c1 & 0xffff0000u);
+      }
     }
     if constexpr (!SCORES) {
       auto cv = [&](uint32_t k) -> uint32_t { return (kv[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
-      if constexpr (BV == 2) {
-        for (int j = threadIdx.x; j < 256; j += blockDim.x) {
-          tv[2 * j] = cv(j & 3u) | (cv((j >> 2) & 3u) << 16);
-          tv[2 * j + 1] = cv((j >> 4) & 3u) | (cv((uint32_t)j >> 6) << 16);
-        }
-      } else {
-        for (int j = threadIdx.x; j < VTAB; j += blockDim.x) tv[j] = cv(j & MV) | (cv((uint32_t)j >> BV) << 16);
-      }
+      for (int j = threadIdx.x; j < VTAB; j += blockDim.x) tv[j] = cv(j & MV) | (cv((uint32_t)j >> BV) << 16);
     }
   }
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.z, kvh = blockIdx.y;
   const int sidx = blockIdx.x * kAttnWaves + wave;
   // compressed tokens: all but the newest min(L, window) of the sequence's L tokens
@@ -240,7 +270,10 @@ attn_kernel(AttnKArgs a) {
   //      large logits (outlier tokens) softmax turns score errors into weight errors, so fp16
   //      (2^-11) operands are not enough there. All waves of the workgroup serve the same
   //      (sequence, KV head); wave 0 leaves the operands in LDS and the loop reads them there.
-  auto query_operands = [&](const float* src, u32x4* dst) -> float {
+  //      With 4-bit keys (K1) the operand word c of K block kb holds coordinate
+  //      q4*d/4 + 4kb + c twice (the code side supplies hi and lo of that coordinate).
+  auto query_operands = [&](const float* src, u32x4* dst, auto dup) -> float {
+    constexpr bool DUP = decltype(dup)::value;
     float qv[D / 4];
     const float* qp = src + ((int64_t)b * a.Hq + h) * D + q4 * (D / 4);
     float mx = 0.f;
@@ -253,27 +286,45 @@ attn_kernel(AttnKArgs a) {
     mx = fmaxf(mx, wave_xor(mx, 32));
     const float qm = mx > 0.f ? mx : 1.f;
     const float inv = 1.0f / qm;
+    if constexpr (DUP) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB1; ++kb)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float v0 = qv[8 * kb + 2 * c] * inv, v1 = qv[8 * kb + 2 * c + 1] * inv;
-        const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
-        const uint32_t l0 = f32_to_bf16_bits(v0 - bf16_bits_to_f32(h0));
-        const uint32_t l1 = f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1));
-        if (wave == 0) {
-          ((uint32_t*)&dst[kb * 64 + lane])[c] = h0 | (h1 << 16);
-          ((uint32_t*)&dst[(KB + kb) * 64 + lane])[c] = l0 | (l1 << 16);
+        for (int c = 0; c < 4; ++c) {
+          const float v = qv[4 * kb + c] * inv;
+          const uint32_t h = f32_to_bf16_bits(v);
+          const uint32_t l = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
+          if (wave == 0) {
+            ((uint32_t*)&dst[kb * 64 + lane])[c] = h | (h << 16);
+            ((uint32_t*)&dst[(KB1 + kb) * 64 + lane])[c] = l | (l << 16);
+          }
         }
-      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float v0 = qv[8 * kb + 2 * c] * inv, v1 = qv[8 * kb + 2 * c + 1] * inv;
+          const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
+          const uint32_t l0 = f32_to_bf16_bits(v0 - bf16_bits_to_f32(h0));
+          const uint32_t l1 = f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1));
+          if (wave == 0) {
+            ((uint32_t*)&dst[kb * 64 + lane])[c] = h0 | (h1 << 16);
+            ((uint32_t*)&dst[(KB + kb) * 64 + lane])[c] = l0 | (l1 << 16);
+          }
+        }
+    }
     return qm;
   };
-  const float qmax = query_operands(a.qrot, sq);
+  const float qmax = query_operands(a.qrot, sq, std::integral_constant<bool, K1>{});
   float sqmax = 0.f;
-  if constexpr (QJL) sqmax = query_operands(a.qsk, ssq);
+  if constexpr (QJL) sqmax = query_operands(a.qsk, ssq, std::false_type{});
   __syncthreads();
-  const float sc = qmax * a.scale;
-  const float sc2 = sqmax * a.scale * a.qjl_c;
+  // the softmax runs in base 2 (v_exp_f32 is 2^x): fused-attention scores are kept in units of
+  // log2(e) and the running max is converted back when the partial is written
+  constexpr float kSU = SCORES ? 1.0f : 1.4426950408889634f;
+  const float sc = qmax * a.scale * kSU;
+  const float sc2 = sqmax * a.scale * a.qjl_c * kSU;
 
   float m_run = -INFINITY, l_run = 0.f, n_run = 0.f;
   f32x4 acc[TV];
@@ -290,8 +341,12 @@ attn_kernel(AttnKArgs a) {
     uint32_t kc[2][NWK];
     uint32_t sg[QJL ? 2 : 1][NWS];
   };
+  // 2-bit value segments of 16 bits (d = 128) are loaded in pairs into one register:
+  // pk[c] = segment of tok(2c) | segment of tok(2c+1) << 16
+  constexpr bool VPACK = !SCORES && BV == 2 && NBV == 16;
   struct VBlk {
-    uint32_t seg[SCORES ? 1 : 8][NWV];
+    uint32_t seg[SCORES || VPACK ? 1 : 8][NWV];
+    uint32_t pk[VPACK ? 4 : 1];
   };
   constexpr int NR = QJL ? 2 : 1;   // norm values a lane loads per block
   const int64_t dense_base = ((int64_t)b * a.Hkv + kvh) * a.max_seq_len;
@@ -327,19 +382,24 @@ attn_kernel(AttnKArgs a) {
     }
   };
   auto tok = [&](int t0, int e) { return min(t0 + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4)), last); };
-  // dense: buffer resources over this (sequence, KV head)'s rows (max_seq_len rows each)
-  const uint32_t nrows = PAGE == kDense ? (uint32_t)a.max_seq_len : 0u;
+  // dense: buffer resources over this (sequence, KV head)'s `len` compressed rows. Reads past
+  // them return 0 (the hardware's range check), so dense fetches need no clamping: a lane's
+  // offsets are a fixed part plus t0 * row bytes, and the tokens of one block differ by
+  // constants that the loads take as immediate offsets.
+  const uint32_t nrows = PAGE == kDense ? (uint32_t)len : 0u;
   const __amdgpu_buffer_rsrc_t r_kp = buffer_rsrc(kp0, nrows * ROWK), r_vp = buffer_rsrc(vp0, nrows * ROWV);
   const __amdgpu_buffer_rsrc_t r_ks = buffer_rsrc(ks0, QJL ? nrows * (D / 8) : 0u);
   auto fetch_k = [&](int t0, int p0, int p1, KBlk& B) {
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      const int tk = min(t0 + 16 * tile + n16, last);
-      const Row row = row_of(tk, t0, p0, p1);
       if constexpr (PAGE == kDense) {
-        load_chunk_buf<NBK, ROWK>(r_kp, row * ROWK, q4 * NBK, B.kc[tile]);
-        if constexpr (QJL) load_chunk_buf<NBS, D / 8>(r_ks, row * (D / 8), q4 * NBS, B.sg[tile]);
+        const uint32_t row = (uint32_t)t0 + (uint32_t)n16;
+        load_chunk_buf<NBK, ROWK>(r_kp, row * ROWK + 16u * tile * ROWK, q4 * NBK, B.kc[tile]);
+        if constexpr (QJL)
+          load_chunk_buf<NBS, D / 8>(r_ks, row * (D / 8) + 16u * tile * (D / 8), q4 * NBS, B.sg[tile]);
       } else {
+        const int tk = min(t0 + 16 * tile + n16, last);
+        const Row row = row_of(tk, t0, p0, p1);
         load_chunk<NBK, ROWK>(kp0 + row * (Row)ROWK, q4 * NBK, B.kc[tile]);
         if constexpr (QJL) load_chunk<NBS, D / 8>(ks0 + row * (Row)(D / 8), q4 * NBS, B.sg[tile]);
       }
@@ -347,13 +407,32 @@ attn_kernel(AttnKArgs a) {
   };
   auto fetch_v = [&](int t0, int p0, int p1, VBlk& B) {
     if constexpr (!SCORES) {
+      if constexpr (VPACK) {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const Row row = row_of(tok(t0, e), t0, p0, p1);
-        if constexpr (PAGE == kDense)
-          load_chunk_buf<NBV, ROWV>(r_vp, row * ROWV, n16 * NBV, B.seg[e]);
-        else
-          load_chunk<NBV, ROWV>(vp0 + row * (Row)ROWV, n16 * NBV, B.seg[e]);
+        for (int c = 0; c < 4; ++c) {
+          u16x2 v;
+          if constexpr (PAGE == kDense) {
+            const uint32_t o = ((uint32_t)t0 + 4u * q4) * ROWV + (uint32_t)n16 * 2u;
+            v[0] = __builtin_amdgcn_raw_buffer_load_b16(r_vp, o + (uint32_t)(2 * c < 4 ? 2 * c : 12 + 2 * c) * ROWV, 0, 0);
+            v[1] = __builtin_amdgcn_raw_buffer_load_b16(r_vp, o + (uint32_t)(2 * c + 1 < 4 ? 2 * c + 1 : 13 + 2 * c) * ROWV, 0, 0);
+          } else {
+            v[0] = *(const uint16_t*)(vp0 + row_of(tok(t0, 2 * c), t0, p0, p1) * (Row)ROWV + n16 * 2);
+            v[1] = *(const uint16_t*)(vp0 + row_of(tok(t0, 2 * c + 1), t0, p0, p1) * (Row)ROWV + n16 * 2);
+          }
+          B.pk[c] = __builtin_bit_cast(uint32_t, v);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (PAGE == kDense) {
+            const uint32_t row = (uint32_t)t0 + 4u * q4;
+            load_chunk_buf<NBV, ROWV>(r_vp, row * ROWV + (uint32_t)(e < 4 ? e : 12 + e) * ROWV, n16 * NBV, B.seg[e]);
+          } else {
+            const Row row = row_of(tok(t0, e), t0, p0, p1);
+            load_chunk<NBV, ROWV>(vp0 + row * (Row)ROWV, n16 * NBV, B.seg[e]);
+          }
+        }
       }
     }
   };
@@ -419,23 +498,58 @@ attn_kernel(AttnKArgs a) {
 
       // ---- scores of the block's two 16-token tiles
       float s[8];
+      f32x4 St[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      if constexpr (K1) {
+        // code p of the lane's chunk sits in nibble p % 8 of word p / 8: the table offsets of the
+        // even nibbles are the bytes of (w << 2) & 0x3c3c3c3c, those of the odd ones the bytes
+        // of (w >> 2) & 0x3c3c3c3c, one byte extract per lookup (the empty asm keeps the
+        // compiler from folding the masks back into a shift and a mask per lookup)
+#pragma unroll
+        for (int kw = 0; kw < KB1 / 2; ++kw) {
+          uint32_t we[2], wo[2];
+#pragma unroll
+          for (int tile = 0; tile < 2; ++tile) {
+            we[tile] = (cur.kc[tile][kw] << 2) & 0x3c3c3c3cu;
+            wo[tile] = (cur.kc[tile][kw] >> 2) & 0x3c3c3c3cu;
+            asm("" : "+v"(we[tile]), "+v"(wo[tile]));
+          }
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int kb = 2 * kw + half, sh = 16 * half;
+            const u32x4 qh = *(const u32x4*)(qbase + kb * 1024);
+            const u32x4 ql = *(const u32x4*)(qbase + (KB1 + kb) * 1024);
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile) {
+              u32x4 ak;
+              ak[0] = lds_word(tkh, (we[tile] >> sh) & 0xffu);
+              ak[1] = lds_word(tkh, (wo[tile] >> sh) & 0xffu);
+              ak[2] = lds_word(tkh, (we[tile] >> (sh + 8)) & 0xffu);
+              ak[3] = lds_word(tkh, (wo[tile] >> (sh + 8)) & 0xffu);
+              St[tile] = mfma16_bf16(ak, qh, St[tile]);
+              St[tile] = mfma16_bf16(ak, ql, St[tile]);
+            }
+          }
+        }
+      }
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile) {
-        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+        f32x4 S = St[tile];
+        if constexpr (!K1) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          u32x4 akh, akl;
+          for (int kb = 0; kb < KB; ++kb) {
+            u32x4 akh, akl;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint32_t idx = bits_at<PK>(cur.kc[tile], (4 * kb + c) * PK);
-            akh[c] = tkh[idx];
-            akl[c] = tkl[idx];
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t idx = bits_at<PK>(cur.kc[tile], (4 * kb + c) * PK);
+              akh[c] = tkh[idx];
+              akl[c] = tkl[idx];
+            }
+            const u32x4 qh = *(const u32x4*)(qbase + kb * 1024);
+            const u32x4 ql = *(const u32x4*)(qbase + (KB + kb) * 1024);
+            S = mfma16_bf16(akh, qh, S);
+            S = mfma16_bf16(akl, qh, S);
+            S = mfma16_bf16(akh, ql, S);
           }
-          const u32x4 qh = *(const u32x4*)(qbase + kb * 1024);
-          const u32x4 ql = *(const u32x4*)(qbase + (KB + kb) * 1024);
-          S = mfma16_bf16(akh, qh, S);
-          S = mfma16_bf16(akl, qh, S);
-          S = mfma16_bf16(akh, ql, S);
         }
         // QJL term: <S q, signs> with the signs as exact bf16 +-1 (bit 1 -> +1) against S q hi + lo
         f32x4 S2 = {0.f, 0.f, 0.f, 0.f};
@@ -458,16 +572,24 @@ attn_kernel(AttnKArgs a) {
         // D layout: lane (head n16, q4) register r = token t0 + 16*tile + 4*q4 + r = tok(4*tile + r)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int tt = t0 + 16 * tile + 4 * q4 + r;
-          const bool ok = tt < end;
-          float v = S[r] * sc * kn[4 * tile + r];
+          float v = S[r] * sc * kn[4 * tile + r];   // sc is per head (the query's normalization)
           if constexpr (QJL) v = fmaf(S2[r] * sc2, rn[4 * tile + r], v);
-          v = ok ? v : -INFINITY;
           if constexpr (SCORES) {
+            const int tt = t0 + 16 * tile + 4 * q4 + r;
+            const bool ok = tt < end;
+            v = ok ? v : -INFINITY;
             float* dst = ok && head_ok ? a.scores + ((int64_t)b * a.Hq + h) * a.max_seq_len + tt : a.sink + lane;
             *dst = v;
           }
           s[4 * tile + r] = v;
+        }
+      }
+      if constexpr (!SCORES) {
+        // only a wave's last block can run past its range: mask there (a uniform branch)
+        if (t0 + 32 > end) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (t0 + 16 * (e >> 2) + 4 * q4 + (e & 3) >= end) s[e] = -INFINITY;
         }
       }
       if constexpr (!SCORES) {
@@ -484,14 +606,14 @@ attn_kernel(AttnKArgs a) {
         nb = fmaxf(nb, wave_xor(nb, 32));
         const float m_new = fmaxf(m_run, mb);
         const float n_new = fmaxf(n_run, nb);
-        const float al = __expf(m_run - m_new);
+        const float al = exp2_fast(m_run - m_new);
         const float inv_n = n_new > 0.f ? 1.0f / n_new : 0.f;
         const float a_acc = al * n_run * inv_n;
         float lsum = 0.f;
         u32x4 bw;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float e0 = __expf(s[2 * c] - m_new), e1 = __expf(s[2 * c + 1] - m_new);
+          const float e0 = exp2_fast(s[2 * c] - m_new), e1 = exp2_fast(s[2 * c + 1] - m_new);
           lsum += e0 + e1;
           bw[c] = pack_f16x2(e0 * vn[2 * c] * inv_n, e1 * vn[2 * c + 1] * inv_n);
         }
@@ -509,18 +631,27 @@ attn_kernel(AttnKArgs a) {
         if constexpr (BV == 2) {
 #pragma unroll
           for (int ch = 0; ch < (NBV + 15) / 16; ++ch) {   // 8 codes = 8 tiles per 16-bit chunk
-            uint32_t z[4];
+            // nibble t of z[c] = the codes of tokens tok(2c), tok(2c+1) for coordinate 8ch + t;
+            // ze / zo carry the table offsets of the even / odd nibbles in their bytes
+            uint32_t ze[4], zo[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-              z[c] = interleave2((vb.seg[2 * c][0] >> (16 * ch)) & 0xffffu, (vb.seg[2 * c + 1][0] >> (16 * ch)) & 0xffffu);
+            for (int c = 0; c < 4; ++c) {
+              uint32_t z;
+              if constexpr (VPACK)
+                z = interleave2_packed(vb.pk[c]);
+              else
+                z = interleave2((vb.seg[2 * c][0] >> (16 * ch)) & 0xffffu, (vb.seg[2 * c + 1][0] >> (16 * ch)) & 0xffffu);
+              ze[c] = (z << 2) & 0x3c3c3c3cu;
+              zo[c] = (z >> 2) & 0x3c3c3c3cu;
+              asm("" : "+v"(ze[c]), "+v"(zo[c]));
+            }
 #pragma unroll
             for (int j = 0; j < 4 && 8 * ch + 2 * j < TV; ++j) {
               u32x4 av0, av1;
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
-                const u32x2 e = *(const u32x2*)&tv[2 * ((z[c] >> (8 * j)) & 255u)];
-                av0[c] = e[0];
-                av1[c] = e[1];
+                av0[c] = lds_word(tv, (ze[c] >> (8 * j)) & 0xffu);
+                av1[c] = lds_word(tv, (zo[c] >> (8 * j)) & 0xffu);
               }
               acc[8 * ch + 2 * j] = mfma16_f16(av0, bw, acc[8 * ch + 2 * j]);
               acc[8 * ch + 2 * j + 1] = mfma16_f16(av1, bw, acc[8 * ch + 2 * j + 1]);
@@ -562,7 +693,7 @@ attn_kernel(AttnKArgs a) {
     if (head_ok) {
       float* P = a.part + (((int64_t)sidx * a.B + b) * a.Hq + h) * (D + 2);
       if (q4 == 0) {
-        P[0] = m_run;
+        P[0] = m_run * 0.6931471805599453f;   // back to natural-log units
         P[1] = lt;
       }
       // D layout of the P.V MFMA: lane (head n16, q4) register r = coordinate group 4*q4 + r
