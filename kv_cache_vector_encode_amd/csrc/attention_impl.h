@@ -326,7 +326,7 @@ attn_kernel(AttnKArgs a) {
   const float sc = qmax * a.scale * kSU;
   const float sc2 = sqmax * a.scale * a.qjl_c * kSU;
 
-  float m_run = -INFINITY, l_run = 0.f, n_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f, n_run = 0.f, inv_n = 0.f;
   f32x4 acc[TV];
 #pragma unroll
   for (int t = 0; t < TV; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -593,38 +593,45 @@ attn_kernel(AttnKArgs a) {
         }
       }
       if constexpr (!SCORES) {
-        // ---- online softmax; weights p_t n^v_t / N with N the running max V norm
+        // ---- online softmax: weights p_t n^v_t / N against a running max m and a running max
+        //      V norm N, both shared by the 4 lanes of a head. They move only when some lane's
+        //      block exceeds them by a margin (2^8 in the weights, 16x in the norms): until then
+        //      the weights stay below 2^12 in fp16 and a block needs no cross-lane reduction
+        //      and no rescale.
         float mb = s[0], nb = vn[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) {
           mb = fmaxf(mb, s[e]);
           nb = fmaxf(nb, vn[e]);
         }
-        mb = fmaxf(mb, wave_xor(mb, 16));
-        mb = fmaxf(mb, wave_xor(mb, 32));
-        nb = fmaxf(nb, wave_xor(nb, 16));
-        nb = fmaxf(nb, wave_xor(nb, 32));
-        const float m_new = fmaxf(m_run, mb);
-        const float n_new = fmaxf(n_run, nb);
-        const float al = exp2_fast(m_run - m_new);
-        const float inv_n = n_new > 0.f ? 1.0f / n_new : 0.f;
-        const float a_acc = al * n_run * inv_n;
+        if (__any(mb > m_run + 8.0f || nb > 16.0f * n_run)) {
+          mb = fmaxf(mb, wave_xor(mb, 16));
+          mb = fmaxf(mb, wave_xor(mb, 32));
+          nb = fmaxf(nb, wave_xor(nb, 16));
+          nb = fmaxf(nb, wave_xor(nb, 32));
+          const float m_new = fmaxf(m_run, mb);
+          const float n_new = fmaxf(n_run, nb);
+          const float al = exp2_fast(m_run - m_new);
+          const float inv_new = n_new > 0.f ? 1.0f / n_new : 0.f;
+          const float a_acc = al * n_run * inv_new;
+          l_run *= al;
+          m_run = m_new;
+          n_run = n_new;
+          inv_n = inv_new;
+          if (__any(a_acc != 1.0f)) {
+#pragma unroll
+            for (int t = 0; t < TV; ++t) acc[t] = acc[t] * a_acc;
+          }
+        }
         float lsum = 0.f;
         u32x4 bw;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float e0 = exp2_fast(s[2 * c] - m_new), e1 = exp2_fast(s[2 * c + 1] - m_new);
+          const float e0 = exp2_fast(s[2 * c] - m_run), e1 = exp2_fast(s[2 * c + 1] - m_run);
           lsum += e0 + e1;
           bw[c] = pack_f16x2(e0 * vn[2 * c] * inv_n, e1 * vn[2 * c + 1] * inv_n);
         }
-        l_run = l_run * al + lsum;
-        m_run = m_new;
-        n_run = n_new;
-        // the running maxima settle after a few blocks: skip the rescale once no lane needs it
-        if (__any(a_acc != 1.0f)) {
-#pragma unroll
-          for (int t = 0; t < TV; ++t) acc[t] = acc[t] * a_acc;
-        }
+        l_run += lsum;
 
         // ---- P.V: lane (coordinate group m = n16, token group g = q4), same 8 tokens; tile t
         //      is coordinate m*d/16 + t, component c the tokens tok(2c), tok(2c+1)
