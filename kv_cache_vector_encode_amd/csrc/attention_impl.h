@@ -228,26 +228,6 @@ attn_kernel(AttnKArgs a) {
   constexpr int NQB = K1 ? KB1 : KB;    // query operand words per pass and lane
   __shared__ u32x4 sq[2 * NQB * 64];   // query B operands [hi, lo][kb][lane], shared by the waves
   __shared__ u32x4 ssq[QJL ? 2 * KB * 64 : 1];   // the same for S q (QJL keys)
-  {
-    // centroids straight from the kernel-argument segment (`a` is the only argument)
-    const char* ka = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
-    const uint32_t* kk = (const uint32_t*)(ka + offsetof(AttnKArgs, ctk));
-    const uint32_t* kv = (const uint32_t*)(ka + offsetof(AttnKArgs, ctv));
-    constexpr uint32_t MK = (1u << BK) - 1u, MV = (1u << BV) - 1u;
-    for (int j = threadIdx.x; j < KTAB; j += blockDim.x) {
-      if constexpr (K1) {
-        tkh[j] = kk[j];
-      } else {
-        const uint32_t c0 = kk[j & MK], c1 = kk[j >> BK];
-        tkh[j] = (c0 & 0xffffu) | (c1 << 16);
-        tkl[j] = (c0 >> 16) | (c1 & 0xffff0000u);
-      }
-    }
-    if constexpr (!SCORES) {
-      auto cv = [&](uint32_t k) -> uint32_t { return (kv[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
-      for (int j = threadIdx.x; j < VTAB; j += blockDim.x) tv[j] = cv(j & MV) | (cv((uint32_t)j >> BV) << 16);
-    }
-  }
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.z, kvh = blockIdx.y;
@@ -316,15 +296,7 @@ attn_kernel(AttnKArgs a) {
     }
     return qm;
   };
-  const float qmax = query_operands(a.qrot, sq, std::integral_constant<bool, K1>{});
-  float sqmax = 0.f;
-  if constexpr (QJL) sqmax = query_operands(a.qsk, ssq, std::false_type{});
-  __syncthreads();
-  // the softmax runs in base 2 (v_exp_f32 is 2^x): fused-attention scores are kept in units of
-  // log2(e) and the running max is converted back when the partial is written
-  constexpr float kSU = SCORES ? 1.0f : 1.4426950408889634f;
-  const float sc = qmax * a.scale * kSU;
-  const float sc2 = sqmax * a.scale * a.qjl_c * kSU;
+  float sc = 0.f, sc2 = 0.f;   // score scales, set once the query operands are built
 
   float m_run = -INFINITY, l_run = 0.f, n_run = 0.f, inv_n = 0.f;
   f32x4 acc[TV];
@@ -450,18 +422,66 @@ attn_kernel(AttnKArgs a) {
   __shared__ f32x4 nstage[kAttnWaves][QJL ? 24 : 16];
   float* const nst = (float*)&nstage[wave][0];
 
+  // The first block's loads go out before the query operands are built, so that their latency
+  // and that of the query loads overlap.
+  KBlk kA, kB;
+  VBlk vA, vB;
+  float nA[NR], nB[NR];
+  int q0 = 0, q1 = 0;   // pages of the next block to fetch
+  if (start < end) {
+    pages(start, q0, q1);
+    fetch_norms(start, q0, q1, nA);
+    fetch_k(start, q0, q1, kA);
+    fetch_v(start, q0, q1, vA);
+    pages(start + 32, q0, q1);
+  }
+  // code -> operand tables and query operands, shared by the workgroup's waves
+  {
+    {
+      // centroids straight from the kernel-argument segment (`a` is the only argument)
+      const char* ka = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+      const uint32_t* kk = (const uint32_t*)(ka + offsetof(AttnKArgs, ctk));
+      const uint32_t* kv = (const uint32_t*)(ka + offsetof(AttnKArgs, ctv));
+      constexpr uint32_t MK = (1u << BK) - 1u, MV = (1u << BV) - 1u;
+      for (int j = threadIdx.x; j < KTAB; j += blockDim.x) {
+        if constexpr (K1) {
+          tkh[j] = kk[j];
+        } else {
+          const uint32_t c0 = kk[j & MK], c1 = kk[j >> BK];
+          tkh[j] = (c0 & 0xffffu) | (c1 << 16);
+          tkl[j] = (c0 >> 16) | (c1 & 0xffff0000u);
+        }
+      }
+      if constexpr (!SCORES) {
+        auto cv = [&](uint32_t k) -> uint32_t { return (kv[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
+        for (int j = threadIdx.x; j < VTAB; j += blockDim.x) tv[j] = cv(j & MV) | (cv((uint32_t)j >> BV) << 16);
+      }
+    }
+    const float qmax = query_operands(a.qrot, sq, std::integral_constant<bool, K1>{});
+    float sqmax = 0.f;
+    if constexpr (QJL) sqmax = query_operands(a.qsk, ssq, std::false_type{});
+    __syncthreads();
+    // the softmax runs in base 2 (v_exp_f32 is 2^x): fused-attention scores are kept in units
+    // of log2(e) and the running max is converted back when the partial is written
+    constexpr float kSU = SCORES ? 1.0f : 1.4426950408889634f;
+    sc = qmax * a.scale * kSU;
+    sc2 = sqmax * a.scale * a.qjl_c * kSU;
+  }
+
   // Double-buffered walk: at the top of a block every load of the next block (norms, key codes,
   // value codes) is issued into the other buffer set, so each load has a whole block of work to
   // arrive before its first use. The two sets alternate by unrolling the walk by two; copying a
   // prefetch buffer instead would make the wave wait for every load in flight.
   if (start < end) {
     uint32_t qoff = (uint32_t)lane * 16u;
-    int q0, q1;   // pages of the next block to fetch
     auto block = [&](int t0, const KBlk& cur, const VBlk& vb, const float (&nr)[NR], KBlk& kN, VBlk& vN,
                      float (&nN)[NR]) {
-      fetch_norms(t0 + 32, q0, q1, nN);
-      fetch_k(t0 + 32, q0, q1, kN);
-      fetch_v(t0 + 32, q0, q1, vN);
+      // past the wave's range a dense fetch would read the next wave's rows: the last block
+      // fetches itself again instead (cache hits); paged fetches clamp their rows already
+      const int nx = (PAGE != kDense || t0 + 32 < end) ? t0 + 32 : t0;
+      fetch_norms(nx, q0, q1, nN);
+      fetch_k(nx, q0, q1, kN);
+      fetch_v(nx, q0, q1, vN);
       pages(t0 + 64, q0, q1);
       // this block's norms through LDS into the lane's 8 tokens
       float kn[8], vn[SCORES ? 1 : 8], rn[QJL ? 8 : 1];
@@ -676,14 +696,6 @@ attn_kernel(AttnKArgs a) {
         }
       }
     };
-    KBlk kA, kB;
-    VBlk vA, vB;
-    float nA[NR], nB[NR];
-    pages(start, q0, q1);
-    fetch_norms(start, q0, q1, nA);
-    fetch_k(start, q0, q1, kA);
-    fetch_v(start, q0, q1, vA);
-    pages(start + 32, q0, q1);
     wait_vmem_all();
     for (int t0 = start;;) {
       block(t0, kA, vA, nA, kB, vB, nB);
@@ -998,6 +1010,12 @@ __global__ void __launch_bounds__(D * kParts) merge_kernel(const float* part, in
   const int64_t sstride = (int64_t)B * Hq * (D + 2);
   const float* P0 = part + ((int64_t)b * Hq + h0) * (D + 2);   // split s, head h: + s*sstride + h*(D+2)
   const int ns = s_eff + has_window;
+  // this thread's rows of Pi_V for the final product, loaded first so that their latency
+  // overlaps the reads of the partials: pvr[j] = Pi[pt*JP + j][k]
+  const float* Pv = piv + (bpr ? b / bpr : 0) * rot_stride + (int64_t)pt * JP * D + k;
+  float pvr[JP];
+#pragma unroll
+  for (int j = 0; j < JP; ++j) pvr[j] = Pv[(int64_t)j * D];
 
   // M_h = max over splits (and the window) of m_s
 #pragma unroll
@@ -1064,15 +1082,13 @@ __global__ void __launch_bounds__(D * kParts) merge_kernel(const float* part, in
   __syncthreads();
 
   // o = Pi_V^T orot, this part's rows
-  const float* Pv = piv + (bpr ? b / bpr : 0) * rot_stride + (int64_t)pt * JP * D + k;   // Pv[j*D] = Pi[pt*JP + j][k]
   float o[HB];
 #pragma unroll
   for (int h = 0; h < HB; ++h) o[h] = 0.f;
-#pragma unroll 16
-  for (int j = 0; j < JP; ++j) {
-    const float pv = Pv[(int64_t)j * D];
 #pragma unroll
-    for (int h = 0; h < HB; ++h) o[h] = fmaf(pv, orot[h][pt * JP + j], o[h]);
+  for (int j = 0; j < JP; ++j) {
+#pragma unroll
+    for (int h = 0; h < HB; ++h) o[h] = fmaf(pvr[j], orot[h][pt * JP + j], o[h]);
   }
 #pragma unroll
   for (int h = 0; h < HB; ++h) red[pt][h][k] = o[h];
