@@ -210,18 +210,20 @@ attn_kernel(AttnKArgs a) {
   constexpr int ROWK = D * BK / 8, ROWV = D * BV / 8;
   constexpr int PK = 2 * BK;            // bits of a pair of K codes
   // Code -> operand tables in LDS. A table of at most 16 words is read without bank conflicts
-  // (lanes that pick the same entry share one read); random picks from a 256-entry table cost
-  // several times that. So:
-  //   4-bit keys (K1): one lookup per code, word = the centroid's bf16 hi | lo << 16, and the
-  //     score MFMA's K dimension runs over (coordinate, hi / lo) with the query duplicated,
-  //     so one product takes (c_hi + c_lo) q_hi and a second one (c_hi + c_lo) q_lo;
+  // (lanes that pick the same entry share one read); random picks from a larger table cost
+  // more LDS cycles, but a byte index is one instruction (a byte select with the shift), a
+  // nibble index two. So:
+  //   4-bit keys (K1): a byte of codes (two coordinates) -> two words, each the centroid's
+  //     bf16 hi | lo << 16, and the score MFMA's K dimension runs over (coordinate, hi / lo)
+  //     with the query duplicated, so one product takes (c_hi + c_lo) q_hi and a second one
+  //     (c_hi + c_lo) q_lo;
   //   2/3-bit keys: a pair of codes (at most 64 entries) -> two bf16 hi (tkh) / lo (tkl)
   //     halves, three products per K block (c_hi q_hi + c_lo q_hi + c_hi q_lo);
   //   values: a pair of V codes (one coordinate of two tokens) -> one fp16 pair; 2-bit codes
-  //     are first interleaved so that each nibble is such a pair.
+  //     are first interleaved so that each nibble is such a pair (16 entries).
   constexpr bool K1 = BK == 4;
   constexpr int KB1 = D / 16;           // score MFMAs per pass with one code per operand word
-  constexpr int KTAB = K1 ? 16 : 1 << PK;
+  constexpr int KTAB = K1 ? 512 : 1 << PK;
   constexpr int VTAB = 1 << (2 * BV);
   __shared__ uint32_t tkh[KTAB], tkl[K1 ? 1 : KTAB];
   __shared__ uint32_t tv[SCORES ? 1 : VTAB];
@@ -445,7 +447,7 @@ attn_kernel(AttnKArgs a) {
       constexpr uint32_t MK = (1u << BK) - 1u, MV = (1u << BV) - 1u;
       for (int j = threadIdx.x; j < KTAB; j += blockDim.x) {
         if constexpr (K1) {
-          tkh[j] = kk[j];
+          tkh[j] = kk[(j & 1) ? ((j >> 5) & 15) : ((j >> 1) & 15)];   // entry j/2: low code, high code
         } else {
           const uint32_t c0 = kk[j & MK], c1 = kk[j >> BK];
           tkh[j] = (c0 & 0xffffu) | (c1 << 16);
@@ -520,34 +522,20 @@ attn_kernel(AttnKArgs a) {
       float s[8];
       f32x4 St[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       if constexpr (K1) {
-        // code p of the lane's chunk sits in nibble p % 8 of word p / 8: the table offsets of the
-        // even nibbles are the bytes of (w << 2) & 0x3c3c3c3c, those of the odd ones the bytes
-        // of (w >> 2) & 0x3c3c3c3c, one byte extract per lookup (the empty asm keeps the
-        // compiler from folding the masks back into a shift and a mask per lookup)
+        // codes 4kb .. 4kb+3 of the lane's chunk are bytes 2(kb%2), 2(kb%2)+1 of word kb/2
 #pragma unroll
-        for (int kw = 0; kw < KB1 / 2; ++kw) {
-          uint32_t we[2], wo[2];
+        for (int kb = 0; kb < KB1; ++kb) {
+          const u32x4 qh = *(const u32x4*)(qbase + kb * 1024);
+          const u32x4 ql = *(const u32x4*)(qbase + (KB1 + kb) * 1024);
+          const int sh = 16 * (kb & 1);
 #pragma unroll
           for (int tile = 0; tile < 2; ++tile) {
-            we[tile] = (cur.kc[tile][kw] << 2) & 0x3c3c3c3cu;
-            wo[tile] = (cur.kc[tile][kw] >> 2) & 0x3c3c3c3cu;
-            asm("" : "+v"(we[tile]), "+v"(wo[tile]));
-          }
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int kb = 2 * kw + half, sh = 16 * half;
-            const u32x4 qh = *(const u32x4*)(qbase + kb * 1024);
-            const u32x4 ql = *(const u32x4*)(qbase + (KB1 + kb) * 1024);
-#pragma unroll
-            for (int tile = 0; tile < 2; ++tile) {
-              u32x4 ak;
-              ak[0] = lds_word(tkh, (we[tile] >> sh) & 0xffu);
-              ak[1] = lds_word(tkh, (wo[tile] >> sh) & 0xffu);
-              ak[2] = lds_word(tkh, (we[tile] >> (sh + 8)) & 0xffu);
-              ak[3] = lds_word(tkh, (wo[tile] >> (sh + 8)) & 0xffu);
-              St[tile] = mfma16_bf16(ak, qh, St[tile]);
-              St[tile] = mfma16_bf16(ak, ql, St[tile]);
-            }
+            const uint32_t w = cur.kc[tile][kb >> 1];
+            const u32x2 p0 = *(const u32x2*)((const char*)tkh + 8u * ((w >> sh) & 0xffu));
+            const u32x2 p1 = *(const u32x2*)((const char*)tkh + 8u * ((w >> (sh + 8)) & 0xffu));
+            const u32x4 ak = {p0[0], p0[1], p1[0], p1[1]};
+            St[tile] = mfma16_bf16(ak, qh, St[tile]);
+            St[tile] = mfma16_bf16(ak, ql, St[tile]);
           }
         }
       }
