@@ -53,6 +53,7 @@ struct AttnKArgs {
   int32_t max_seq_len, block_size, bs_shift, mbps;
   int32_t B, Hq, Hkv, G, s_eff;
   int32_t window;     // newest tokens held in the full-precision window (0: none)
+  int32_t one_round;  // 1 when every wave of the grid is resident at once (progress priorities)
   float scale;
   uint32_t ctk[16];   // K centroids as bf16 hi | lo << 16
   uint32_t ctv[8];    // V centroids as fp16, two per word
@@ -685,12 +686,30 @@ attn_kernel(AttnKArgs a) {
       }
     };
     wait_vmem_all();
+    // Waves sharing a SIMD otherwise progress at very different speeds (the oldest wave is
+    // issued first), and the SIMD runs its last blocks with fewer and fewer waves. When the
+    // whole grid is resident, a wave lowers its issue priority as it passes half and then three
+    // quarters of its range, so the others catch up and all finish close together.
+    const bool prio = !SCORES && a.one_round;
+    const int t_half = start + (end - start) / 2, t_3q = start + 3 * (end - start) / 4;
+    int lvl = 0;   // 0: priority 3, 1: past half (priority 1), 2: past three quarters (0)
+    if (prio) __builtin_amdgcn_s_setprio(3);
     for (int t0 = start;;) {
+      if (prio) {
+        if (lvl < 2 && t0 >= t_3q) {
+          lvl = 2;
+          __builtin_amdgcn_s_setprio(0);
+        } else if (lvl < 1 && t0 >= t_half) {
+          lvl = 1;
+          __builtin_amdgcn_s_setprio(1);
+        }
+      }
       block(t0, kA, vA, nA, kB, vB, nB);
       if ((t0 += 32) >= end) break;
       block(t0, kB, vB, nB, kA, vA, nA);
       if ((t0 += 32) >= end) break;
     }
+    if (prio) __builtin_amdgcn_s_setprio(0);
   }
 
   if constexpr (!SCORES) {
@@ -1154,6 +1173,11 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   a.G = Hq / p->num_kv_heads;
   a.s_eff = lay.splits * kAttnWaves;
   a.window = p->window;
+  {
+    const int64_t waves = (int64_t)lay.splits * kAttnWaves * p->num_kv_heads * B;
+    const int64_t resident = (int64_t)attn_wpe(D, BK, BV, QJL, PAGE != kDense) * 4 * device_cu_count(rk.device);
+    a.one_round = waves <= resident ? 1 : 0;
+  }
   a.scale = p->scale;
   LevelArgs lk = make_levels(ck), lv = make_levels(cv);
   for (int j = 0; j < 16; ++j) a.ctk[j] = lk.centroid_bf16x2[j];
