@@ -15,7 +15,7 @@
 // KV head, token range) and walks it 32 tokens at a time.
 //   scores: 16x16x32 bf16 MFMA in three hi/lo passes, A = centroids of 16 tokens (lane m+16g
 //     holds token m's codes for coordinates g*d/4 + 8kb .. +8), B = the G <= 16 rotated
-//     queries of the group (normalized by their max |entry|), D[token][head].
+//     queries of the group (times the score scale), D[token][head].
 //   QJL keys (TurboQuantCompressorV2.asymmetric_attention_scores on the same page) add
 //     ||r_t|| sqrt(pi/2)/d <S q, signs_t>: a second product with A = the token's signs as
 //     bf16 +-1 (exact; same lane layout as the codes) and B = S q split into bf16 hi + lo.
@@ -248,27 +248,21 @@ attn_kernel(AttnKArgs a) {
   const int h = kvh * a.G + (head_ok ? n16 : 0);
 
   // ---- rotated query as the score MFMA's B operand: lane (head n16, g = q4) holds
-  //      q'[h][q4*d/4 + 8kb + e] / qmax for kb < KB, e < 8, split into bf16 hi + lo. Scores
+  //      f q'[h][q4*d/4 + 8kb + e] for kb < KB, e < 8, split into bf16 hi + lo, where f is the
+  //      score scale (bf16 has fp32's exponent range, so the scale can ride on the operand
+  //      and the products come out as scores up to the key's norm). Scores
   //      take three bf16 passes (q_hi c_hi + q_hi c_lo + q_lo c_hi, ~2^-17 relative): with
   //      large logits (outlier tokens) softmax turns score errors into weight errors, so fp16
   //      (2^-11) operands are not enough there. All waves of the workgroup serve the same
   //      (sequence, KV head); wave 0 leaves the operands in LDS and the loop reads them there.
   //      With 4-bit keys (K1) the operand word c of K block kb holds coordinate
   //      q4*d/4 + 4kb + c twice (the code side supplies hi and lo of that coordinate).
-  auto query_operands = [&](const float* src, u32x4* dst, auto dup) -> float {
+  auto query_operands = [&](const float* src, u32x4* dst, float inv, auto dup) {
     constexpr bool DUP = decltype(dup)::value;
     float qv[D / 4];
     const float* qp = src + ((int64_t)b * a.Hq + h) * D + q4 * (D / 4);
-    float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      qv[i] = head_ok ? qp[i] : 0.f;
-      mx = fmaxf(mx, fabsf(qv[i]));
-    }
-    mx = fmaxf(mx, wave_xor(mx, 16));
-    mx = fmaxf(mx, wave_xor(mx, 32));
-    const float qm = mx > 0.f ? mx : 1.f;
-    const float inv = 1.0f / qm;
+    for (int i = 0; i < D / 4; ++i) qv[i] = head_ok ? qp[i] : 0.f;
     if constexpr (DUP) {
 #pragma unroll
       for (int kb = 0; kb < KB1; ++kb)
@@ -297,11 +291,8 @@ attn_kernel(AttnKArgs a) {
           }
         }
     }
-    return qm;
   };
-  float sc = 0.f, sc2 = 0.f;   // score scales, set once the query operands are built
-
-  float m_run = -INFINITY, l_run = 0.f, n_run = 0.f, inv_n = 0.f;
+  float m_run = -INFINITY, l_run = 0.f, n_run = 0.f, n_eff = 1.0f, m_eff = -INFINITY;
   f32x4 acc[TV];
 #pragma unroll
   for (int t = 0; t < TV; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -460,15 +451,12 @@ attn_kernel(AttnKArgs a) {
         for (int j = threadIdx.x; j < VTAB; j += blockDim.x) tv[j] = cv(j & MV) | (cv((uint32_t)j >> BV) << 16);
       }
     }
-    const float qmax = query_operands(a.qrot, sq, std::integral_constant<bool, K1>{});
-    float sqmax = 0.f;
-    if constexpr (QJL) sqmax = query_operands(a.qsk, ssq, std::false_type{});
-    __syncthreads();
     // the softmax runs in base 2 (v_exp_f32 is 2^x): fused-attention scores are kept in units
     // of log2(e) and the running max is converted back when the partial is written
     constexpr float kSU = SCORES ? 1.0f : 1.4426950408889634f;
-    sc = qmax * a.scale * kSU;
-    sc2 = sqmax * a.scale * a.qjl_c * kSU;
+    query_operands(a.qrot, sq, a.scale * kSU, std::integral_constant<bool, K1>{});
+    if constexpr (QJL) query_operands(a.qsk, ssq, a.scale * a.qjl_c * kSU, std::false_type{});
+    __syncthreads();
   }
 
   // Double-buffered walk: at the top of a block every load of the next block (norms, key codes,
@@ -581,8 +569,8 @@ attn_kernel(AttnKArgs a) {
         // D layout: lane (head n16, q4) register r = token t0 + 16*tile + 4*q4 + r = tok(4*tile + r)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = S[r] * sc * kn[4 * tile + r];   // sc is per head (the query's normalization)
-          if constexpr (QJL) v = fmaf(S2[r] * sc2, rn[4 * tile + r], v);
+          float v = S[r] * kn[4 * tile + r];
+          if constexpr (QJL) v = fmaf(S2[r], rn[4 * tile + r], v);
           if constexpr (SCORES) {
             const int tt = t0 + 16 * tile + 4 * q4 + r;
             const bool ok = tt < end;
@@ -603,10 +591,11 @@ attn_kernel(AttnKArgs a) {
       }
       if constexpr (!SCORES) {
         // ---- online softmax: weights p_t n^v_t / N against a running max m and a running max
-        //      V norm N, both shared by the 4 lanes of a head. They move only when some lane's
-        //      block exceeds them by a margin (2^8 in the weights, 16x in the norms): until then
-        //      the weights stay below 2^12 in fp16 and a block needs no cross-lane reduction
-        //      and no rescale.
+        //      V norm N (taken as 1 while it is 0 or subnormal), both shared by the 4 lanes of a head. They
+        //      move only when some lane's block exceeds them by a margin (2^8 in the weights, 16x
+        //      in the norms): until then the weights stay below 2^12 in fp16 and a block needs no
+        //      cross-lane reduction and no rescale. 1/N rides in the exponent: p_t / N =
+        //      2^(s_t - m_e) with m_e = m + log2 N, and l gains N * sum 2^(s_t - m_e).
         float mb = s[0], nb = vn[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) {
@@ -620,13 +609,14 @@ attn_kernel(AttnKArgs a) {
           nb = fmaxf(nb, wave_xor(nb, 32));
           const float m_new = fmaxf(m_run, mb);
           const float n_new = fmaxf(n_run, nb);
+          const float ne_new = n_new >= 1.17549435e-38f ? n_new : 1.0f;   // 0 (or subnormal): 1
           const float al = exp2_fast(m_run - m_new);
-          const float inv_new = n_new > 0.f ? 1.0f / n_new : 0.f;
-          const float a_acc = al * n_run * inv_new;
+          const float a_acc = al * n_eff / ne_new;
           l_run *= al;
           m_run = m_new;
           n_run = n_new;
-          inv_n = inv_new;
+          n_eff = ne_new;
+          m_eff = m_new + __builtin_amdgcn_logf(ne_new);   // v_log_f32 is log2
           if (__any(a_acc != 1.0f)) {
 #pragma unroll
             for (int t = 0; t < TV; ++t) acc[t] = acc[t] * a_acc;
@@ -636,11 +626,11 @@ attn_kernel(AttnKArgs a) {
         u32x4 bw;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float e0 = exp2_fast(s[2 * c] - m_run), e1 = exp2_fast(s[2 * c + 1] - m_run);
+          const float e0 = exp2_fast(s[2 * c] - m_eff), e1 = exp2_fast(s[2 * c + 1] - m_eff);
           lsum += e0 + e1;
-          bw[c] = pack_f16x2(e0 * vn[2 * c] * inv_n, e1 * vn[2 * c + 1] * inv_n);
+          bw[c] = pack_f16x2(e0 * vn[2 * c], e1 * vn[2 * c + 1]);
         }
-        l_run += lsum;
+        l_run = fmaf(lsum, n_eff, l_run);
 
         // ---- P.V: lane (coordinate group m = n16, token group g = q4), same 8 tokens; tile t
         //      is coordinate m*d/16 + t, component c the tokens tok(2c), tok(2c+1)
@@ -726,7 +716,7 @@ attn_kernel(AttnKArgs a) {
 #pragma unroll
       for (int t = 0; t < TV; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) P[2 + (4 * q4 + r) * (D / 16) + t] = acc[t][r] * n_run;
+        for (int r = 0; r < 4; ++r) P[2 + (4 * q4 + r) * (D / 16) + t] = acc[t][r] * n_eff;
     }
   }
 }
