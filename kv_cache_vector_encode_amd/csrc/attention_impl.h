@@ -464,7 +464,9 @@ attn_kernel(AttnKArgs a) {
   // arrive before its first use. The two sets alternate by unrolling the walk by two; copying a
   // prefetch buffer instead would make the wave wait for every load in flight.
   if (start < end) {
-    uint32_t qoff = (uint32_t)lane * 16u;
+    // lanes of heads past the group's G read lane 63's operand, which is zero when G < 16:
+    // the reads of those lanes then share one address, which costs LDS almost nothing
+    uint32_t qoff = (uint32_t)(head_ok ? lane : 63) * 16u;
     auto block = [&](int t0, const KBlk& cur, const VBlk& vb, const float (&nr)[NR], KBlk& kN, VBlk& vN,
                      float (&nN)[NR]) {
       // past the wave's range a dense fetch would read the next wave's rows: the last block
