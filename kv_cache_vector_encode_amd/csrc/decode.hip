@@ -229,7 +229,7 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
       } else {
         uint8_t* dst = vec < v_end ? (uint8_t*)a.out + (vec * D + hh * HALF + 16 * t) * E : a.sink + 64 * lane;
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) *(u32x4*)(dst + 16 * k) = ch[k];
+        for (int k = 0; k < CPT; ++k) __builtin_nontemporal_store(ch[k], (u32x4*)(dst + 16 * k));
       }
     }
     if constexpr (Geo::STAGE) {
@@ -243,7 +243,9 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
         const uint32_t rowi = off / RB, c = (off % RB) / 16;
         const u32x4 q = *(const u32x4*)(stg + 16 * (rowi * RC + (c ^ (rowi & SW))));
         uint8_t* dst = vbase + rowi < v_end ? tbase + off : a.sink + 16 * lane;
-        *(u32x4*)dst = q;
+        // non-temporal: the decoded stream is far larger than the caches, and left in them as
+        // dirty lines it is written back during whatever kernel runs next
+        __builtin_nontemporal_store(q, (u32x4*)dst);
       }
     }
   }
