@@ -276,3 +276,62 @@ def test_paged_ragged_workload(dev, d):
     ls = lay_slots.cpu().numpy()
     check_decode(dec, kp_h[ls], kn_h[ls], c["pk"], d, bk, "paged K gather decode d%d" % d)
     _check_paged(c, d, bk, bv, o.cpu().numpy().astype(np.float64), None, seqs, "paged ragged d%d" % d)
+
+
+def test_attention_softmax_margins(dev):
+    # The fused kernel moves its running max and running value-norm max only past a margin and
+    # folds 1/N into the exponent; these caches drive both paths hard: logits that keep growing
+    # along the sequence, isolated large-logit spikes, value norms that grow 1.02x per token (many
+    # 16x steps), leading blocks of zero value norms (N taken as 1), subnormal value norms, and a
+    # head whose values are all zero. Codes are random bytes; norms and queries are seeded.
+    d, bk, bv, B, Hq, Hkv, T = 128, 4, 2, 3, 8, 2, 700
+    log("case: attention softmax margins")
+    kp = ti.random_bytes((B, Hkv, T, d * bk // 8), 31, dev)
+    vp = ti.random_bytes((B, Hkv, T, d * bv // 8), 32, dev)
+    t = np.arange(T, dtype=np.float64)
+    kn = np.ones((B, Hkv, T), np.float32)
+    vn = np.ones((B, Hkv, T), np.float32)
+    kn[0] = (1.0 + 0.05 * t).astype(np.float32)
+    kn[1, :, ::50] = 40.0
+    kn[2] = ti.random_norms((Hkv, T), 34).numpy()
+    vn[0] = (1.02 ** t).astype(np.float32)
+    vn[1, :, :64] = 0.0
+    vn[2, 0, :32] = np.float32(1e-39)
+    vn[2, 1, :] = 0.0
+    q = ti.normal((B, Hq, d), 33, scale=4.0, dtype=torch.bfloat16, device=dev)
+    rk, pk = rotation_pair(d, [42])
+    rv, pv = rotation_pair(d, [542])
+    ck, cv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    o, lse = tq.attn_decode(ck, rk, cv, rv, q, kp, upload(kn, dev), vp, upload(vn, dev), out_dtype=torch.float32,
+                            return_lse=True)
+    torch.cuda.synchronize()
+    khat = oatt.decode_cache(kp.cpu().numpy(), kn, pk[0], ocb.codebook(d, bk).centroids, bk, d)
+    vhat = oatt.decode_cache(vp.cpu().numpy(), vn, pv[0], ocb.codebook(d, bv).centroids, bv, d)
+    s_ref = oatt.scores(to64(q), khat, 1 / math.sqrt(d))
+    log("softmax margins: score range %.1f .. %.1f" % (float(s_ref.min()), float(s_ref.max())))
+    o64 = o.cpu().numpy().astype(np.float64)
+    assert np.all(o64[2, 4:] == 0.0)          # query heads of the all-zero value head
+    check_attention(o64, lse.cpu().numpy(), to64(q), khat, vhat, 1 / math.sqrt(d), [T] * B, "softmax margins")
+
+
+@pytest.mark.parametrize("splits", [0, 16])
+def test_attention_one_round_and_more(dev, splits):
+    # splits 0: the grid is one round of resident waves (issue priorities by progress);
+    # 16 splits over 128 (sequence, KV head) pairs: more waves than fit at once (no priorities)
+    d, bk, bv, B, Hq, Hkv, T = 128, 4, 2, 16, 32, 8, 512
+    log("case: attention %s" % ("one round" if splits == 0 else "%d splits" % splits))
+    kp = ti.random_bytes((B, Hkv, T, d * bk // 8), 41, dev)
+    vp = ti.random_bytes((B, Hkv, T, d * bv // 8), 42, dev)
+    kn = ti.random_norms((B, Hkv, T), 43, median=2.0, device=dev)
+    vn = ti.random_norms((B, Hkv, T), 44, device=dev)
+    q = ti.normal((B, Hq, d), 45, dtype=torch.bfloat16, device=dev)
+    rk, pk = rotation_pair(d, [42])
+    rv, pv = rotation_pair(d, [542])
+    ck, cv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    lens = torch.tensor([(T * (i + 3)) // 19 for i in range(B)], dtype=torch.int32, device=dev)
+    o = tq.attn_decode(ck, rk, cv, rv, q, kp, kn, vp, vn, seq_lens=lens, out_dtype=torch.float32, num_splits=splits)
+    torch.cuda.synchronize()
+    khat = oatt.decode_cache(kp.cpu().numpy(), kn.cpu().numpy(), pk[0], ocb.codebook(d, bk).centroids, bk, d)
+    vhat = oatt.decode_cache(vp.cpu().numpy(), vn.cpu().numpy(), pv[0], ocb.codebook(d, bv).centroids, bv, d)
+    check_attention(o.cpu().numpy().astype(np.float64), None, to64(q), khat, vhat, 1 / math.sqrt(d),
+                    lens.cpu().numpy(), "splits %d" % splits)
