@@ -252,9 +252,10 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
 
-    long = None
+    long = attn32k = None
     if not args.no_long:
         long = long_context_layer(tq, ti, torch, dev)
+        attn32k = decode_attention_32k(tq, ti, torch, dev)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -270,6 +271,7 @@ def main():
         "kernels_note": "per-call ms from an untimed calibration pass (3 steps, every call bracketed by events)",
         **extra,
         "long_context_layer": long,
+        "decode_attention_32k": attn32k,
         "next_rows": nxt,
         "source_hash": src_hash,
     }
@@ -371,6 +373,33 @@ def next_rows(tq, ti, torch, dev, K, V, kp, kn, vp, vn, rot, ck, cv, q, kp4, kn4
                                                batch_per_rot=1, workspace=wsa), reps=reps)
     out["window_append_1_token"] = {"batch": L, "kv_heads": H, "us": round(ms * 1e3, 2)}
     return out
+
+
+def decode_attention_32k(tq, ti, torch, dev, reps: int = 10):
+    """Fused decode attention over a long context: batch 32, 32 query heads over 8 KV heads, 32768
+    tokens, d=128, K4/V2 (random code bytes with log-normal norms, as in the parity test of this
+    size). The 832 MiB cache exceeds the last-level cache, so every call streams it from HBM."""
+    shape = ti.AttnShape()
+    B, Hq, Hkv, T, d = shape.batch, shape.q_heads, shape.kv_heads, shape.tokens, shape.head_dim
+    rk = tq.Rotation.from_gaussian(ti.rotation_gaussian(d, 42))
+    rv = tq.Rotation.from_gaussian(ti.rotation_gaussian(d, 542))
+    ck, cv = tq.Codebook(d, 4), tq.Codebook(d, 2)
+    kp = ti.random_bytes((B, Hkv, T, d * 4 // 8), 31, device=dev)
+    vp = ti.random_bytes((B, Hkv, T, d * 2 // 8), 32, device=dev)
+    kn = ti.random_norms((B, Hkv, T), 33, device=dev)
+    vn = ti.random_norms((B, Hkv, T), 34, median=11.0, device=dev)
+    q = ti.normal((B, Hq, d), 11, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    tq.attn_decode(ck, rk, cv, rv, q, kp, kn, vp, vn, out=out)
+    ws = out._tq_workspace
+    ms = _time(torch, lambda: tq.attn_decode(ck, rk, cv, rv, q, kp, kn, vp, vn, out=out, workspace=ws), reps)
+    alg = B * Hkv * T * (d * 4 // 8 + 4 + d * 2 // 8 + 4) + 2 * B * Hq * d * 2
+    res = {"ms": round(ms, 4), "context_tokens_per_s": round(B * T / (ms * 1e-3), 1),
+           "GB/s": round(alg / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "workload": "batch 32 x 32 query heads over 8 KV heads x 32768 tokens x d=128, K4/V2"}
+    del kp, vp, kn, vn
+    torch.cuda.empty_cache()
+    return res
 
 
 def long_context_layer(tq, ti, torch, dev, reps: int = 10):
