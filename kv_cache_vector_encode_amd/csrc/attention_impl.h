@@ -13,14 +13,16 @@
 //
 // Work layout. Kernel 1 rotates every query (fp32). Kernel 2: a wave owns one (sequence,
 // KV head, token range) and walks it 32 tokens at a time.
-//   scores: 16x16x32 bf16 MFMA in three hi/lo passes, A = centroids of 16 tokens (lane m+16g
-//     holds token m's codes for coordinates g*d/4 + 8kb .. +8), B = the G <= 16 rotated
-//     queries of the group (times the score scale), D[token][head].
+//   scores: 16x16x32 bf16 MFMA on hi/lo splits, A = centroids of 16 tokens (lane m+16g holds
+//     token m's codes for coordinates g*d/4 + ...), B = the G <= 16 rotated queries of the
+//     group (times the score scale), D[token][head]; three passes for 2/3-bit keys, two for
+//     4-bit keys (whose K dimension runs over (coordinate, hi / lo) against a duplicated query).
 //   QJL keys (TurboQuantCompressorV2.asymmetric_attention_scores on the same page) add
 //     ||r_t|| sqrt(pi/2)/d <S q, signs_t>: a second product with A = the token's signs as
 //     bf16 +-1 (exact; same lane layout as the codes) and B = S q split into bf16 hi + lo.
-//   softmax: per head running max m, running sum l; the value weights p_t n^v_t are kept
-//     relative to the running max V norm N so they lie in [0, 1] for fp16.
+//   softmax (base 2): per head running max m, running sum l; the value weights p_t n^v_t are
+//     kept relative to the running max V norm N so that they fit fp16; m and N move only past
+//     a margin, so most blocks need no cross-lane reduction.
 //   P.V: 16x16x32 fp16 MFMA computing acc^T[coord][head]. The 32 tokens of a block are
 //     permuted so that lane (head, g) already holds, from the score step, the weights of the
 //     8 tokens it must supply (4g..4g+3 and 16+4g..16+4g+3): no shuffles. The A operand is
