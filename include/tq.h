@@ -175,7 +175,8 @@ int tq_decode(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors
  * Cache layouts (device; K codes at cb_k's width, V codes at cb_v's width, rows as in
  * tq_encode, norms float32):
  *   dense (block_table == NULL): packed [batch, num_kv_heads, max_seq_len, row],
- *         norms [batch, num_kv_heads, max_seq_len];
+ *         norms [batch, num_kv_heads, max_seq_len]; max_seq_len * row must be < 2^32
+ *         bytes (else TQ_ERR_INVALID_ARG: use the paged layout);
  *   paged: pools packed [num_blocks, num_kv_heads, block_size, row], norms
  *         [num_blocks, num_kv_heads, block_size]; token t of sequence b is in block
  *         block_table[b * max_blocks_per_seq + t / block_size] at offset t % block_size.

@@ -875,6 +875,17 @@ static int check_attn(const tq_attn_params* p, bool scores_only, const char* who
     if ((int64_t)p->block_size * p->max_blocks_per_seq < p->max_seq_len)
       return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": block_size * max_blocks_per_seq < max_seq_len");
   }
+  if (!p->block_table) {
+    // dense caches are read through buffer resources with 32-bit byte offsets within one
+    // (sequence, KV head)'s rows
+    const int64_t d = p->rot_k->rot.d;
+    int64_t row = d * p->cb_k->cb.bits / 8;
+    if (!scores_only) row = std::max(row, d * (int64_t)p->cb_v->cb.bits / 8);
+    if ((int64_t)p->max_seq_len * row >= ((int64_t)1 << 32))
+      return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": max_seq_len = " + std::to_string(p->max_seq_len) +
+                                          " is too long for a dense cache (rows of one sequence and KV head must span"
+                                          " less than 4 GiB); use the paged layout");
+  }
   if (p->num_splits < 0) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": num_splits must be >= 0");
   if (p->window < 0) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": window must be >= 0");
   if (p->window > 0 && !scores_only) {

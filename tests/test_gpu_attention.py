@@ -335,3 +335,22 @@ def test_attention_one_round_and_more(dev, splits):
     vhat = oatt.decode_cache(vp.cpu().numpy(), vn.cpu().numpy(), pv[0], ocb.codebook(d, bv).centroids, bv, d)
     check_attention(o.cpu().numpy().astype(np.float64), None, to64(q), khat, vhat, 1 / math.sqrt(d),
                     lens.cpu().numpy(), "splits %d" % splits)
+
+
+def test_attention_dense_length_limit(dev):
+    # dense caches are addressed with 32-bit byte offsets per (sequence, KV head): a row span of
+    # 4 GiB or more is refused before any launch
+    d = 128
+    rk, _ = rotation_pair(d, [42])
+    rv, _ = rotation_pair(d, [542])
+    ck, cv = tq.Codebook(d, 4), tq.Codebook(d, 2)
+    q = torch.zeros(1, 8, d, dtype=torch.bfloat16, device=dev)
+    kp = torch.zeros(1, 2, 8, d * 4 // 8, dtype=torch.uint8, device=dev)
+    vp = torch.zeros(1, 2, 8, d * 2 // 8, dtype=torch.uint8, device=dev)
+    kn = torch.zeros(1, 2, 8, device=dev)
+    p = tq._params(ck, rk, q, kp, kn, cv, rv, vp, kn)
+    p.max_seq_len = 1 << 26                  # 64-byte key rows: exactly 4 GiB
+    with pytest.raises(tq.TQError, match="too long for a dense cache"):
+        tq.attn_workspace_size(p)
+    p.max_seq_len = (1 << 26) - 1
+    assert tq.attn_workspace_size(p) > 0
