@@ -252,14 +252,14 @@ attn_kernel(AttnKArgs a) {
   // ---- rotated query as the score MFMA's B operand: lane (head n16, g = q4) holds
   //      f q'[h][q4*d/4 + 8kb + e] for kb < KB, e < 8, split into bf16 hi + lo, where f is the
   //      score scale (bf16 has fp32's exponent range, so the scale can ride on the operand
-  //      and the products come out as scores up to the key's norm). Scores
-  //      take three bf16 passes (q_hi c_hi + q_hi c_lo + q_lo c_hi, ~2^-17 relative): with
-  //      large logits (outlier tokens) softmax turns score errors into weight errors, so fp16
-  //      (2^-11) operands are not enough there. All waves of the workgroup serve the same
+  //      and the products come out as scores up to the key's norm). 2/3-bit keys take three
+  //      bf16 passes (q_hi c_hi + q_hi c_lo + q_lo c_hi), 4-bit keys two ((c_hi + c_lo) q_hi and
+  //      (c_hi + c_lo) q_lo), both ~2^-17 relative: with large logits (outlier tokens) softmax
+  //      turns score errors into weight errors, so fp16 (2^-11) operands are not enough there. All waves of the workgroup serve the same
   //      (sequence, KV head); wave 0 leaves the operands in LDS and the loop reads them there.
   //      With 4-bit keys (K1) the operand word c of K block kb holds coordinate
   //      q4*d/4 + 4kb + c twice (the code side supplies hi and lo of that coordinate).
-  auto query_operands = [&](const float* src, u32x4* dst, float inv, auto dup) {
+  auto query_operands = [&](const float* src, u32x4* dst, float f, auto dup) {
     constexpr bool DUP = decltype(dup)::value;
     float qv[D / 4];
     const float* qp = src + ((int64_t)b * a.Hq + h) * D + q4 * (D / 4);
@@ -270,7 +270,7 @@ attn_kernel(AttnKArgs a) {
       for (int kb = 0; kb < KB1; ++kb)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float v = qv[4 * kb + c] * inv;
+          const float v = qv[4 * kb + c] * f;
           const uint32_t h = f32_to_bf16_bits(v);
           const uint32_t l = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
           if (wave == 0) {
@@ -283,7 +283,7 @@ attn_kernel(AttnKArgs a) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float v0 = qv[8 * kb + 2 * c] * inv, v1 = qv[8 * kb + 2 * c + 1] * inv;
+          const float v0 = qv[8 * kb + 2 * c] * f, v1 = qv[8 * kb + 2 * c + 1] * f;
           const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
           const uint32_t l0 = f32_to_bf16_bits(v0 - bf16_bits_to_f32(h0));
           const uint32_t l1 = f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1));
