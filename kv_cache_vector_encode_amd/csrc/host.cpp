@@ -220,34 +220,45 @@ LevelArgs make_levels(const Codebook& cb) {
     lv.centroid_bf16x2[k] = (uint32_t)hi | ((uint32_t)lo << 16);
   }
   // Quantization table: bin width just under the smallest gap between boundaries, so a bin
-  // holds at most one boundary; offset = bins per side so f >= 0 for every boundary.
+  // holds at most one boundary; offset = ceil(scale) + 1 so f = y * scale + offset >= 1 for
+  // |y| <= 1 (the entry format needs one float exponent per bin).
   double gap = INFINITY;
   for (int k = 0; k + 1 < L - 1; ++k) gap = std::min(gap, cb.thresholds[k + 1] - cb.thresholds[k]);
   if (!(gap < INFINITY)) gap = 1.0;   // one boundary (1 bit): any width works
   const double w = gap * (1.0 - 1e-3);
-  const double tmax = cb.thresholds[L - 2];
-  const int per_side = (int)std::ceil(tmax / w) + 1;
   lv.lut.scale = (float)(1.0 / w);
-  lv.lut.offset = (float)per_side;
+  const float off = std::ceil(lv.lut.scale) + 1.0f;
+  lv.lut.offset = off;
   float fthr[kMaxLevels];
-  for (int k = 0; k < L - 1; ++k) fthr[k] = (float)(cb.thresholds[k] / w + per_side);
+  for (int k = 0; k < L - 1; ++k) fthr[k] = (float)(cb.thresholds[k] / w + (double)off);
   for (int j = 0; j < kLutBins; ++j) {
-    float thr = FLT_MAX;
+    bool has = false;
+    float thr = 0.f;
     uint32_t base = 0;
     for (int k = 0; k < L - 1; ++k) {
       if (fthr[k] < (float)j) ++base;
-      else if (fthr[k] < (float)(j + 1)) thr = fthr[k];
+      else if (fthr[k] < (float)(j + 1)) {
+        thr = fthr[k];
+        has = true;
+      }
     }
-    uint32_t tb;
-    std::memcpy(&tb, &thr, 4);
-    lv.lut.entry[j] = (tb & ~15u) | base;
+    uint32_t e;
+    if (has) {
+      std::memcpy(&e, &thr, 4);
+      e = e + 1u - (1u << 24) - (base << 24);
+    } else {
+      const float lowest = j == 0 ? 0.5f : (float)j;
+      std::memcpy(&e, &lowest, 4);
+      e -= base << 24;
+    }
+    lv.lut.entry[j] = e;
   }
   return lv;
 }
 
 bool lut_covers_unit_range(const LevelArgs& lv) {
-  // |y| <= 1 must land inside the table
-  return lv.lut.scale + lv.lut.offset + 1.0f < (float)kLutBins && lv.lut.offset >= 1.0f;
+  // |y| <= 1 must land inside the table, at f >= 1
+  return lv.lut.scale + lv.lut.offset + 1.0f < (float)kLutBins && lv.lut.offset - lv.lut.scale >= 1.0f;
 }
 
 // ------------------------------------------------------------------------------------
@@ -316,12 +327,15 @@ static double orthogonality_error(int d, const double* pi) {
 }
 
 // MFMA A-operand tiles for the 32x32x16 (bf16/fp16) instructions. Tile (t, kb) of a matrix
-// M is 64 lanes x 8 elements: lane l = m + 32*hh supplies M[sigma_t(m)][hh*d/2 + 8*kb + e],
+// M is 64 lanes x 8 elements: lane l = m + 32*hh supplies M[sigma_t(m)][col(kb, hh) + e],
 // e = 0..7, where output row sigma_t(m) = hh(m)*d/2 + 16 t + i(m), hh(m) = (m/4)%2,
 // i(m) = 4*(m/8) + m%4. With that row order the 32x32 result lands so that lane
 // (vector v, half hh) holds outputs hh*d/2 + 16 t + i in accumulator register i.
+// Column order: col = hh*d/2 + 8 kb matches B operands taken from such accumulators (decode,
+// the QJL sketch); with `paired`, col = 16 kb + 8 hh matches B operands loaded from memory
+// (the encodes), where lanes v and v + 32 then read the two halves of one 32-byte piece.
 template <typename F>
-static void build_tiles(int d, F value, uint16_t* dst) {
+static void build_tiles(int d, F value, uint16_t* dst, bool paired = false) {
   const int T = d / 32, KB = d / 16, half = d / 2;
   for (int t = 0; t < T; ++t)
     for (int kb = 0; kb < KB; ++kb)
@@ -329,7 +343,7 @@ static void build_tiles(int d, F value, uint16_t* dst) {
         int m = lane % 32, hh = lane / 32;
         int row = ((m / 4) % 2) * half + 16 * t + 4 * (m / 8) + m % 4;
         for (int e = 0; e < 8; ++e) {
-          int col = hh * half + 8 * kb + e;
+          int col = (paired ? 16 * kb + 8 * hh : hh * half + 8 * kb) + e;
           dst[(((size_t)t * KB + kb) * 64 + lane) * 8 + e] = value(row, col);
         }
       }
@@ -357,12 +371,12 @@ static int upload_rotation(Rotation& R) {
     uint16_t* hi = (uint16_t*)(host.data() + R.enc_off + r * R.enc_stride);
     uint16_t* lo = hi + dd;
     // encode: y = Pi x, tiles of Pi split as bf16 hi + bf16 lo
-    build_tiles(d, [&](int row, int col) { return to_bf16((float)P[(size_t)row * d + col]); }, hi);
+    build_tiles(d, [&](int row, int col) { return to_bf16((float)P[(size_t)row * d + col]); }, hi, true);
     build_tiles(d, [&](int row, int col) {
       double v = P[(size_t)row * d + col];
       float h = from_bf16(to_bf16((float)v));
       return to_bf16((float)(v - (double)h));
-    }, lo);
+    }, lo, true);
     // decode: x = Pi^T c, tiles of Pi^T in fp16
     uint16_t* de = (uint16_t*)(host.data() + R.dec_off + r * R.dec_stride);
     build_tiles(d, [&](int row, int col) { return to_f16(P[(size_t)col * d + row]); }, de);

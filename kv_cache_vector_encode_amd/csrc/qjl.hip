@@ -105,11 +105,12 @@ qjl_encode_kernel(QjlKArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vl = lane & 31, hh = lane >> 5;
 
-  // Inputs: lane (v, hh) reads its d/2 contiguous elements with 16-byte loads; bf16 tiles are
-  // prefetched one tile ahead. Every access is unconditional (masked lanes read row v_begin and
-  // write the sink), as in the encode kernel.
+  // Inputs: lane (v, hh) reads elements 16kb + 8hh .. +7 (K block kb) with 16-byte loads, in the
+  // column order of Pi's encode tiles; bf16 tiles are prefetched one tile ahead. Every access is
+  // unconditional (masked lanes read row v_begin and write the sink), as in the encode kernel.
   constexpr int ELEM = IN == TQ_F32 ? 4 : 2;
   constexpr int NRAW = HALF * ELEM / 16;
+  constexpr int PER = ELEM / 2;          // 16-byte loads per K block
   constexpr bool PREFETCH = (IN == TQ_BF16) && D <= 128;
   constexpr int WAVES = qjl_waves<D>();
   const int64_t wstride = (int64_t)gridDim.x * WAVES;
@@ -117,9 +118,9 @@ qjl_encode_kernel(QjlKArgs a) {
     const int64_t v = v_begin + tl * 32 + vl;
     const bool ok = v < v_end;
     const int64_t vs = ok ? v : v_begin;
-    const uint8_t* xp = (const uint8_t*)a.x + (vs * a.x_row_stride + hh * HALF) * ELEM;
+    const uint8_t* xp = (const uint8_t*)a.x + (vs * a.x_row_stride + 8 * hh) * ELEM;
 #pragma unroll
-    for (int k = 0; k < NRAW; ++k) raw[k] = *(const u32x4*)(xp + 16 * k);
+    for (int k = 0; k < NRAW; ++k) raw[k] = *(const u32x4*)(xp + (k / PER) * 32 * PER + (k % PER) * 16);
     if constexpr (SLOT) {
       const int64_t s = a.slot[vs];
       return ok ? s : -1;
@@ -224,8 +225,7 @@ qjl_encode_kernel(QjlKArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float f = fmaf(acc[i], fs, foff);
-        const uint32_t e = lut[(uint32_t)f];
-        const uint32_t code = (e & 15u) + (f > __uint_as_float(e) ? 1u : 0u);
+        const uint32_t code = (__float_as_uint(f) - lut[(uint32_t)f]) >> 24;
         const int pos = (16 * t + i) * BITS;
         pk[pos >> 5] |= code << (pos & 31);
         if ((pos & 31) + BITS > 32) pk[(pos >> 5) + 1] |= code >> (32 - (pos & 31));

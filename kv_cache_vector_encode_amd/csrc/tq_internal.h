@@ -59,9 +59,12 @@ struct Qjl {
 
 // Quantization table for the encode. With f = y * scale + offset (y the rotated, normalized
 // coordinate), bin = floor(f) holds at most one decision boundary: code = base[bin] + (f > thr[bin]),
-// which equals #{k : t_k < y}. Bins cover f in [0, kLutBins) for |y| <= 1. An entry is the
-// float bits of thr (FLT_MAX if the bin has no boundary) with its 4 low mantissa bits replaced by
-// base: thr moves by < 2^-19 of f, i.e. < 3e-6 of y, inside the 1e-5 parity window.
+// which equals #{k : t_k < y}. The offset keeps f >= 1 for |y| <= 1 (up to rounding: bin 0 takes
+// f in [0.5, 1)), so all f of one bin share a float exponent and their bit patterns differ by
+// less than 2^23. An entry e is chosen so that (bits(f) - e) >> 24 is the code:
+//   bin with boundary thr:  e = bits(thr) + 1 - 2^24 - (base << 24)   (f > thr <=> bits(f) > bits(thr))
+//   bin without boundary:   e = bits(lowest f of the bin) - (base << 24)
+// The boundary is kept exactly as a float.
 constexpr int kLutBins = 128;
 struct QuantLut {
   float scale, offset;

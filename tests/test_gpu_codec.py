@@ -69,6 +69,31 @@ def test_identity_rotation_is_scalar_quantization(dev):
                  "identity rotation")
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_extreme_coordinates(dev, d):
+    """y = +-1 in one coordinate, the two ends of the encode's quantization table, and 0 in the
+    others: signed basis vectors under the identity rotation, and signed rows of a Haar rotation
+    (y = Pi x = +-e_i up to rounding), float32 inputs, every width."""
+    eye = np.eye(d)
+    rot_id = tq.Rotation.from_matrix(eye)
+    rot, pis = rotation_pair(d, [d + 3])
+    cases = [(rot_id, eye, np.concatenate([eye, -eye]) * 3.0, "basis"),
+             (rot, pis[0], np.concatenate([pis[0], -pis[0]]) * 0.5, "rows")]
+    for bits in (2, 3, 4):
+        cb = tq.Codebook(d, bits)
+        for r, pi, x, what in cases:
+            xd = torch.from_numpy(x).float().to(dev)
+            log("case: extreme coordinates", what, "d", d, "bits", bits)
+            packed, norms = tq.encode(cb, r, xd)
+            torch.cuda.synchronize()
+            check_encode(to64(xd), packed.cpu().numpy(), norms.cpu().numpy(), pi, d, bits,
+                         "extreme %s d%d b%d" % (what, d, bits))
+            codes = unpack(packed.cpu().numpy(), bits, d)
+            top = np.abs(x @ pi.T).argmax(axis=1)
+            hit = codes[np.arange(2 * d), top]
+            assert np.all(hit[:d] == 2 ** bits - 1) and np.all(hit[d:] == 0)
+
+
 def test_zero_and_small_vectors(dev):
     d = 128
     x = torch.zeros(64, d)
