@@ -66,6 +66,30 @@ struct EncGeo {
   // so one 8-wave workgroup (2 waves per SIMD).
   static constexpr int WG_PER_CU = D == 256 ? 1 : 2;
 };
+// Byte B of `word` = (byte 3 of lo) | (byte 3 of hi) << 4; for B > 0 the other bytes are kept,
+// for B = 0 (written first) bytes 1-3 are cleared: two SDWA instructions (byte-select sources,
+// byte-select destination), where shifting each code out of byte 3 and or-ing it into place
+// takes four. The codes are < 16, so each byte 3 is one nibble.
+template <int B>
+__device__ __forceinline__ uint32_t nibble_pair_to_byte(uint32_t word, uint32_t lo, uint32_t hi) {
+  uint32_t t;
+  asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+      : "=v"(t) : "v"(hi));
+  if constexpr (B == 0)
+    asm("v_or_b32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
+        : "=v"(word) : "v"(lo), "v"(t));
+  else if constexpr (B == 1)
+    asm("v_or_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3 src1_sel:DWORD"
+        : "+v"(word) : "v"(lo), "v"(t));
+  else if constexpr (B == 2)
+    asm("v_or_b32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3 src1_sel:DWORD"
+        : "+v"(word) : "v"(lo), "v"(t));
+  else
+    asm("v_or_b32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3 src1_sel:DWORD"
+        : "+v"(word) : "v"(lo), "v"(t));
+  return word;
+}
+
 template <int D, int IN>
 constexpr int enc_waves() { return 8; }
 template <int D, int IN>
@@ -211,6 +235,7 @@ encode_kernel(EncodeKArgs a) {
     uint32_t pk[Geo::CHUNK_DW];
 #pragma unroll
     for (int w = 0; w < Geo::CHUNK_DW; ++w) pk[w] = 0u;
+    uint32_t wprev = 0u;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       // a fresh opaque offset per tile: the scheduler cannot pull later tiles' Pi reads ahead
@@ -230,10 +255,26 @@ encode_kernel(EncodeKArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float f = fmaf(acc[i], fs, foff);
-        const uint32_t code = (__float_as_uint(f) - lut[(uint32_t)f]) >> 24;
+        const uint32_t w = __float_as_uint(f) - lut[(uint32_t)f];   // the code is byte 3 of w
         const int pos = (16 * t + i) * BITS;
-        pk[pos >> 5] |= code << (pos & 31);
-        if ((pos & 31) + BITS > 32) pk[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+        if constexpr (BITS == 4) {
+          // two codes per byte: byte 3 of the odd coordinate's w goes to the high nibble and the
+          // even one's to the low nibble, written straight into byte (i % 8) / 2 of the word
+          if (i & 1) {
+            uint32_t& word = pk[pos >> 5];
+            switch ((i & 7) >> 1) {
+              case 0: word = nibble_pair_to_byte<0>(word, wprev, w); break;
+              case 1: word = nibble_pair_to_byte<1>(word, wprev, w); break;
+              case 2: word = nibble_pair_to_byte<2>(word, wprev, w); break;
+              default: word = nibble_pair_to_byte<3>(word, wprev, w); break;
+            }
+          }
+          wprev = w;
+        } else {
+          const uint32_t code = w >> 24;
+          pk[pos >> 5] |= code << (pos & 31);
+          if ((pos & 31) + BITS > 32) pk[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+        }
         // table reads in groups of 8: all 16 in flight at once would not fit in registers
         if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       }
