@@ -71,28 +71,11 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
 
   const int r = blockIdx.y;
   const u32x4* gfrag = a.frag + (int64_t)r * a.frag_stride;
-  for (int i = threadIdx.x; i < Geo::FRAG_U4; i += blockDim.x) smem[i] = gfrag[i];
-  {
-    // centroids straight from the kernel-argument segment (indexing the by-value copy with a
-    // lane-dependent index would go through scratch)
-    const uint32_t* kc = (const uint32_t*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
-                                           offsetof(DecodeKArgs, ctab));
-    auto cent = [&](uint32_t k) -> uint32_t { return (kc[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
-    for (int j = threadIdx.x; j < Geo::TAB_N; j += blockDim.x) {
-      if constexpr (Geo::PER_LOOKUP == 4) {
-        tab[2 * j] = cent(j & MASK) | (cent((j >> BITS) & MASK) << 16);
-        tab[2 * j + 1] = cent((j >> (2 * BITS)) & MASK) | (cent(j >> (3 * BITS)) << 16);
-      } else {
-        tab[j] = cent(j & MASK) | (cent(j >> BITS) << 16);
-      }
-    }
-  }
-  __syncthreads();
 
   const int64_t v_begin = a.vpr ? (int64_t)r * a.vpr : 0;
   const int64_t v_end = a.vpr ? min(a.n, v_begin + a.vpr) : a.n;
   const int64_t ntile = (v_end - v_begin + 31) / 32;
-  if (ntile <= 0) return;
+  if (ntile <= 0) return;   // uniform per workgroup: no thread is left at the barrier below
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vl = lane & 31, hh = lane >> 5;
   constexpr int OE = OUT == TQ_F32 ? 4 : 2;
@@ -139,8 +122,27 @@ __global__ void __launch_bounds__(kDecWaves * 64) decode_kernel(DecodeKArgs a) {
   int64_t tile = (int64_t)blockIdx.x * kDecWaves + wave;
   uint32_t cwn[Geo::CHUNK_DW];
   float nrmn;
+  // the first tile's loads are issued before the table copies below, so the two latencies overlap
   fetch(row_of(tile), cwn, nrmn);
   int64_t row_nn = row_of(tile + wstride);
+
+  for (int i = threadIdx.x; i < Geo::FRAG_U4; i += blockDim.x) smem[i] = gfrag[i];
+  {
+    // centroids straight from the kernel-argument segment (indexing the by-value copy with a
+    // lane-dependent index would go through scratch)
+    const uint32_t* kc = (const uint32_t*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+                                           offsetof(DecodeKArgs, ctab));
+    auto cent = [&](uint32_t k) -> uint32_t { return (kc[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
+    for (int j = threadIdx.x; j < Geo::TAB_N; j += blockDim.x) {
+      if constexpr (Geo::PER_LOOKUP == 4) {
+        tab[2 * j] = cent(j & MASK) | (cent((j >> BITS) & MASK) << 16);
+        tab[2 * j + 1] = cent((j >> (2 * BITS)) & MASK) | (cent(j >> (3 * BITS)) << 16);
+      } else {
+        tab[j] = cent(j & MASK) | (cent(j >> BITS) << 16);
+      }
+    }
+  }
+  __syncthreads();
   wait_vmem_all();
 
   for (; tile < ntile; tile += wstride) {

@@ -109,28 +109,11 @@ encode_kernel(EncodeKArgs a) {
 
   const int r = blockIdx.y;
   const u32x4* gfrag = a.frag + (int64_t)r * a.frag_stride;
-  if constexpr (Geo::LDS) {
-    for (int i = threadIdx.x; i < Geo::FRAG_U4; i += blockDim.x) smem[i] = gfrag[i];
-  }
-  {
-    // read the table straight from the kernel-argument segment (the only argument is `a`, at
-    // offset 0): indexing the by-value copy would spill the whole struct to scratch
-    const uint32_t* klut = (const uint32_t*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
-                                             offsetof(EncodeKArgs, lut));
-    for (int i = threadIdx.x; i < kLutBins; i += blockDim.x) lut[i] = klut[i];
-    const float* kcsq = (const float*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
-                                       offsetof(EncodeKArgs, csq));
-    if (threadIdx.x < kMaxLevels) csq[threadIdx.x] = kcsq[threadIdx.x];
-  }
-  __syncthreads();
-  // Tile reads go through an offset the compiler cannot prove loop-invariant; otherwise it
-  // hoists every tile of Pi into registers and spills.
-  const char* abase = Geo::LDS ? (const char*)smem : (const char*)gfrag;
 
   const int64_t v_begin = a.vpr ? (int64_t)r * a.vpr : 0;
   const int64_t v_end = a.vpr ? min(a.n, v_begin + a.vpr) : a.n;
   const int64_t ntile = (v_end - v_begin + 31) / 32;
-  if (ntile <= 0) return;
+  if (ntile <= 0) return;   // uniform per workgroup: no thread is left at the barrier below
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vl = lane & 31, hh = lane >> 5;
 
@@ -163,10 +146,27 @@ encode_kernel(EncodeKArgs a) {
   int64_t tile = (int64_t)blockIdx.x * WAVES + wave;
   u32x4 xr[NRAW];
   int64_t rown = -1;
-  if (PREFETCH) {
-    rown = fetch(tile, xr);
-    wait_vmem_all();
+  // the first tile's loads are issued before the table copies below, so the two latencies overlap
+  if (PREFETCH) rown = fetch(tile, xr);
+
+  if constexpr (Geo::LDS) {
+    for (int i = threadIdx.x; i < Geo::FRAG_U4; i += blockDim.x) smem[i] = gfrag[i];
   }
+  {
+    // read the table straight from the kernel-argument segment (the only argument is `a`, at
+    // offset 0): indexing the by-value copy would spill the whole struct to scratch
+    const uint32_t* klut = (const uint32_t*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+                                             offsetof(EncodeKArgs, lut));
+    for (int i = threadIdx.x; i < kLutBins; i += blockDim.x) lut[i] = klut[i];
+    const float* kcsq = (const float*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+                                       offsetof(EncodeKArgs, csq));
+    if (threadIdx.x < kMaxLevels) csq[threadIdx.x] = kcsq[threadIdx.x];
+  }
+  __syncthreads();
+  if (PREFETCH) wait_vmem_all();
+  // Tile reads go through an offset the compiler cannot prove loop-invariant; otherwise it
+  // hoists every tile of Pi into registers and spills.
+  const char* abase = Geo::LDS ? (const char*)smem : (const char*)gfrag;
 
   for (; tile < ntile; tile += wstride) {
     u32x4 xh[KB], xl[SPLIT_X ? KB : 1];
