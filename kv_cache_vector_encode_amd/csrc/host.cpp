@@ -8,7 +8,10 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <set>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "tq_internal.h"
@@ -205,6 +208,12 @@ static uint16_t to_f16(double v) {
   return sign | (uint16_t)bitsv;
 }
 
+static double from_f16(uint16_t h) {
+  const int e = (h >> 10) & 31, m = h & 1023;
+  double v = e == 0 ? std::ldexp((double)m, -24) : std::ldexp(1.0 + m / 1024.0, e - 15);
+  return (h & 0x8000) ? -v : v;
+}
+
 LevelArgs make_levels(const Codebook& cb) {
   LevelArgs lv;
   std::memset(&lv, 0, sizeof(lv));
@@ -213,6 +222,10 @@ LevelArgs make_levels(const Codebook& cb) {
   for (int j = h - 1; j < kMaxLevels / 2; ++j) lv.pos_thresholds[j] = INFINITY;
   for (int k = 0; k < L; ++k) {
     lv.centroid_f16[k] = to_f16(cb.centroids[k]);
+    // decode operands c = c_hi + c_lo, both scaled by 2^8 so that c_lo stays a normal fp16 number
+    const double chi = from_f16(lv.centroid_f16[k]);
+    lv.dec_c_hi[k] = to_f16(256.0 * chi);
+    lv.dec_c_lo[k] = to_f16(256.0 * (cb.centroids[k] - chi));
     lv.centroid_f32[k] = (float)cb.centroids[k];
     lv.centroid_sq[k] = (float)(cb.centroids[k] * cb.centroids[k]);
     const uint16_t hi = to_bf16((float)cb.centroids[k]);
@@ -349,6 +362,26 @@ static void build_tiles(int d, F value, uint16_t* dst, bool paired = false) {
       }
 }
 
+// Decode tiles of Pi^T: as build_tiles (column order hh*d/2 + 8 kb, the B operands come from a
+// lane's packed chunk), with the output coordinates cut into qs slices of d/qs: slice q's tiles
+// t' = 0 .. T/qs - 1 come first, and lane (vector v, half hh) ends up holding the slice
+// coordinates q*d/qs + hh*d/(2 qs) + 16 t' + i in accumulator register i. Each slice holds two
+// sets, `value(row, col, set)` for set 0 then set 1.
+template <typename F>
+static void build_dec_tiles(int d, int qs, F value, uint16_t* dst) {
+  const int T = d / 32, KB = d / 16, TS = T / qs, sc = d / qs;
+  size_t o = 0;
+  for (int q = 0; q < qs; ++q)
+    for (int set = 0; set < 2; ++set)
+      for (int t = 0; t < TS; ++t)
+        for (int kb = 0; kb < KB; ++kb)
+          for (int lane = 0; lane < 64; ++lane) {
+            const int m = lane % 32, hh = lane / 32;
+            const int row = q * sc + ((m / 4) % 2) * (sc / 2) + 16 * t + 4 * (m / 8) + m % 4;
+            for (int e = 0; e < 8; ++e) dst[o++] = value(row, hh * (d / 2) + 8 * kb + e, set);
+          }
+}
+
 static int upload_rotation(Rotation& R) {
   int dev = 0, count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || count <= 0)
@@ -357,7 +390,7 @@ static int upload_rotation(Rotation& R) {
   const int d = R.d;
   const size_t dd = (size_t)d * d;
   R.enc_stride = 4 * dd;
-  R.dec_stride = 2 * dd;
+  R.dec_stride = 4 * dd;
   R.f32_stride = 4 * dd;
   R.enc_off = 0;
   R.dec_off = R.enc_stride * R.n_rot;
@@ -377,9 +410,13 @@ static int upload_rotation(Rotation& R) {
       float h = from_bf16(to_bf16((float)v));
       return to_bf16((float)(v - (double)h));
     }, lo, true);
-    // decode: x = Pi^T c, tiles of Pi^T in fp16
+    // decode: x = Pi^T c, tiles of 2^11 P_hi and 2^11 P_lo with Pi^T = P_hi + P_lo in fp16
     uint16_t* de = (uint16_t*)(host.data() + R.dec_off + r * R.dec_stride);
-    build_tiles(d, [&](int row, int col) { return to_f16(P[(size_t)col * d + row]); }, de);
+    build_dec_tiles(d, d == 256 ? 4 : 1, [&](int row, int col, int set) {
+      const double v = P[(size_t)col * d + row];
+      const double hi = from_f16(to_f16(v));
+      return to_f16(2048.0 * (set == 0 ? hi : v - hi));
+    }, de);
     float* f = (float*)(host.data() + R.f32_off + r * R.f32_stride);
     for (size_t i = 0; i < dd; ++i) f[i] = (float)P[i];
     float* ft = (float*)(host.data() + R.f32t_off + r * R.f32_stride);
@@ -447,6 +484,21 @@ static int upload_qjl(Qjl& Q, const float* sketch) {
   }
   Q.device = dev;
   return TQ_OK;
+}
+
+hipError_t set_kernel_lds(const void* kernel, int device, size_t lds) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  std::lock_guard<std::mutex> lk(mu);
+  if (done.count({kernel, device})) return hipSuccess;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (cur != device) (void)hipSetDevice(cur);
+  if (e == hipSuccess) done.insert({kernel, device});
+  return e;
 }
 
 int device_cu_count(int device) {

@@ -332,12 +332,9 @@ static hipError_t launch_qjl_t(const QjlEncodeLaunch& Q) {
   const int nrot = L.vectors_per_rot ? (int)((L.n + L.vectors_per_rot - 1) / L.vectors_per_rot) : 1;
   const int64_t tiles = (per_rot + 31) / 32;
   const size_t lds = Geo::LDS ? 2 * Geo::FRAG_U4 * sizeof(u32x4) : 0;
-  static bool attr_done = false;
-  if (!attr_done && lds > 0) {
-    hipError_t e = hipFuncSetAttribute((const void*)qjl_encode_kernel<D, BITS, IN, SLOT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (lds > 0) {
+    hipError_t e = set_kernel_lds((const void*)qjl_encode_kernel<D, BITS, IN, SLOT>, L.rot->device, lds);
     if (e != hipSuccess) return e;
-    attr_done = true;
   }
   const int cu = device_cu_count(L.rot->device);
   const int64_t want = (int64_t)cu * Geo::WG_PER_CU;

@@ -27,7 +27,9 @@ struct Rotation {
   std::vector<double> pi;        // [n_rot, d, d] row-major
   // Device buffers (one allocation, offsets below), per rotation:
   //  enc_frag: bf16 MFMA A tiles of Pi (hi then lo), 4*d*d bytes
-  //  dec_frag: fp16 MFMA A tiles of Pi^T, 2*d*d bytes
+  //  dec_frag: fp16 MFMA A tiles of Pi^T for the decode, 4*d*d bytes: per output slice (one at
+  //            d <= 128, four at d = 256) the set 2^11 P_hi, then the set 2^11 P_lo, with
+  //            Pi^T = P_hi + P_lo and P_hi = fp16(Pi^T)
   //  pi_f32:   Pi in float32 row-major, 4*d*d bytes
   //  pit_f32:  Pi^T in float32 row-major, 4*d*d bytes
   //  pad:      kZeroBytes of zeros that masked lanes load from, then kSinkBytes that masked
@@ -75,6 +77,8 @@ struct QuantLut {
 struct LevelArgs {
   float pos_thresholds[kMaxLevels / 2];   // t_{L/2+1} .. t_{L-1}: positive decision boundaries
   uint16_t centroid_f16[kMaxLevels];      // c_k as fp16 bits
+  uint16_t dec_c_hi[kMaxLevels];          // decode operands: 2^8 fp16(c_k) and 2^8 (c_k - fp16(c_k)),
+  uint16_t dec_c_lo[kMaxLevels];          //   each as fp16 bits
   uint32_t centroid_bf16x2[kMaxLevels];   // c_k = hi + lo as bf16 bits: hi | lo << 16
   float centroid_f32[kMaxLevels];
   float centroid_sq[kMaxLevels];          // c_k^2 (float64 square, rounded once)
@@ -174,6 +178,10 @@ hipError_t launch_attention_qjl(const tq_attn_params* p, const Codebook& ck, con
                                 bool scores_only, const AttnLayout& lay, hipStream_t stream);
 
 int device_cu_count(int device);
+
+// Raise a kernel's dynamic LDS limit to `lds` bytes on `device`, once per (kernel, device);
+// thread-safe (handles may be shared by threads, and two first calls may race).
+hipError_t set_kernel_lds(const void* kernel, int device, size_t lds);
 
 }  // namespace tq
 

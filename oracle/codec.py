@@ -123,6 +123,32 @@ def decode(packed, norms, pi, centroids, bits: int, d: int):
     return decode_codes(unpack_codes(packed, bits, d), norms, pi, centroids)
 
 
+# (significant bits, frexp exponent of the smallest normal, largest finite value) per format
+_FORMATS = {
+    torch.bfloat16: (8, -125, (2.0 - 2.0 ** -7) * 2.0 ** 127),
+    torch.float16: (11, -13, 65504.0),
+    torch.float32: (24, -125, float(np.finfo(np.float32).max)),
+}
+
+
 def cast(x, dtype: torch.dtype):
-    """Round a float64 array to a storage dtype (round to nearest even) and back to float64."""
-    return torch.from_numpy(np.asarray(x, dtype=np.float64)).to(dtype).to(torch.float64).numpy()
+    """Round float64 values to a storage dtype and return them as float64.
+
+    The decode's last step casts to the input's dtype (KV Cache API page,
+    TurboQuantCompressorMSE.decompress); read as IEEE round-to-nearest-even of the exact value.
+    Written from that definition: with x = m 2^e (frexp, m in [0.5, 1)), the spacing of the
+    format's values near x is q = 2^(max(e, e_min) - p) for p significant bits (the max covers
+    the subnormal range), and x rounds to rint(x / q) * q (rint breaks ties to even); a result
+    beyond the largest finite value is infinite. One rounding step: converting float64 to float32
+    first and then to the 16-bit format rounds twice and can land on the other neighbour.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == torch.float64:
+        return x.copy()
+    p, emin, big = _FORMATS[dtype]
+    _, e = np.frexp(x)
+    q = np.ldexp(1.0, np.maximum(e, emin) - p)
+    with np.errstate(invalid="ignore", over="ignore"):
+        y = np.rint(x / q) * q
+        y = np.where(np.abs(y) > big, np.copysign(np.inf, x), y)
+    return np.where(np.isfinite(x), y, x)

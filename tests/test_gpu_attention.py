@@ -109,12 +109,14 @@ def test_attention_bf16_output_and_scale(dev):
                     [T] * B, "bf16 out, scale 0.3")
 
 
-def _paged(dev, S, max_len, Hkv, Hq, d, bk, bv, seed=7, oracle_rows=None):
-    """Paged pool [num_blocks, Hkv, 16, row] of one layer's tokens, written by tq_encode through a
-    slot mapping. oracle_rows: sequences whose rows are then replaced by oracle-side inputs
-    (all sequences: the oracle's encode of their tokens; a list: random code bytes with the
-    tokens' own norms, cheap at full size) so that the attention check reads no GPU-written row."""
-    shape = ti.PagedShape(sequences=S, max_len=max_len, kv_heads=Hkv, q_heads=Hq)
+def _paged(dev, S, max_len, Hkv, Hq, d, bk, bv, seed=7, oracle_rows=None, shape=None):
+    """Paged pool [num_blocks, Hkv, block_size, row] of one layer's tokens, written by tq_encode
+    through a slot mapping. oracle_rows: sequences whose rows are then replaced by oracle-side
+    inputs (all sequences: the oracle's encode of their tokens; a list: random code bytes with
+    the tokens' own norms, cheap at full size) so that the attention check reads no GPU-written
+    row."""
+    if shape is None:
+        shape = ti.PagedShape(sequences=S, max_len=max_len, kv_heads=Hkv, q_heads=Hq)
     lay = ti.paged_layout(shape, seed=seed)
     total = int(lay.seq_starts[-1])
     k, v, _ = ti.paged_layer_tokens(shape, total, d, layer=seed, device=dev)
@@ -199,12 +201,62 @@ def test_attention_paged_small(dev, d, bk, bv):
                             out_dtype=torch.float32, return_lse=True, num_kv_heads=Hkv)
     torch.cuda.synchronize()
     _check_paged(c, d, bk, bv, o.cpu().numpy().astype(np.float64), lse.cpu().numpy(), range(S), "paged small")
-    # scores from the paged cache equal the dense recomputation of the same tokens
+    # scores from the paged cache, entry by entry against the oracle's scores over the gathered pages
     s = tq.scores_compressed(c["ck"], c["rk"], c["q"], c["kp"], c["kn"], seq_lens=lay.seq_lens.to(dev),
                              max_seq_len=int(lay.seq_lens.max()), block_table=lay.block_table.to(dev),
                              block_size=16, num_kv_heads=Hkv)
     torch.cuda.synchronize()
-    assert torch.isfinite(s[0, :, : int(lay.seq_lens[0])]).all()
+    _check_paged_scores(c, d, bk, s.cpu().numpy().astype(np.float64), range(S), "paged small scores")
+
+
+def _check_paged_scores(c, d, bk, got, seqs, what):
+    """Paged tq_scores_compressed output `got` ([S, Hq, max_len], or a map from sequence to its
+    [Hq, max_len] rows) against oracle.attention.scores over
+    the sequence's gathered rows (the oracle-side pool copies), at the Cauchy-Schwarz bar; entries
+    past a sequence's length are left untouched (NaN)."""
+    lay = c["lay"]
+    bs = c["shape"].block_size
+    lens = lay.seq_lens.numpy()
+    table = lay.block_table.numpy()
+    cb = ocb.codebook(d, bk)
+    q64 = to64(c["q"])
+    scale = 1 / math.sqrt(d)
+    worst = 0.0
+    for s_ in seqs:
+        L = int(lens[s_])
+        sub = np.array([s_])
+        kseq = oatt.gather_paged(c["kp_host"], table[sub], [L], bs)[0]        # [Hkv, L, row]
+        knseq = oatt.gather_paged(c["kn_host"], table[sub], [L], bs)[0]       # [Hkv, L]
+        khat = oatt.decode_cache(kseq, knseq, c["pk"], cb.centroids, bk, d)[None]
+        ref = oatt.scores(q64[s_:s_ + 1], khat, scale)[0]
+        codes = occ.unpack_codes(kseq.reshape(-1, kseq.shape[-1]), bk, d).reshape(kseq.shape[0], L, d)
+        bound = score_bounds(q64[s_:s_ + 1], knseq[None], codes[None], cb, scale)[0]
+        g = got[s_]                                                            # [Hq, max_len]
+        err = np.abs(g[:, :L] - ref)
+        assert np.all(err <= bound), "%s seq %d: score error %.3g of the bound" % (what, s_, float(np.max(err / bound)))
+        assert np.all(np.isnan(g[:, L:])), (what, s_)
+        worst = max(worst, float(np.max(err / bound)))
+    log("%s: %d sequences, worst score error / bound = %.3g" % (what, len(list(seqs)), worst))
+
+
+@pytest.mark.parametrize("block", [12, 48])
+def test_paged_any_block_size(dev, block):
+    """Pages of 12 and 48 tokens: not a power of two, so every token's page is looked up on its own
+    (the kernels' general paging path); scores and attention against the oracle."""
+    d, bk, bv, S, Hkv, Hq = 128, 3, 2, 5, 2, 8
+    log("case: paged block %d" % block)
+    shape = ti.PagedShape(sequences=S, max_len=500, kv_heads=Hkv, q_heads=Hq, block_size=block)
+    c = _paged(dev, S, 500, Hkv, Hq, d, bk, bv, seed=3, oracle_rows="all", shape=shape)
+    lay = c["lay"]
+    args = dict(seq_lens=lay.seq_lens.to(dev), max_seq_len=int(lay.seq_lens.max()),
+                block_table=lay.block_table.to(dev), block_size=block, num_kv_heads=Hkv)
+    s = tq.scores_compressed(c["ck"], c["rk"], c["q"], c["kp"], c["kn"], **args)
+    o, lse = tq.attn_decode(c["ck"], c["rk"], c["cv"], c["rv"], c["q"], c["kp"], c["kn"], c["vp"], c["vn"],
+                            out_dtype=torch.float32, return_lse=True, **args)
+    torch.cuda.synchronize()
+    _check_paged_scores(c, d, bk, s.cpu().numpy().astype(np.float64), range(S), "paged block %d scores" % block)
+    _check_paged(c, d, bk, bv, o.cpu().numpy().astype(np.float64), lse.cpu().numpy(), range(S),
+                 "paged block %d" % block)
 
 
 def test_fused_attention_workload_full(dev):
@@ -276,6 +328,14 @@ def test_paged_ragged_workload(dev, d):
     ls = lay_slots.cpu().numpy()
     check_decode(dec, kp_h[ls], kn_h[ls], c["pk"], d, bk, "paged K gather decode d%d" % d)
     _check_paged(c, d, bk, bv, o.cpu().numpy().astype(np.float64), None, seqs, "paged ragged d%d" % d)
+    # paged scores of the checked sequences (one query per sequence, all 32 heads)
+    sc = tq.scores_compressed(c["ck"], c["rk"], c["q"], c["kp"], c["kn"], seq_lens=lay.seq_lens.to(dev),
+                              max_seq_len=int(lay.seq_lens.max()), block_table=lay.block_table.to(dev),
+                              block_size=16, num_kv_heads=shape.kv_heads)
+    torch.cuda.synchronize()
+    got = {s_: sc[s_].cpu().numpy().astype(np.float64) for s_ in seqs}
+    del sc
+    _check_paged_scores(c, d, bk, got, seqs, "paged ragged d%d scores" % d)
 
 
 def test_attention_softmax_margins(dev):

@@ -280,7 +280,7 @@ def test_qjl_error_paths(dev):
     with pytest.raises(tq.TQError, match="not supported on the GPU"):
         tq.qjl_encode(cb1, sk, x)
     cb64 = tq.Codebook(64, 2)
-    with pytest.raises(tq.TQError, match="does not match"):
+    with pytest.raises((ValueError, tq.TQError), match="does not match"):
         tq.qjl_encode(cb64, sk, x)
     cb = tq.Codebook(d, 2)
     sg = torch.empty(4 * 16 + 8, dtype=torch.uint8, device=dev)[8:].view(4, 16)   # misaligned signs
@@ -290,7 +290,7 @@ def test_qjl_error_paths(dev):
     q = torch.zeros(1, 8, d, dtype=torch.bfloat16, device=dev)
     kp = torch.zeros(1, 2, 8, d * 2 // 8, dtype=torch.uint8, device=dev)
     kn = torch.zeros(1, 2, 8, device=dev)
-    with pytest.raises(tq.TQError, match="not created on rot_k"):
+    with pytest.raises((ValueError, tq.TQError), match="not created on rot_k"):
         tq.scores_compressed(cb, other, q, kp, kn, qjl=sk, k_signs=torch.zeros(1, 2, 8, 16, dtype=torch.uint8,
                                                                              device=dev), k_rnorms=kn)
 

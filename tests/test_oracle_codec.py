@@ -207,6 +207,47 @@ def test_storage_cast_rounds_to_nearest_even():
     assert list(codec.cast(v, torch.bfloat16)) == [1.0, 1.0 + 4 * 2 ** -8]
 
 
+def test_storage_cast_rounds_once():
+    # just above a 16-bit halfway point by less than a float32 ulp: rounding through float32
+    # first lands on the halfway point and then on the even neighbour (the wrong one)
+    assert codec.cast(np.array([1.0 + 2 ** -8 + 2 ** -30]), torch.bfloat16)[0] == 1.0 + 2 ** -7
+    assert codec.cast(np.array([-(1.0 + 2 ** -8 + 2 ** -30)]), torch.bfloat16)[0] == -(1.0 + 2 ** -7)
+    assert codec.cast(np.array([1.0 + 2 ** -11 + 2 ** -40]), torch.float16)[0] == 1.0 + 2 ** -10
+
+
+def test_storage_cast_float16_matches_numpy():
+    # numpy converts float64 to float16 in one correctly rounded step (subnormals, overflow and
+    # ties included): an independent implementation of the same definition
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.normal(size=20000) * np.exp(rng.uniform(-25, 12, size=20000)),
+                        [0.0, -0.0, 2.0 ** -25, 3 * 2.0 ** -25, 2.0 ** -24, 65504.0, 65519.9, 65520.0, -7e4,
+                         np.inf, -np.inf]])
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).astype(np.float64)
+    got = codec.cast(x, torch.float16)
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_storage_cast_bfloat16_is_nearest():
+    # brute force: the result is a bfloat16 value (torch keeps it exactly), no other bfloat16
+    # value is nearer, and exact ties go to the even significand
+    rng = np.random.default_rng(6)
+    x = rng.normal(size=5000) * np.exp(rng.uniform(-20, 20, size=5000))
+    x = np.concatenate([x, 1.0 + (2 * np.arange(1, 200) + 1) * 2.0 ** -8])   # exact ties
+    y = codec.cast(x, torch.bfloat16)
+    yt = torch.from_numpy(y).to(torch.bfloat16)
+    assert np.array_equal(yt.double().numpy(), y)                      # representable
+    up = torch.nextafter(yt, torch.full_like(yt, float("inf"))).double().numpy()
+    dn = torch.nextafter(yt, torch.full_like(yt, float("-inf"))).double().numpy()
+    err = np.abs(y - x)
+    assert np.all(err <= np.abs(up - x)) and np.all(err <= np.abs(dn - x))
+    tie = (err == np.abs(up - x)) | (err == np.abs(dn - x))
+    bits = yt.view(torch.int16).numpy()
+    assert np.all(bits[tie] % 2 == 0)
+    assert codec.cast(np.array([3.4e38 * 1.01]), torch.bfloat16)[0] == np.inf
+
+
 # --- byte accounting -------------------------------------------------------------------
 
 def test_ratios_the_pages_print(golden_dir):
