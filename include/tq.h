@@ -244,6 +244,18 @@ int tq_scores_compressed(const tq_attn_params* p, float* scores, tq_stream_t str
  * o = 0 and lse = -inf. */
 int tq_attn_decode(const tq_attn_params* p, tq_stream_t stream);
 
+/* tq_attn_decode without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * parameters, results and errors as tq_attn_decode, except that p->workspace and
+ * p->workspace_bytes are ignored: the rotated queries and split partials go to a static device
+ * array of 32 MiB (one per GPU the library runs on, held until the process ends) that the
+ * library resolves once per device; no device memory is allocated or freed by this call.
+ * A call whose tq_attn_workspace_size exceeds 32 MiB fails with TQ_ERR_WORKSPACE before any
+ * launch (use fewer num_splits or tq_attn_decode). All calls on one GPU share that array and
+ * nothing in it must start at zero: calls that overlap on one GPU (other streams, other host
+ * threads) race, so serialize them (one stream, or events between streams). */
+int tq_attn_decode_noalloc(const tq_attn_params* p, tq_stream_t stream);
+
 /* ---- affine group quantization of values ---------------------------------------------------
  * KV Cache API page, quantize_values / dequantize_values: per group of 32 consecutive
  * elements of a vector, zero = min, scale = max((max - min) / (2^bits - 1), 1e-12) in float32,

@@ -18,6 +18,7 @@ from . import _lib
 from ._lib import AttnParams, TQError, TQ_BF16, TQ_F16, TQ_F32, check, lib
 
 __all__ = ["Codebook", "Rotation", "QJLSketch", "encode", "qjl_encode", "decode", "scores_compressed", "attn_decode",
+           "attn_decode_noalloc",
            "attn_workspace_size", "packed_row_bytes", "TQError", "TQ_F32", "TQ_BF16", "TQ_F16",
            "dtype_code"]
 
@@ -495,6 +496,20 @@ def attn_decode(cb_k: Codebook, rot_k: Rotation, cb_v: Codebook, rot_v: Rotation
     check(lib().tq_attn_decode(C.byref(p), _stream(stream)))
     out._tq_workspace = ws
     return (out, lse) if return_lse else out
+
+
+def attn_decode_noalloc(cb_k: Codebook, rot_k: Rotation, cb_v: Codebook, rot_v: Rotation, q: torch.Tensor,
+                        k_packed, k_norms, v_packed, v_norms, out: torch.Tensor, lse=None, seq_lens=None,
+                        max_seq_len=None, block_table=None, block_size=0, batch_per_rot=0, scale=None, num_splits=0,
+                        num_kv_heads=None, stream=None, k_window=None, v_window=None, qjl=None, k_signs=None,
+                        k_rnorms=None):
+    """attn_decode into caller-owned `out` (and `lse`) with libtq's static scratch as the
+    workspace: the call allocates nothing. Calls that overlap on one GPU race on that scratch."""
+    p = _params(cb_k, rot_k, q, k_packed, k_norms, cb_v, rot_v, v_packed, v_norms, seq_lens, max_seq_len,
+                block_table, block_size, batch_per_rot, scale, out, lse, num_splits, num_kv_heads, k_window,
+                v_window, qjl, k_signs, k_rnorms)
+    check(lib().tq_attn_decode_noalloc(C.byref(p), _stream(stream)))
+    return out
 
 
 def window_append(cb_k: Codebook, rot_k: Rotation, cb_v: Codebook, rot_v: Rotation, k_new: torch.Tensor,

@@ -18,7 +18,8 @@ EXPORTS = (
     "tq_codebook_free", "tq_rotation_from_gaussian", "tq_rotation_from_matrix", "tq_rotation_compute",
     "tq_rotation_get", "tq_rotation_dims", "tq_rotation_free", "tq_rotation_hadamard", "tq_encode",
     "tq_encode_norm_corrected", "tq_decode",
-    "tq_attn_workspace_size", "tq_scores_compressed", "tq_attn_decode", "tq_window_append_workspace_size",
+    "tq_attn_workspace_size", "tq_scores_compressed", "tq_attn_decode", "tq_attn_decode_noalloc",
+    "tq_window_append_workspace_size",
     "tq_window_append", "tq_gq_encode", "tq_gq_decode", "tq_qjl_create", "tq_qjl_free", "tq_qjl_encode",
 )
 
@@ -85,6 +86,7 @@ def lib():
         "tq_attn_workspace_size": ([C.POINTER(AttnParams)], C.c_size_t),
         "tq_scores_compressed": ([C.POINTER(AttnParams), vp, vp], i32),
         "tq_attn_decode": ([C.POINTER(AttnParams), vp], i32),
+        "tq_attn_decode_noalloc": ([C.POINTER(AttnParams), vp], i32),
         "tq_window_append_workspace_size": ([C.POINTER(WindowAppendParams)], C.c_size_t),
         "tq_window_append": ([C.POINTER(WindowAppendParams), vp], i32),
         "tq_gq_encode": ([i32, i32, vp, i32, i64, i64, vp, vp, vp, vp], i32),

@@ -1,6 +1,8 @@
 // Scores and fused decode attention: workspace layout and the dispatch of the plain (MSE-key)
 // kernels; the kernels themselves are in attention_impl.h, the QJL-key dispatch in
 // attention_qjl.hip.
+#include <mutex>
+
 #include "attention_impl.h"
 
 namespace tq {
@@ -40,6 +42,33 @@ AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu) {
   L.total = qbytes + align256(nparts * p->batch * p->num_q_heads * (d + 2) * sizeof(float));
   if (L.total == 0) L.total = 256;
   return L;
+}
+
+// ---- static scratch for callers that cannot allocate (tq_attn_decode_noalloc) -------------------
+// The workspace of an attention call (rotated queries and split partials) held in a file-scope
+// device array: every GPU the library runs on holds one copy of kAttnScratchBytes until the
+// process ends. Host code never passes `scratch` itself to a kernel (in host code the name is a
+// stand-in, not a device address); attn_scratch resolves the array's address on each device once,
+// with that device current, and callers pass that pointer.
+static __device__ __align__(256) uint8_t scratch[kAttnScratchBytes];
+
+hipError_t attn_scratch(int device, void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device) return hipErrorInvalidDevice;   // the caller makes `device` current
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[device] = a;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
 }
 
 hipError_t launch_attention(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,

@@ -974,7 +974,8 @@ size_t tq_attn_workspace_size(const tq_attn_params* p) {
   return attn_workspace_layout(p, p->rot_k->rot.d, device_cu_count(dev)).total;
 }
 
-static int attn_common(const tq_attn_params* p, float* scores, bool scores_only, tq_stream_t stream, const char* who) {
+static int attn_common(const tq_attn_params* p, float* scores, bool scores_only, tq_stream_t stream, const char* who,
+                       bool static_scratch = false) {
   int s = check_attn(p, scores_only, who);
   if (s) return s;
   if (p->batch == 0 || p->max_seq_len == 0) {
@@ -1007,15 +1008,31 @@ static int attn_common(const tq_attn_params* p, float* scores, bool scores_only,
   }
   const int d = p->rot_k->rot.d;
   AttnLayout lay = attn_workspace_layout(p, d, device_cu_count(p->rot_k->rot.device));
-  if (!p->workspace) return fail(TQ_ERR_WORKSPACE, std::string(who) + ": workspace is NULL");
-  if (!aligned(p->workspace, 256)) return fail(TQ_ERR_ALIGN, std::string(who) + ": workspace must be 256-byte aligned");
-  if (p->workspace_bytes < lay.total)
-    return fail(TQ_ERR_WORKSPACE, std::string(who) + ": workspace_bytes = " + std::to_string(p->workspace_bytes) +
-                                      " is smaller than the " + std::to_string(lay.total) + " bytes needed");
-  if ((s = check_device(p->rot_k->rot, who))) return s;
+  tq_attn_params ps = *p;   // with the static scratch as the workspace (static_scratch)
+  if (static_scratch) {
+    if (lay.total > kAttnScratchBytes)
+      return fail(TQ_ERR_WORKSPACE, std::string(who) + ": this call needs " + std::to_string(lay.total) +
+                                        " bytes of scratch but the static scratch holds " +
+                                        std::to_string(kAttnScratchBytes) +
+                                        " (fewer num_splits, a smaller batch, or tq_attn_decode with a workspace)");
+    if ((s = check_device(p->rot_k->rot, who))) return s;
+    void* ptr = nullptr;
+    hipError_t e = attn_scratch(p->rot_k->rot.device, &ptr);
+    if (e != hipSuccess)
+      return fail(TQ_ERR_HIP, std::string(who) + ": resolving the static scratch failed: " + hipGetErrorString(e));
+    ps.workspace = ptr;
+    ps.workspace_bytes = kAttnScratchBytes;
+  } else {
+    if (!p->workspace) return fail(TQ_ERR_WORKSPACE, std::string(who) + ": workspace is NULL");
+    if (!aligned(p->workspace, 256)) return fail(TQ_ERR_ALIGN, std::string(who) + ": workspace must be 256-byte aligned");
+    if (p->workspace_bytes < lay.total)
+      return fail(TQ_ERR_WORKSPACE, std::string(who) + ": workspace_bytes = " + std::to_string(p->workspace_bytes) +
+                                        " is smaller than the " + std::to_string(lay.total) + " bytes needed");
+    if ((s = check_device(p->rot_k->rot, who))) return s;
+  }
   const Codebook& cv = scores_only ? p->cb_k->cb : p->cb_v->cb;
   const Rotation& rv = scores_only ? p->rot_k->rot : p->rot_v->rot;
-  return hip_status(launch_attention(p, p->cb_k->cb, cv, p->rot_k->rot, rv, scores, scores_only, lay,
+  return hip_status(launch_attention(&ps, p->cb_k->cb, cv, p->rot_k->rot, rv, scores, scores_only, lay,
                                      (hipStream_t)stream),
                     who);
 }
@@ -1026,6 +1043,10 @@ int tq_scores_compressed(const tq_attn_params* p, float* scores, tq_stream_t str
 
 int tq_attn_decode(const tq_attn_params* p, tq_stream_t stream) {
   return attn_common(p, nullptr, false, stream, "tq_attn_decode");
+}
+
+int tq_attn_decode_noalloc(const tq_attn_params* p, tq_stream_t stream) {
+  return attn_common(p, nullptr, false, stream, "tq_attn_decode_noalloc", true);
 }
 
 }  // extern "C"

@@ -172,6 +172,10 @@ AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu);
 hipError_t launch_attention(const tq_attn_params* p, const Codebook& ck, const Codebook& cv,
                             const Rotation& rk, const Rotation& rv, float* scores_out,
                             bool scores_only, const AttnLayout& lay, hipStream_t stream);
+// Static scratch of tq_attn_decode_noalloc: kAttnScratchBytes per device; attn_scratch returns
+// the device address of `device`'s copy (resolved once per device, which must be current).
+constexpr size_t kAttnScratchBytes = (size_t)32 << 20;
+hipError_t attn_scratch(int device, void** ptr);
 // The same with QJL keys (p->qjl_k set), in its own translation unit.
 hipError_t launch_attention_qjl(const tq_attn_params* p, const Codebook& ck, const Codebook& cv,
                                 const Rotation& rk, const Rotation& rv, float* scores_out,
