@@ -19,11 +19,13 @@ AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu) {
     if (nblk < 1) nblk = 1;
     // one full round of resident waves (waves per SIMD x 4 SIMDs x CUs): a partial last round
     // would run the chip at a fraction of its occupancy, and every extra wave pays the
-    // prologue (operand tables, query operands) and one more partial for the merge; at least
-    // 4 blocks of 32 tokens per wave. The round is counted for 2-bit values (other value widths
-    // run a fraction of a round more or less).
-    const int wpe = attn_wpe(d, p->cb_k->cb.bits, 2, p->qjl_k != nullptr, p->block_table != nullptr);
-    const int64_t target = (int64_t)wpe * 4 * num_cu;
+    // prologue (operand tables, query operands) and a share of one more partial for the merge;
+    // at least 4 blocks of 32 tokens per wave.
+    // scores-only calls run the kernels built with the K width on the (unused) V side
+    const int bk = p->cb_k->cb.bits, bv = p->cb_v ? p->cb_v->cb.bits : bk;
+    const int dev = p->rot_k->rot.device;
+    const int per_cu = p->qjl_k ? attn_resident_waves_qjl(p, d, bk, bv, dev) : attn_resident_waves(p, d, bk, bv, dev);
+    const int64_t target = (int64_t)per_cu * num_cu;
     int64_t s_eff = (target + pairs - 1) / pairs;
     const int64_t cap = nblk >= 8 ? nblk / 4 : 1;
     if (s_eff > cap) s_eff = cap;
@@ -37,8 +39,9 @@ AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu) {
   const size_t qbytes = p->qjl_k ? 2 * qvec : qvec;
   L.qsk_off = qvec;
   L.part_off = qbytes;
-  // one partial per split, plus one for the recent-token window
-  const size_t nparts = (size_t)kAttnWaves * splits + (p->window > 0 ? 1 : 0);
+  // one partial per split (a workgroup combines its waves' partials), plus one for the
+  // recent-token window
+  const size_t nparts = (size_t)splits + (p->window > 0 ? 1 : 0);
   L.total = qbytes + align256(nparts * p->batch * p->num_q_heads * (d + 2) * sizeof(float));
   if (L.total == 0) L.total = 256;
   return L;
@@ -69,6 +72,14 @@ hipError_t attn_scratch(int device, void** ptr) {
   }
   *ptr = addr[device];
   return hipSuccess;
+}
+
+int attn_resident_waves(const tq_attn_params* p, int d, int bk, int bv, int device) {
+  switch (d) {
+    case 64: return attn_resident<64, false>(p, bk, bv, device);
+    case 128: return attn_resident<128, false>(p, bk, bv, device);
+    default: return attn_resident<256, false>(p, bk, bv, device);
+  }
 }
 
 hipError_t launch_attention(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,

@@ -34,6 +34,7 @@
 #include <math.h>
 
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -707,20 +708,59 @@ attn_kernel(AttnKArgs a) {
   }
 
   if constexpr (!SCORES) {
+    // this wave's partial (m in natural-log units, l, acc relative to e^m); lane (head n16, q4)
+    // holds the coordinate groups 4*q4 + r (register r of the P.V MFMA's D layout)
     float lt = l_run;
     lt += wave_xor(lt, 16);
     lt += wave_xor(lt, 32);
-    if (head_ok) {
-      float* P = a.part + (((int64_t)sidx * a.B + b) * a.Hq + h) * (D + 2);
-      if (q4 == 0) {
-        P[0] = m_run * 0.6931471805599453f;   // back to natural-log units
-        P[1] = lt;
+    float mw = m_run * 0.6931471805599453f;   // back to natural-log units
+    float av[4 * TV];
+#pragma unroll
+    for (int t = 0; t < TV; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) av[r * TV + t] = acc[t][r] * n_eff;
+    // The workgroup's four waves cover adjacent token ranges of one (sequence, KV head): their
+    // partials are combined here through LDS (waves 2, 3 into 0, 1, then 1 into 0), so one
+    // partial per workgroup goes to the merge. Each lane meets the same lane of the other waves,
+    // which holds the same heads and coordinates.
+    constexpr int CW = 4 * TV + 3;   // floats per lane slot (odd stride: no bank conflicts)
+    __shared__ float cmb[2][64][CW];
+    auto put = [&](float* sl) {
+      sl[0] = mw;
+      sl[1] = lt;
+#pragma unroll
+      for (int i = 0; i < 4 * TV; ++i) sl[2 + i] = av[i];
+    };
+    auto take = [&](const float* sl) {
+      const float m2 = sl[0];
+      const float M = fmaxf(mw, m2);
+      if (M > -INFINITY) {
+        const float w1 = __expf(mw - M), w2 = __expf(m2 - M);   // a -inf side weighs 0
+        lt = lt * w1 + sl[1] * w2;
+#pragma unroll
+        for (int i = 0; i < 4 * TV; ++i) av[i] = av[i] * w1 + sl[2 + i] * w2;
+        mw = M;
       }
-      // D layout of the P.V MFMA: lane (head n16, q4) register r = coordinate group 4*q4 + r
+    };
+    if (wave >= 2) put(&cmb[wave - 2][lane][0]);
+    __syncthreads();
+    if (wave < 2) take(&cmb[wave][lane][0]);
+    __syncthreads();
+    if (wave == 1) put(&cmb[0][lane][0]);
+    __syncthreads();
+    if (wave == 0) {
+      take(&cmb[0][lane][0]);
+      if (head_ok) {
+        float* P = a.part + (((int64_t)blockIdx.x * a.B + b) * a.Hq + h) * (D + 2);
+        if (q4 == 0) {
+          P[0] = mw;
+          P[1] = lt;
+        }
 #pragma unroll
-      for (int t = 0; t < TV; ++t)
+        for (int t = 0; t < TV; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) P[2 + (4 * q4 + r) * (D / 16) + t] = acc[t][r] * n_eff;
+          for (int r = 0; r < 4; ++r) P[2 + (4 * q4 + r) * (D / 16) + t] = av[r * TV + t];
+      }
     }
   }
 }
@@ -1119,6 +1159,50 @@ __global__ void __launch_bounds__(D * kParts) merge_kernel(const float* part, in
   }
 }
 
+// Resident waves per CU of the fused-attention kernel instance (registers and LDS as compiled),
+// from the runtime's occupancy calculator, once per (instance, device). The split count sizes the
+// grid to one round of them.
+template <int D, int BK, int BV, int PAGE, bool QJL>
+static int attn_resident_waves_t(int device) {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  std::lock_guard<std::mutex> lk(mu);
+  if (device >= 0 && device < 64 && cached[device]) return cached[device];
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, (const void*)attn_kernel<D, BK, BV, false, PAGE, QJL>,
+                                                   kAttnWaves * 64, 0) != hipSuccess ||
+      blocks <= 0)
+    blocks = attn_wpe(D, BK, BV, QJL, PAGE != kDense);   // the build's target: wpe waves per SIMD
+  const int w = blocks * kAttnWaves;
+  if (device >= 0 && device < 64) cached[device] = w;
+  return w;
+}
+
+template <int D, int BK, int BV, bool QJL>
+static int attn_resident_p(const tq_attn_params* p, int device) {
+  if (!p->block_table) return attn_resident_waves_t<D, BK, BV, kDense, QJL>(device);
+  const int bs = p->block_size;
+  if (bs >= 16 && (bs & (bs - 1)) == 0) return attn_resident_waves_t<D, BK, BV, kPagedPow2, QJL>(device);
+  return attn_resident_waves_t<D, BK, BV, kPagedAny, QJL>(device);
+}
+
+template <int D, bool QJL>
+static int attn_resident(const tq_attn_params* p, int bk, int bv, int device) {
+  auto by_bv = [&](auto kb) -> int {
+    constexpr int BK = decltype(kb)::value;
+    switch (bv) {
+      case 2: return attn_resident_p<D, BK, 2, QJL>(p, device);
+      case 3: return attn_resident_p<D, BK, 3, QJL>(p, device);
+      default: return attn_resident_p<D, BK, 4, QJL>(p, device);
+    }
+  };
+  switch (bk) {
+    case 2: return by_bv(std::integral_constant<int, 2>{});
+    case 3: return by_bv(std::integral_constant<int, 3>{});
+    default: return by_bv(std::integral_constant<int, 4>{});
+  }
+}
+
 template <int D, int BK, int BV, int PAGE, bool QJL>
 static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
                                 const Rotation& rv, float* scores, bool scores_only, const AttnLayout& lay,
@@ -1169,7 +1253,7 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   a.window = p->window;
   {
     const int64_t waves = (int64_t)lay.splits * kAttnWaves * p->num_kv_heads * B;
-    const int64_t resident = (int64_t)attn_wpe(D, BK, BV, QJL, PAGE != kDense) * 4 * device_cu_count(rk.device);
+    const int64_t resident = (int64_t)attn_resident_waves_t<D, BK, BV, PAGE, QJL>(rk.device) * device_cu_count(rk.device);
     a.one_round = waves <= resident ? 1 : 0;
   }
   a.scale = p->scale;
@@ -1204,7 +1288,7 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
     w.Hq = Hq;
     w.Hkv = p->num_kv_heads;
     w.G = a.G;
-    w.slot = a.s_eff;
+    w.slot = lay.splits;
     w.scale = p->scale;
     const dim3 wg((unsigned)p->num_kv_heads, (unsigned)B);
     if (p->window_dtype == TQ_F32)
@@ -1218,15 +1302,15 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   const int64_t rs = (int64_t)(rv.f32_stride / sizeof(float));
   switch (p->out_dtype) {
     case TQ_F32:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_F32>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, a.s_eff, has_win, B, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F32>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, lay.splits, has_win, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
       break;
     case TQ_BF16:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_BF16>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, a.s_eff, has_win, B, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_BF16>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, lay.splits, has_win, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
       break;
     default:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_F16>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, a.s_eff, has_win, B, Hq,
+      hipLaunchKernelGGL((merge_kernel<D, TQ_F16>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, lay.splits, has_win, B, Hq,
                          p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
   }
   return hipGetLastError();

@@ -15,4 +15,12 @@ hipError_t launch_attention_qjl(const tq_attn_params* p, const Codebook& ck, con
   }
 }
 
+int attn_resident_waves_qjl(const tq_attn_params* p, int d, int bk, int bv, int device) {
+  switch (d) {
+    case 64: return attn_resident<64, true>(p, bk, bv, device);
+    case 128: return attn_resident<128, true>(p, bk, bv, device);
+    default: return attn_resident<256, true>(p, bk, bv, device);
+  }
+}
+
 }  // namespace tq

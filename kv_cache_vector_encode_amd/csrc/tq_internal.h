@@ -169,6 +169,9 @@ struct AttnLayout {
   size_t total;
 };
 AttnLayout attn_workspace_layout(const tq_attn_params* p, int d, int num_cu);
+// Resident waves per CU of the fused-attention kernel for these parameters (plain / QJL keys).
+int attn_resident_waves(const tq_attn_params* p, int d, int bk, int bv, int device);
+int attn_resident_waves_qjl(const tq_attn_params* p, int d, int bk, int bv, int device);
 hipError_t launch_attention(const tq_attn_params* p, const Codebook& ck, const Codebook& cv,
                             const Rotation& rk, const Rotation& rv, float* scores_out,
                             bool scores_only, const AttnLayout& lay, hipStream_t stream);

@@ -71,7 +71,7 @@ def test_noalloc_refuses_oversized_calls():
     c = _case(dev, 2, 16, 4, 64, 128, 4, 2, 2)
     out = torch.empty(2, 16, 128, dtype=torch.float32, device=dev)
     p = tq._params(c["ck"], c["rk"], c["q"], c["kp"], c["kn"], c["cv"], c["rv"], c["vp"], c["vn"], out=out)
-    p.num_splits = 4096          # 4 x 4096 partials x 2 x 16 heads x 130 floats: ~136 MB > 32 MiB
+    p.num_splits = 4096          # 4096 partials x 2 x 16 heads x 130 floats: ~68 MB > 32 MiB
     assert tq.attn_workspace_size(p) > 32 << 20
     st = _lib.lib().tq_attn_decode_noalloc(C.byref(p), C.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == -5 and "static scratch holds" in _lib.last_error()
