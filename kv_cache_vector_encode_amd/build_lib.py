@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 SOURCES = ["host.cpp", "encode.hip", "decode.hip", "attention.hip", "attention_qjl.hip", "window.hip",
-           "groupquant.hip", "qjl.hip"]
+           "groupquant.hip", "qjl.hip", "wht.hip"]
 
 
 def hipcc() -> str:

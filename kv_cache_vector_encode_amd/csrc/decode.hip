@@ -346,6 +346,7 @@ static hipError_t dec_bits(const DecodeLaunch& L) {
 }
 
 hipError_t launch_decode(const DecodeLaunch& L) {
+  if (L.rot->hadamard) return launch_decode_wht(L);
   switch (L.rot->d) {
     case 64: return dec_bits<64>(L);
     case 128: return dec_bits<128>(L);

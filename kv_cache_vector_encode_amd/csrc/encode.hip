@@ -391,6 +391,7 @@ static hipError_t dispatch_bits(const EncodeLaunch& L) {
 }
 
 hipError_t launch_encode(const EncodeLaunch& L) {
+  if (L.rot->hadamard) return launch_encode_wht(L);
   switch (L.rot->d) {
     case 64: return dispatch_bits<64>(L);
     case 128: return dispatch_bits<128>(L);

@@ -572,10 +572,11 @@ int tq_codebook_dims(const tq_codebook_t* cb, int* d, int* bits) {
 
 void tq_codebook_free(tq_codebook_t* cb) { delete cb; }
 
-static tq_rotation_t* make_rotation(int d, int n_rot, std::vector<double>&& pi) {
+static tq_rotation_t* make_rotation(int d, int n_rot, std::vector<double>&& pi, bool hadamard = false) {
   tq_rotation_t* h = new tq_rotation_t;
   h->rot.d = d;
   h->rot.n_rot = n_rot;
+  h->rot.hadamard = hadamard;
   h->rot.pi = std::move(pi);
   if (upload_rotation(h->rot) != TQ_OK) {
     delete h;
@@ -671,7 +672,7 @@ tq_rotation_t* tq_rotation_hadamard(int d, int n_rot, const int8_t* signs) {
         const double sj = signs ? (double)signs[(size_t)r * d + j] : 1.0;
         pi[(size_t)r * dd + (size_t)i * d + j] = h * sj;
       }
-  return make_rotation(d, n_rot, std::move(pi));
+  return make_rotation(d, n_rot, std::move(pi), true);
 }
 
 int tq_rotation_get(const tq_rotation_t* rot, double* pi) {

@@ -24,6 +24,7 @@ struct Codebook {
 // Rotation stack: float64 host copy and device operand tiles.
 struct Rotation {
   int d = 0, n_rot = 0, device = -1;
+  bool hadamard = false;         // Pi = H_d diag(s) / sqrt(d): encode / decode by the fast transform
   std::vector<double> pi;        // [n_rot, d, d] row-major
   // Device buffers (one allocation, offsets below), per rotation:
   //  enc_frag: bf16 MFMA A tiles of Pi (hi then lo), 4*d*d bytes
@@ -104,6 +105,7 @@ struct EncodeLaunch {
   hipStream_t stream;
 };
 hipError_t launch_encode(const EncodeLaunch& a);
+hipError_t launch_encode_wht(const EncodeLaunch& a);   // Hadamard rotations (fast transform)
 
 // QJL key encode: the MSE encode of `enc` (codebook at the MSE width, no norm correction) plus
 // the residual's sign sketch and norm.
@@ -159,6 +161,7 @@ struct DecodeLaunch {
   hipStream_t stream;
 };
 hipError_t launch_decode(const DecodeLaunch& a);
+hipError_t launch_decode_wht(const DecodeLaunch& a);   // Hadamard rotations (fast transform)
 
 // Attention / scores: workspace layout is computed by attn_workspace_layout.
 struct AttnLayout {
