@@ -150,7 +150,7 @@ tq_qjl_t* tq_qjl_create(const tq_rotation_t* rot, const float* sketch);
 void tq_qjl_free(tq_qjl_t* qjl);
 
 /* QJL encode of keys with qjl's rotation: packed / norms exactly as tq_encode with cb (the
- * MSE codebook, 2..4 bits, same d), plus (device, row j as in tq_encode)
+ * MSE codebook, 1..4 bits for keys of 2..5 bits, same d), plus (device, row j as in tq_encode)
  *   signs[j]:  d/8 bytes, bit i (LSB-first stream as the codes) = 1 iff (S_r r)_i >= 0;
  *   rnorms[j]: ||r||_2 as float32.
  * signs must be 16-byte aligned, rnorms 4-byte aligned; other arguments and errors as in
@@ -221,7 +221,7 @@ typedef struct {
   int32_t window_dtype;
   /* QJL keys (optional; KV Cache API page, TurboQuantCompressorV2.asymmetric_attention_scores):
    * with qjl_k != NULL the compressed keys were written by tq_qjl_encode with cb_k and qjl_k
-   * (built on rot_k), and every compressed score becomes
+   * (built on rot_k; cb_k may then have 1 bit, keys of 2 bits), and every compressed score becomes
    *   scale * (n_t <Pi_K q, c_K[idx_t]> + ||r_t|| sqrt(pi/2)/d <S q, signs_t>).
    * k_signs (d/8 bytes per token, 16-byte aligned base) and k_rnorms (float32) follow the
    * layout of k_packed / k_norms (dense or paged). qjl_k = NULL: plain MSE keys. */

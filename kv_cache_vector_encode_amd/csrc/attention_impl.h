@@ -1197,6 +1197,9 @@ static int attn_resident(const tq_attn_params* p, int bk, int bv, int device) {
     }
   };
   switch (bk) {
+    case 1:
+      if constexpr (QJL) return by_bv(std::integral_constant<int, 1>{});
+      return kAttnWaves;
     case 2: return by_bv(std::integral_constant<int, 2>{});
     case 3: return by_bv(std::integral_constant<int, 3>{});
     default: return by_bv(std::integral_constant<int, 4>{});
@@ -1341,6 +1344,10 @@ template <int D, bool QJL>
 static hipError_t attn_bk(const tq_attn_params* p, const Codebook& ck, const Codebook& cv, const Rotation& rk,
                           const Rotation& rv, float* scores, bool so, const AttnLayout& lay, hipStream_t st) {
   switch (ck.bits) {
+    case 1:
+      // 1-bit MSE codes only under the QJL sketch (keys of 2 bits); the host refuses the rest
+      if constexpr (QJL) return attn_bv<D, 1, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
+      return hipErrorInvalidValue;
     case 2: return attn_bv<D, 2, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
     case 3: return attn_bv<D, 3, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);
     default: return attn_bv<D, 4, QJL>(p, ck, cv, rk, rv, scores, so, lay, st);

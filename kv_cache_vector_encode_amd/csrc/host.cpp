@@ -823,9 +823,9 @@ int tq_qjl_encode(const tq_codebook_t* cb, const tq_qjl_t* qjl, int64_t vectors_
   if (!qjl) return fail(TQ_ERR_NULL, W + ": qjl is NULL");
   const Rotation& R = *qjl->q.rot;
   if (!cb) return fail(TQ_ERR_NULL, W + ": cb is NULL");
-  if (!gpu_bits_ok(cb->cb.bits))
+  if (cb->cb.bits < 1 || cb->cb.bits > 4)
     return fail(TQ_ERR_INVALID_ARG, W + ": codebook bits = " + std::to_string(cb->cb.bits) +
-                                        " is not supported on the GPU; accepted 2, 3, 4 (keys of 3..5 bits)");
+                                        " is not supported on the GPU; accepted 1..4 (keys of 2..5 bits)");
   if (cb->cb.d != R.d)
     return fail(TQ_ERR_INVALID_ARG, W + ": codebook d = " + std::to_string(cb->cb.d) + " does not match d = " +
                                         std::to_string(R.d));
@@ -907,8 +907,16 @@ int tq_decode(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors
 
 static int check_attn(const tq_attn_params* p, bool scores_only, const char* who) {
   if (!p) return fail(TQ_ERR_NULL, std::string(who) + ": params is NULL");
-  int s = check_pair(p->cb_k, p->rot_k, who);
-  if (s) return s;
+  int s;
+  if (p->qjl_k && p->cb_k && p->cb_k->cb.bits == 1) {
+    // QJL keys of 2 bits: a 1-bit MSE stage under the sign sketch
+    if (!p->rot_k) return fail(TQ_ERR_NULL, std::string(who) + ": rot_k is NULL");
+    if (p->cb_k->cb.d != p->rot_k->rot.d)
+      return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": codebook d = " + std::to_string(p->cb_k->cb.d) +
+                                          " does not match rotation d = " + std::to_string(p->rot_k->rot.d));
+  } else if ((s = check_pair(p->cb_k, p->rot_k, who))) {
+    return s;
+  }
   if (!scores_only) {
     if ((s = check_pair(p->cb_v, p->rot_v, who))) return s;
     if (p->rot_v->rot.d != p->rot_k->rot.d)

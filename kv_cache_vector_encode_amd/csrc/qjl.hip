@@ -365,6 +365,7 @@ static hipError_t qjl_in(const QjlEncodeLaunch& Q) {
 template <int D>
 static hipError_t qjl_bits(const QjlEncodeLaunch& Q) {
   switch (Q.enc.bits) {
+    case 1: return qjl_in<D, 1>(Q);
     case 2: return qjl_in<D, 2>(Q);
     case 3: return qjl_in<D, 3>(Q);
     default: return qjl_in<D, 4>(Q);

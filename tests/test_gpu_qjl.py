@@ -67,7 +67,7 @@ def _check_qjl_encode(x64, packed, norms, signs, rnorms, pi, S64, d, mbits, what
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("mbits", [2, 3, 4])
+@pytest.mark.parametrize("mbits", [1, 2, 3, 4])
 def test_qjl_encode(dev, d, mbits):
     n = 777                                    # several 32-vector tiles and a ragged tail
     log("case: qjl encode d%d mse bits %d" % (d, mbits))
@@ -146,7 +146,7 @@ def _oracle_keys(c, d, mbits):
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("mbits", [2, 3])
+@pytest.mark.parametrize("mbits", [1, 2, 3, 4])
 def test_qjl_scores(dev, d, mbits):
     B, Hq, Hkv, T = 3, 8, 2, 200
     log("case: qjl scores d%d mse bits %d" % (d, mbits))
@@ -206,6 +206,7 @@ def _check_qjl_attention(o, lse, q64, keys, vhat, pi, S64, cbo, scale, lens, wha
 
 
 @pytest.mark.parametrize("d,mbits,bv,Hq,Hkv", [(128, 3, 2, 32, 8), (128, 2, 3, 8, 8), (64, 2, 4, 16, 2),
+                                               (128, 1, 2, 32, 8), (64, 1, 3, 8, 2), (256, 1, 4, 8, 4),
                                                 (64, 3, 2, 16, 1), (256, 3, 3, 8, 2), (256, 2, 2, 4, 4)])
 def test_qjl_attention_dense(dev, d, mbits, bv, Hq, Hkv):
     B, T = 4, 333
@@ -277,8 +278,9 @@ def test_qjl_error_paths(dev):
     sk = tq.QJLSketch(rot, _sketches(d, [42]))
     cb1 = tq.Codebook(d, 1)
     x = torch.zeros(4, d, dtype=torch.bfloat16, device=dev)
+    # 1-bit codes are a QJL key's MSE stage only: the plain encode refuses them
     with pytest.raises(tq.TQError, match="not supported on the GPU"):
-        tq.qjl_encode(cb1, sk, x)
+        tq.encode(cb1, rot, x)
     cb64 = tq.Codebook(64, 2)
     with pytest.raises((ValueError, tq.TQError), match="does not match"):
         tq.qjl_encode(cb64, sk, x)
