@@ -50,20 +50,24 @@ struct EncodeKArgs {
 };
 
 
-template <int D, int BITS>
+template <int D, int BITS, int QS = 1>
 struct EncGeo {
   static constexpr int T = D / 32;                 // output tiles
   static constexpr int KB = D / 16;                // K blocks
   static constexpr int HALF = D / 2;               // coordinates per lane
+  static constexpr int TS = T / QS;                // output tiles per workgroup slice
   static constexpr int ROW = D * BITS / 8;         // packed bytes per vector
-  static constexpr int CHUNK = HALF * BITS / 8;    // packed bytes per lane
-  static constexpr int CHUNK_DW = CHUNK / 4;
-  static constexpr int G = (CHUNK % 16 == 0 && ROW % 16 == 0) ? 16 : ((CHUNK % 8 == 0 && ROW % 8 == 0) ? 8 : 4);
-  static constexpr int FRAG_U4 = 2 * T * KB * 64;  // hi and lo tiles, u32x4 per lane
-  static constexpr bool LDS = (D <= 128);
+  static constexpr int CHUNK = HALF * BITS / 8;    // packed bytes per lane (its half of the row)
+  static constexpr int CHUNK_S = CHUNK / QS;       // of those, the bytes of this slice
+  static constexpr int CHUNK_DW = CHUNK_S / 4;
+  static constexpr int G = (CHUNK_S % 16 == 0 && ROW % 16 == 0) ? 16 : ((CHUNK_S % 8 == 0 && ROW % 8 == 0) ? 8 : 4);
+  static constexpr int SET_U4 = TS * KB * 64;      // one slice's tiles of one pass, u32x4 per lane
+  static constexpr int FRAG_U4 = 2 * SET_U4;       // hi and lo tiles of the slice
+  static constexpr bool LDS = (D <= 128) || QS > 1;
   // Occupancy plan: at d <= 128, two 8-wave workgroups per CU (2 x 64 KiB of Pi tiles in LDS),
-  // i.e. 4 waves per SIMD within 128 VGPRs; d=256 reads Pi from L2 and needs up to 256 VGPRs,
-  // so one 8-wave workgroup (2 waves per SIMD).
+  // i.e. 4 waves per SIMD within 128 VGPRs; d=256 needs up to 256 VGPRs, so one 8-wave
+  // workgroup (2 waves per SIMD), holding half of Pi's output rows (128 KiB) when split in two
+  // slices, else reading Pi from L2.
   static constexpr int WG_PER_CU = D == 256 ? 1 : 2;
 };
 // Byte B of `word` = (byte 3 of lo) | (byte 3 of hi) << 4; for B > 0 the other bytes are kept,
@@ -95,12 +99,16 @@ constexpr int enc_waves() { return 8; }
 template <int D, int IN>
 constexpr int enc_wpe() { return D == 256 ? 2 : 4; }
 
-template <int D, int BITS, int IN, bool SLOT>
+// QS > 1 (d = 256): QS workgroups share each group of vectors, each computing the output tiles of
+// one slice of the coordinates with that slice's rows of Pi in LDS (the dense Pi, 256 KiB as hi +
+// lo, does not fit). The QS workgroups of a group are numbered 8 apart, which places them on one
+// XCD, so the repeated reads of each input row hit that XCD's L2. The slice q = 0 stores the norm.
+template <int D, int BITS, int IN, bool SLOT, int QS>
 __global__ void __launch_bounds__((enc_waves<D, IN>() * 64))
 __attribute__((amdgpu_waves_per_eu(enc_wpe<D, IN>())))
 encode_kernel(EncodeKArgs a) {
-  using Geo = EncGeo<D, BITS>;
-  constexpr int T = Geo::T, KB = Geo::KB, HALF = Geo::HALF;
+  using Geo = EncGeo<D, BITS, QS>;
+  constexpr int T = Geo::TS, KB = Geo::KB, HALF = Geo::HALF;
   constexpr bool SPLIT_X = (IN != TQ_BF16);
   constexpr int WAVES = enc_waves<D, IN>();
   extern __shared__ u32x4 smem[];
@@ -108,6 +116,11 @@ encode_kernel(EncodeKArgs a) {
   __shared__ float csq[kMaxLevels];
 
   const int r = blockIdx.y;
+  // slice q and vector-group slot of this workgroup (the slices of one slot are 8 apart)
+  const int wg = blockIdx.x;
+  const int q = QS == 1 ? 0 : (wg >> 3) % QS;
+  const int slot_id = QS == 1 ? wg : (wg & 7) + 8 * (wg / (8 * QS));
+  const int nslots = gridDim.x / QS;
   const u32x4* gfrag = a.frag + (int64_t)r * a.frag_stride;
 
   const int64_t v_begin = a.vpr ? (int64_t)r * a.vpr : 0;
@@ -127,7 +140,7 @@ encode_kernel(EncodeKArgs a) {
   constexpr int NRAW = HALF * ELEM / 16;
   constexpr int PER = ELEM / 2;          // 16-byte loads per K block
   constexpr bool PREFETCH = (IN == TQ_BF16);
-  const int64_t wstride = (int64_t)gridDim.x * WAVES;
+  const int64_t wstride = (int64_t)nslots * WAVES;
   // loads tile tl's inputs and returns the packed row its codes go to (-1: none)
   auto fetch = [&](int64_t tl, u32x4 (&raw)[NRAW]) -> int64_t {
     const int64_t v = v_begin + tl * 32 + vl;
@@ -143,14 +156,18 @@ encode_kernel(EncodeKArgs a) {
       return ok ? v : -1;
     }
   };
-  int64_t tile = (int64_t)blockIdx.x * WAVES + wave;
+  int64_t tile = (int64_t)slot_id * WAVES + wave;
   u32x4 xr[NRAW];
   int64_t rown = -1;
   // the first tile's loads are issued before the table copies below, so the two latencies overlap
   if (PREFETCH) rown = fetch(tile, xr);
 
   if constexpr (Geo::LDS) {
-    for (int i = threadIdx.x; i < Geo::FRAG_U4; i += blockDim.x) smem[i] = gfrag[i];
+    // the slice's tiles of each pass: tiles (pass, t, kb) are stored pass-major, then t, then kb
+    for (int i = threadIdx.x; i < Geo::FRAG_U4; i += blockDim.x) {
+      const int pass = i / Geo::SET_U4, k = i - pass * Geo::SET_U4;
+      smem[i] = gfrag[(pass * QS + q) * Geo::SET_U4 + k];
+    }
   }
   {
     // read the table straight from the kernel-argument segment (the only argument is `a`, at
@@ -289,29 +306,31 @@ encode_kernel(EncodeKArgs a) {
     //      the input's length): store n / ||c[idx]||, ||c[idx]||^2 summed over this lane's codes
     //      and the other half of the vector
     float nst = nrm;
-    if (a.norm_correct) {
-      float cs0 = 0.f, cs1 = 0.f;
+    if constexpr (QS == 1) {
+      if (a.norm_correct) {
+        float cs0 = 0.f, cs1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < HALF; ++j) {
-        const int pos = j * BITS;
-        uint32_t code = pk[pos >> 5] >> (pos & 31);
-        if ((pos & 31) + BITS > 32) code |= pk[(pos >> 5) + 1] << (32 - (pos & 31));
-        const float c2 = csq[code & ((1u << BITS) - 1u)];
-        if (j & 1)
-          cs1 += c2;
-        else
-          cs0 += c2;
+        for (int j = 0; j < HALF; ++j) {
+          const int pos = j * BITS;
+          uint32_t code = pk[pos >> 5] >> (pos & 31);
+          if ((pos & 31) + BITS > 32) code |= pk[(pos >> 5) + 1] << (32 - (pos & 31));
+          const float c2 = csq[code & ((1u << BITS) - 1u)];
+          if (j & 1)
+            cs1 += c2;
+          else
+            cs0 += c2;
+        }
+        float cs = cs0 + cs1;
+        cs += wave_xor(cs, 32);
+        nst = nrm / sqrtf(cs);
       }
-      float cs = cs0 + cs1;
-      cs += wave_xor(cs, 32);
-      nst = nrm / sqrtf(cs);
     }
 
     // ---- store
     {
       const bool ok = row >= 0;
-      uint8_t* dst = ok ? a.packed + row * Geo::ROW + hh * Geo::CHUNK : a.sink + 64 * lane;
-      float* np = ok && hh == 0 ? a.norms + row : (float*)(a.sink + 4096) + lane;
+      uint8_t* dst = ok ? a.packed + row * Geo::ROW + hh * Geo::CHUNK + q * Geo::CHUNK_S : a.sink + 64 * lane;
+      float* np = ok && hh == 0 && q == 0 ? a.norms + row : (float*)(a.sink + 4096) + lane;
       if constexpr (Geo::G == 16) {
 #pragma unroll
         for (int w = 0; w < Geo::CHUNK_DW; w += 4)
@@ -328,9 +347,9 @@ encode_kernel(EncodeKArgs a) {
   }
 }
 
-template <int D, int BITS, int IN, bool SLOT>
+template <int D, int BITS, int IN, bool SLOT, int QS>
 static hipError_t launch_encode_t(const EncodeLaunch& L) {
-  using Geo = EncGeo<D, BITS>;
+  using Geo = EncGeo<D, BITS, QS>;
   EncodeKArgs k;
   k.frag = (const u32x4*)L.rot->enc(0);
   k.frag_stride = (int64_t)(L.rot->enc_stride / sizeof(u32x4));
@@ -352,24 +371,31 @@ static hipError_t launch_encode_t(const EncodeLaunch& L) {
   const int64_t tiles = (per_rot + 31) / 32;
   const size_t lds = Geo::LDS ? Geo::FRAG_U4 * sizeof(u32x4) : 0;
   if (lds > 0) {
-    hipError_t e = set_kernel_lds((const void*)encode_kernel<D, BITS, IN, SLOT>, L.rot->device, lds);
+    hipError_t e = set_kernel_lds((const void*)encode_kernel<D, BITS, IN, SLOT, QS>, L.rot->device, lds);
     if (e != hipSuccess) return e;
   }
   constexpr int WAVES = enc_waves<D, IN>();
   const int cu = device_cu_count(L.rot->device);
   const int64_t want = (int64_t)cu * Geo::WG_PER_CU;
-  int64_t bx = (want + nrot - 1) / nrot;
+  int64_t slots = (want / QS + nrot - 1) / nrot;
   const int64_t need = (tiles + WAVES - 1) / WAVES;
-  if (bx > need) bx = need;
-  if (bx < 1) bx = 1;
-  dim3 grid((unsigned)bx, (unsigned)nrot);
-  hipLaunchKernelGGL((encode_kernel<D, BITS, IN, SLOT>), grid, dim3(WAVES * 64), lds, L.stream, k);
+  if (slots > need) slots = need;
+  if (slots < 1) slots = 1;
+  if (QS > 1) slots = (slots + 7) / 8 * 8;   // whole groups of 8 slots: a slot's slices share an XCD
+  dim3 grid((unsigned)(slots * QS), (unsigned)nrot);
+  hipLaunchKernelGGL((encode_kernel<D, BITS, IN, SLOT, QS>), grid, dim3(WAVES * 64), lds, L.stream, k);
   return hipGetLastError();
 }
 
 template <int D, int BITS, int IN>
 static hipError_t dispatch_slot(const EncodeLaunch& L) {
-  return L.slot_mapping ? launch_encode_t<D, BITS, IN, true>(L) : launch_encode_t<D, BITS, IN, false>(L);
+  // d = 256: two slices with Pi's rows in LDS, except for the norm correction, which needs the
+  // code energies of the whole vector in one workgroup
+  if constexpr (D == 256) {
+    if (!L.norm_correct)
+      return L.slot_mapping ? launch_encode_t<D, BITS, IN, true, 2>(L) : launch_encode_t<D, BITS, IN, false, 2>(L);
+  }
+  return L.slot_mapping ? launch_encode_t<D, BITS, IN, true, 1>(L) : launch_encode_t<D, BITS, IN, false, 1>(L);
 }
 
 template <int D, int BITS>
