@@ -401,6 +401,37 @@ def next_rows(tq, ti, torch, dev, K, V, kp, kn, vp, vn, rot, ck, cv, q, kp4, kn4
     return out
 
 
+def hadamard_fast_transform(tq, ti, torch, dev, reps: int = 10):
+    """A Hadamard rotation encodes and decodes by the fast Walsh-Hadamard transform (no
+    MFMA), a Haar rotation by the dense MFMA kernels; 1,048,576 bf16 vectors at 3 bits (the 70B-class
+    layer's keys at d=128, the same byte count at d=256), each call streaming from HBM."""
+    res = {}
+    for d in (128, 256):
+        n = 1048576
+        x = torch.randn(n, d, generator=ti.generator(dev, 77 + d), device=dev).to(torch.bfloat16)
+        cb = tq.Codebook(d, 3)
+        rots = {"haar_mfma": tq.Rotation.from_gaussian(ti.rotation_gaussian(d, 42)),
+                "hadamard_fwht": tq.Rotation.hadamard(d, ti.random_signs(1, d, 5))}
+        pk = torch.empty(n, d * 3 // 8, dtype=torch.uint8, device=dev)
+        nm = torch.empty(n, device=dev)
+        out = torch.empty(n, d, dtype=torch.bfloat16, device=dev)
+        alg = n * (d * 2 + d * 3 // 8 + 4)
+        rec = {}
+        for name, rot in rots.items():
+            ms_e = _time(torch, lambda: tq.encode(cb, rot, x, packed=pk, norms=nm), reps)
+            ms_d = _time(torch, lambda: tq.decode(cb, rot, pk, nm, out=out), reps)
+            rec[name] = {"encode_ms": round(ms_e, 4), "encode_hbm_frac": _frac(alg, ms_e),
+                         "decode_ms": round(ms_d, 4), "decode_hbm_frac": _frac(alg, ms_d)}
+            if name == "haar_mfma":
+                rec[name]["encode_mfma_TFLOPs"] = round(n * 2 * 2 * d * d / (ms_e * 1e-3) / 1e12, 1)
+                rec[name]["decode_mfma_TFLOPs"] = round(n * 3 * 2 * d * d / (ms_d * 1e-3) / 1e12, 1)
+        res["d%d" % d] = rec
+        del x, pk, nm, out
+        torch.cuda.empty_cache()
+    res["workload"] = "1,048,576 bf16 N(0,1) vectors, 3 bits, per d; Haar (dense MFMA) vs Hadamard (fast transform)"
+    return res
+
+
 def decode_attention_32k(tq, ti, torch, dev, reps: int = 10):
     """Fused decode attention over a long context: batch 32, 32 query heads over 8 KV heads, 32768
     tokens, d=128, K4/V2 (random code bytes with log-normal norms, as in the parity test of this
@@ -630,6 +661,9 @@ def main():
         extra["paged_ragged"] = paged_ragged(tq, ti, torch, dev)
         show("paged_ragged", extra["paged_ragged"])
         extra["codec_check_4096"] = codec_check_latency(tq, ti, torch, dev)
+        if nxt is not None:
+            nxt["hadamard_fast_transform"] = hadamard_fast_transform(tq, ti, torch, dev)
+            show("hadamard_fast_transform", nxt["hadamard_fast_transform"])
         extra["next_rows"] = nxt
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
