@@ -58,18 +58,27 @@ def unpack_signs(packed, d: int):
     return np.where(codec.unpack_codes(packed, 1, d) > 0, 1, -1).astype(np.int8)
 
 
-def scores(q, codes, norms, signs, rnorms, pi, S, centroids_mse, scale: float):
-    """s[i, t] = scale * (<q_i, k_mse_t> + ||r_t|| sqrt(pi/2)/m <S q_i, signs_t>).
-    q [Q, d]; per-key arrays over T keys. Returns [Q, T]."""
-    q = np.asarray(q, dtype=np.float64)
+def key_estimate(codes, norms, signs, rnorms, pi, S, centroids_mse):
+    """Each key as the estimator sees it, [T, d]: the MSE reconstruction n_t (c[idx_t] Pi) plus
+    the sketch's reconstruction of the residual, ||r_t|| sqrt(pi/2) / rows * S^T z_t, where z_t
+    are the stored signs and rows is the number of sketch rows. The page's estimator
+    <q, k_mse> + ||r|| sqrt(pi/2)/rows <S q, z> is the inner product of q with this vector
+    (<S q, z> = <q, S^T z>)."""
     S = np.asarray(S, dtype=np.float64)
+    rows = S.shape[0]
     c = np.asarray(centroids_mse, dtype=np.float64)
-    chat = c[np.asarray(codes).astype(np.int64)]
-    k_mse = (chat @ np.asarray(pi, dtype=np.float64)) * np.asarray(norms, dtype=np.float64)[:, None]
-    m = S.shape[0]
-    term1 = q @ k_mse.T
-    term2 = (q @ S.T) @ np.asarray(signs, dtype=np.float64).T
-    return scale * (term1 + math.sqrt(math.pi / 2) / m * term2 * np.asarray(rnorms, dtype=np.float64)[None, :])
+    recon = (c[np.asarray(codes).astype(np.int64)] @ np.asarray(pi, dtype=np.float64))
+    recon *= np.asarray(norms, dtype=np.float64)[:, None]
+    z = np.asarray(signs, dtype=np.float64)
+    gain = np.asarray(rnorms, dtype=np.float64) * (math.sqrt(math.pi / 2) / rows)
+    return recon + gain[:, None] * (z @ S)
+
+
+def scores(q, codes, norms, signs, rnorms, pi, S, centroids_mse, scale: float):
+    """s[i, t] = scale * <q_i, key_estimate_t> = scale * (<q_i, k_mse_t> + ||r_t|| sqrt(pi/2)/m
+    <S q_i, signs_t>), m sketch rows. q [Q, d]; per-key arrays over T keys. Returns [Q, T]."""
+    q = np.asarray(q, dtype=np.float64)
+    return scale * (q @ key_estimate(codes, norms, signs, rnorms, pi, S, centroids_mse).T)
 
 
 def cache_scores(q, codes, norms, signs, rnorms, pi, S, centroids_mse, scale: float, seq_lens=None):

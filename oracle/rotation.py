@@ -68,9 +68,9 @@ def hadamard_matrix(d: int):
 def hadamard_rotation(d: int, signs=None):
     """Hadamard rotation: Pi = H_d diag(s) / sqrt(d), s in {+1, -1}^d (all +1 if None).
 
-    Turbo Attention PyPI page, "The codec" table, "Hadamard rotation" row: a Walsh-Hadamard
-    transform spreads outlier channels across the vector and queries are rotated the same
-    way. Reading: the orthonormal Sylvester-ordered transform, optionally preceded by a sign
+    Turbo Attention PyPI page, "The codec" table, "Hadamard rotation" row: the rotation is a
+    Walsh-Hadamard transform, whose purpose there is to smear large channels over all
+    coordinates; the query side uses it too. Reading: the orthonormal Sylvester-ordered transform, optionally preceded by a sign
     flip per input channel (a randomized Hadamard transform when the signs are drawn at
     random); y = Pi x means y = H (s * x) / sqrt(d).
     """
