@@ -4,8 +4,8 @@
 // Method: s_t = scale <q, k_hat_t> (KV Cache API page, ginkgoq.github.io/TurboQuant/api/kv,
 // TurboQuantKVCache.attention_scores) and o = softmax(s) v_hat (TurboQuantKVCache.attend).
 // Because k_hat_t = n_t Pi_K^T c_K[idx_t], <q, k_hat_t> = n_t <Pi_K q, c_K[idx_t]>: the query is
-// rotated once and keys are never un-rotated (Turbo Attention PyPI page, "The codec": queries
-// rotated the same way, so scores need no un-rotation). Likewise sum_t p_t v_hat_t =
+// rotated once and keys are never un-rotated (Turbo Attention PyPI page, "The codec", which
+// applies the key rotation to the queries as well). Likewise sum_t p_t v_hat_t =
 // Pi_V^T sum_t p_t n^v_t c_V[idx^v_t]: values are accumulated in the rotated domain and
 // rotated back once per (sequence, head). Split-K over tokens with an online softmax and a
 // log-sum-exp merge plays the role of the pages' split-K paged decode kernel (same page,
@@ -151,9 +151,6 @@ __device__ __forceinline__ uint32_t lds_word(const uint32_t* t, uint32_t off) {
   return *(const uint32_t*)((const char*)t + off);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
 
 // PB bits at bit `pos` of w (pos is a compile-time constant after unrolling)
 template <int PB, int NW>

@@ -20,6 +20,17 @@
 // ~1.2e-7 of the vector norm per element. The A1 = 2^11 P_hi operand is read once for two
 // products, so LDS reads grow by half a tile set per product, not by two.
 //
+// Instruction budget. On gfx950 the vector ALU and LDS instructions of a SIMD issue largely
+// in series with its MFMAs (a probe that gives each wave independent fp32 FMAs next to its
+// MFMA chains runs in nearly the sum of the two times), so everything around the MFMAs is
+// kept to few instructions: the code -> operand tables return each 32-bit operand word
+// straight into its MFMA register (hi and lo tables, one LDS read per word, no moves), a
+// code pair's table offset is two ALU operations, the staging area is padded rather than
+// swizzled so that every LDS address is a per-lane base plus a constant, and without a slot
+// gather the packed rows are read, and every output row is written, through buffer
+// resources over the tile's rows: a lane's address is a 32-bit offset from a uniform base,
+// and rows past the end read as zero or are dropped by the hardware's range check.
+//
 // Head size 256: the two tile sets of the whole Pi^T (256 KiB) do not fit in LDS, so four
 // workgroups share each group of vectors, each holding the tiles of one quarter of the output
 // coordinates (64 KiB) and writing that quarter of every row. The four are numbered 8 apart,
@@ -37,8 +48,7 @@ struct DecodeKArgs {
   const float* norms;
   const int64_t* slot;
   void* out;
-  const uint8_t* zero;   // zeros that masked lanes load (>= one packed chunk)
-  uint8_t* sink;         // where masked lanes store (>= 64 lanes x 16 bytes)
+  const uint8_t* zero;   // zeros that masked lanes load with a slot gather (>= one packed chunk)
   int64_t n, vpr;
   uint32_t chi[8];       // 2^8 c_hi as fp16, two per word
   uint32_t clo[8];       // 2^8 c_lo as fp16, two per word
@@ -57,20 +67,31 @@ struct DecGeo {
   static constexpr int E = OUT == TQ_F32 ? 4 : 2;  // output bytes per element
   static constexpr int SET_U4 = TS * KB * 64;       // one tile set of a slice, in u32x4
   static constexpr int FRAG_U4 = 2 * SET_U4;        // A1 and A2
-  // Code -> centroid tables: 2-bit codes go four at a time (one byte -> four fp16 hi, four
-  // fp16 lo), 3- and 4-bit codes two at a time (6 or 8 bits -> two hi, two lo).
+  // Code -> centroid tables, a hi table and a lo table: 2-bit codes go four at a time (one
+  // byte -> four fp16, two words per entry), 3- and 4-bit codes two at a time (6 or 8 bits ->
+  // two fp16, one word per entry).
   static constexpr int PER_LOOKUP = BITS == 2 ? 4 : 2;
-  static constexpr int TAB_N = 1 << (PER_LOOKUP * BITS);
-  static constexpr int TAB_WORDS = TAB_N * PER_LOOKUP;   // hi and lo words per entry
+  static constexpr int LOOKUP_BITS = PER_LOOKUP * BITS;
+  static constexpr int TAB_N = 1 << LOOKUP_BITS;
+  static constexpr int ENTRY_B = PER_LOOKUP * 2;            // bytes per entry (fp16 each)
+  static constexpr int TAB_B = TAB_N * ENTRY_B;             // bytes per table
+  // the lo table starts LO_OFF bytes after the hi one: further apart than one two-address LDS
+  // read reaches and not a multiple of its stride, so each word is read into its own register
+  static constexpr int LO_OFF = (TAB_B > 2048 ? TAB_B : 2048) + 8;
   // Launch shape. The decode is bound by its output stores, and HBM write throughput falls
   // when many waves keep stores in flight, so every head size runs 8 waves per CU: d = 64 in
   // two 4-wave workgroups, d = 128 and 256 in one 8-wave workgroup (the tile sets take
   // 64 KiB); float32 outputs at d = 128 stage twice the bytes, so 4 waves there.
   static constexpr int WAVES = D == 64 ? 4 : ((D == 128 && OUT == TQ_F32) ? 4 : 8);
   static constexpr int WG_PER_CU = D == 64 ? 2 : 1;
-  static constexpr size_t stage_bytes = (size_t)32 * SC * E;   // per wave
+  // staging: 32 rows of the slice's SB bytes, each padded by 16 bytes so that rows written by
+  // consecutive lanes start in different banks
+  static constexpr int SB = SC * E;
+  static constexpr int STG_ROW = SB + 16;
+  static constexpr size_t stage_bytes = (size_t)32 * STG_ROW;
   static constexpr size_t lds_bytes = (size_t)FRAG_U4 * 16 + (size_t)WAVES * stage_bytes;
-  static_assert(lds_bytes + TAB_WORDS * 4 <= 160 * 1024, "decode LDS budget");
+  static_assert(lds_bytes + LO_OFF + TAB_B <= 160 * 1024, "decode LDS budget");
+  static_assert(1024 % SB == 0, "a 1 KiB store covers whole staged rows");
 };
 
 // 8 waves per CU are 2 per SIMD: up to 256 registers per wave
@@ -82,10 +103,11 @@ __global__ void __launch_bounds__((DecGeo<D, BITS, OUT>::WAVES * 64))
 __attribute__((amdgpu_waves_per_eu(dec_wpe<D, BITS, OUT>())))
 decode_kernel(DecodeKArgs a) {
   using Geo = DecGeo<D, BITS, OUT>;
-  constexpr int TS = Geo::TS, KB = Geo::KB, QS = Geo::QS, WAVES = Geo::WAVES, E = Geo::E;
+  constexpr int TS = Geo::TS, KB = Geo::KB, QS = Geo::QS, WAVES = Geo::WAVES, E = Geo::E, DW = Geo::CHUNK_DW;
   constexpr uint32_t MASK = (1u << BITS) - 1u;
   extern __shared__ u32x4 smem[];
-  __shared__ __attribute__((aligned(16))) uint32_t tab[Geo::TAB_WORDS];   // read 8 or 16 bytes at a time
+  // hi table at 0, lo table at LO_OFF (TAB_B bytes each)
+  __shared__ __attribute__((aligned(16))) uint32_t tab[(Geo::LO_OFF + Geo::TAB_B) / 4];
 
   const int r = blockIdx.y;
   // slice q and vector-group slot of this workgroup (slices of one slot are 8 apart)
@@ -99,52 +121,85 @@ decode_kernel(DecodeKArgs a) {
   const int64_t v_end = a.vpr ? min(a.n, v_begin + a.vpr) : a.n;
   const int64_t ntile = (v_end - v_begin + 31) / 32;
   if (ntile <= 0) return;   // uniform per workgroup: no thread is left at the barrier below
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index through readfirstlane, so that tile indices and the buffer resources built
+  // from them stay uniform (scalar registers)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int vl = lane & 31, hh = lane >> 5;
   uint8_t* stg = (uint8_t*)(smem + Geo::FRAG_U4) + wave * Geo::stage_bytes;
 
-  // Two-stage prefetch: the packed row of the next tile is loaded while this tile is decoded,
-  // and with a slot gather the slot index is read one tile earlier still. Every load and store
-  // is issued unconditionally (masked lanes read the zero page and write the sink): the memory
-  // counter is in order, and a branch around an access would make the wait for a prefetched
-  // load also wait for the stores issued after it.
+  // rows of tile tl that exist (0 past the end), uniform
+  auto valid_rows = [&](int64_t tl) -> uint32_t {
+    const int64_t left = v_end - (v_begin + tl * 32);
+    return left <= 0 ? 0u : (left >= 32 ? 32u : (uint32_t)left);
+  };
+  // Prefetch one tile ahead (and with a slot gather, the slot index one tile earlier still).
   const int64_t wstride = (int64_t)nslots * WAVES;
-  auto row_of = [&](int64_t tl) -> int64_t {
-    const int64_t v = v_begin + tl * 32 + vl;
-    const bool ok = tl < ntile && v < v_end;
+  auto slot_row = [&](int64_t tl) -> int64_t {
     if constexpr (SLOT) {
+      const int64_t v = v_begin + tl * 32 + vl;
+      const bool ok = tl < ntile && v < v_end;
       const int64_t s = a.slot[ok ? v : v_begin];
       return ok ? s : -1;
     } else {
-      return ok ? v : -1;
+      (void)tl;
+      return 0;
     }
   };
-  auto fetch = [&](int64_t row, uint32_t (&cw)[Geo::CHUNK_DW], float& nrm) {
-    const uint8_t* src = row >= 0 ? a.packed + row * Geo::ROW + hh * Geo::CHUNK : a.zero;
-    if constexpr (Geo::G == 16) {
+  auto fetch = [&](int64_t tl, int64_t srow, uint32_t (&cw)[DW], float& nrm) {
+    if constexpr (SLOT) {
+      const uint8_t* src = srow >= 0 ? a.packed + srow * Geo::ROW + hh * Geo::CHUNK : a.zero;
+      if constexpr (Geo::G == 16) {
 #pragma unroll
-      for (int w = 0; w < Geo::CHUNK_DW; w += 4) {
-        u32x4 v = *(const u32x4*)(src + 4 * w);
-        cw[w] = v[0]; cw[w + 1] = v[1]; cw[w + 2] = v[2]; cw[w + 3] = v[3];
-      }
-    } else if constexpr (Geo::G == 8) {
+        for (int w = 0; w < DW; w += 4) {
+          const u32x4 v = *(const u32x4*)(src + 4 * w);
+          cw[w] = v[0]; cw[w + 1] = v[1]; cw[w + 2] = v[2]; cw[w + 3] = v[3];
+        }
+      } else if constexpr (Geo::G == 8) {
 #pragma unroll
-      for (int w = 0; w < Geo::CHUNK_DW; w += 2) {
-        u32x2 v = *(const u32x2*)(src + 4 * w);
-        cw[w] = v[0]; cw[w + 1] = v[1];
+        for (int w = 0; w < DW; w += 2) {
+          const u32x2 v = *(const u32x2*)(src + 4 * w);
+          cw[w] = v[0]; cw[w + 1] = v[1];
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < DW; ++w) cw[w] = *(const uint32_t*)(src + 4 * w);
       }
+      nrm = *(srow >= 0 ? a.norms + srow : (const float*)a.zero);
     } else {
+      (void)srow;
+      // the tile's rows through a buffer resource: rows past the end read as zero
+      const int64_t vb = v_begin + tl * 32;
+      const uint32_t nv = valid_rows(tl);
+      const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(a.packed + (nv ? vb : 0) * Geo::ROW, nv * Geo::ROW);
+      const __amdgpu_buffer_rsrc_t rn = buffer_rsrc(a.norms + (nv ? vb : 0), nv * 4u);
+      const uint32_t off = (uint32_t)(vl * Geo::ROW + hh * Geo::CHUNK);
+      if constexpr (Geo::G == 16) {
 #pragma unroll
-      for (int w = 0; w < Geo::CHUNK_DW; ++w) cw[w] = *(const uint32_t*)(src + 4 * w);
+        for (int w = 0; w < DW; w += 4) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rp, off + 4 * w, 0, 0);
+          cw[w] = v[0]; cw[w + 1] = v[1]; cw[w + 2] = v[2]; cw[w + 3] = v[3];
+        }
+      } else if constexpr (Geo::G == 8) {
+#pragma unroll
+        for (int w = 0; w < DW; w += 2) {
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rp, off + 4 * w, 0, 0);
+          cw[w] = v[0]; cw[w + 1] = v[1];
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < DW; ++w) cw[w] = __builtin_amdgcn_raw_buffer_load_b32(rp, off + 4 * w, 0, 0);
+      }
+      nrm = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, (uint32_t)vl * 4u, 0, 0));
     }
-    nrm = *(row >= 0 ? a.norms + row : (const float*)a.zero);
   };
+
   int64_t tile = (int64_t)slot_id * WAVES + wave;
-  uint32_t cwn[Geo::CHUNK_DW];
-  float nrmn;
+  uint32_t cwA[DW], cwB[DW];
+  float nA, nB;
+  int64_t sA = slot_row(tile), sB = 0;
   // the first tile's loads are issued before the table copies below, so the two latencies overlap
-  fetch(row_of(tile), cwn, nrmn);
-  int64_t row_nn = row_of(tile + wstride);
+  fetch(tile, sA, cwA, nA);
+  sB = slot_row(tile + wstride);
 
   for (int i = threadIdx.x; i < Geo::FRAG_U4; i += blockDim.x) smem[i] = gfrag[i];
   {
@@ -154,59 +209,73 @@ decode_kernel(DecodeKArgs a) {
     const uint32_t* khi = (const uint32_t*)(kseg + offsetof(DecodeKArgs, chi));
     const uint32_t* klo = (const uint32_t*)(kseg + offsetof(DecodeKArgs, clo));
     auto cent = [&](const uint32_t* t, uint32_t k) -> uint32_t { return (t[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
+    constexpr int EW = Geo::ENTRY_B / 4;   // words per entry
     for (int j = threadIdx.x; j < Geo::TAB_N; j += blockDim.x) {
-      if constexpr (Geo::PER_LOOKUP == 4) {
-        // entry j: codes j, j>>2, j>>4, j>>6 as {hi01, hi23, lo01, lo23}
-        const uint32_t k0 = j & MASK, k1 = (j >> BITS) & MASK, k2 = (j >> (2 * BITS)) & MASK, k3 = j >> (3 * BITS);
-        tab[4 * j] = cent(khi, k0) | (cent(khi, k1) << 16);
-        tab[4 * j + 1] = cent(khi, k2) | (cent(khi, k3) << 16);
-        tab[4 * j + 2] = cent(klo, k0) | (cent(klo, k1) << 16);
-        tab[4 * j + 3] = cent(klo, k2) | (cent(klo, k3) << 16);
-      } else {
-        // entry j: codes j & MASK, j >> BITS as {hi pair, lo pair}
-        const uint32_t k0 = j & MASK, k1 = j >> BITS;
-        tab[2 * j] = cent(khi, k0) | (cent(khi, k1) << 16);
-        tab[2 * j + 1] = cent(klo, k0) | (cent(klo, k1) << 16);
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const uint32_t* kc = part ? klo : khi;
+        uint32_t* t = tab + part * (Geo::LO_OFF / 4) + EW * j;
+        if constexpr (Geo::PER_LOOKUP == 4) {
+          // entry j: codes j, j>>2, j>>4, j>>6 as two words
+          const uint32_t k0 = j & MASK, k1 = (j >> BITS) & MASK, k2 = (j >> (2 * BITS)) & MASK, k3 = j >> (3 * BITS);
+          t[0] = cent(kc, k0) | (cent(kc, k1) << 16);
+          t[1] = cent(kc, k2) | (cent(kc, k3) << 16);
+        } else {
+          // entry j: codes j & MASK, j >> BITS as one word
+          t[0] = cent(kc, j & MASK) | (cent(kc, j >> BITS) << 16);
+        }
       }
     }
   }
   __syncthreads();
   wait_vmem_all();
 
-  for (; tile < ntile; tile += wstride) {
-    const int64_t vbase = v_begin + tile * 32;
-    uint32_t cw[Geo::CHUNK_DW];
-#pragma unroll
-    for (int w = 0; w < Geo::CHUNK_DW; ++w) cw[w] = cwn[w];
-    // x_hat = acc * n * 2^-19 (the operand scalings, a power of two)
-    const float ns = nrmn * 0x1p-19f;
-    fetch(row_nn, cwn, nrmn);
-    row_nn = row_of(tile + 2 * wstride);
+  // per-lane LDS and output offsets (the rest of every address is a constant)
+  constexpr int CPT = E;                            // 16-byte chunks per lane per tile (16 outputs)
+  constexpr uint32_t RB = D * E;                    // bytes per output row
+  constexpr uint32_t ROWS_PER_STORE = 1024 / Geo::SB;
+  uint8_t* const stg_w = stg + vl * Geo::STG_ROW + 16 * hh * (Geo::SC / 2 * E / 16);
+  const uint32_t lrow = (uint32_t)(16 * lane) / Geo::SB, lchunk = ((uint32_t)(16 * lane) % Geo::SB) / 16;
+  const uint8_t* const stg_r = stg + lrow * Geo::STG_ROW + 16 * lchunk;
+  const uint32_t out_off = lrow * RB + (uint32_t)q * Geo::SB + 16 * lchunk;
 
-    // ---- codes -> fp16 centroids (hi and lo), 8 per K block (the lane's codes 8kb .. 8kb+7)
+  auto decode_tile = [&](const uint32_t (&cw)[DW], float nrm, int64_t tl) {
+    const int64_t vbase = v_begin + tl * 32;
+    // x_hat = acc * n * 2^-19 (the operand scalings, a power of two)
+    const float ns = nrm * 0x1p-19f;
+
+    // ---- codes -> fp16 centroids (hi and lo), 8 per K block (the lane's codes 8kb .. 8kb+7),
+    //      every word read from its table straight into its operand register
     u32x4 bhi[KB], blo[KB];
+    const char* tb = (const char*)tab;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       if constexpr (BITS == 2) {
-        // 8 codes = 16 bits = two table bytes, four fp16 hi and four lo each
-        const uint32_t bits16 = cw[kb >> 1] >> (16 * (kb & 1));
-        const u32x4 q0 = *(const u32x4*)&tab[4 * (bits16 & 255u)];
-        const u32x4 q1 = *(const u32x4*)&tab[4 * ((bits16 >> 8) & 255u)];
-        bhi[kb] = u32x4{q0[0], q0[1], q1[0], q1[1]};
-        blo[kb] = u32x4{q0[2], q0[3], q1[2], q1[3]};
+        // 8 codes = 16 bits = two table bytes, two fp16 words each
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int p = 16 * kb + 8 * h;               // bit position of the byte in the chunk
+          const uint32_t w = cw[p >> 5];
+          const int s = p & 31;
+          const uint32_t off = (s >= 3 ? (w >> (s - 3)) : (w << (3 - s))) & (255u << 3);
+          const u32x2 eh = *(const u32x2*)(tb + off);
+          const u32x2 el = *(const u32x2*)(tb + Geo::LO_OFF + off);
+          bhi[kb][2 * h] = eh[0]; bhi[kb][2 * h + 1] = eh[1];
+          blo[kb][2 * h] = el[0]; blo[kb][2 * h + 1] = el[1];
+        }
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           constexpr int PB = 2 * BITS;           // bits per code pair
           const int pos = (4 * kb + c) * PB;     // compile-time after unrolling
-          uint32_t idx;
-          if ((pos & 31) + PB <= 32)
-            idx = cw[pos >> 5] >> (pos & 31);
+          const int s = pos & 31;
+          uint32_t off;
+          if (s + PB <= 32)
+            off = (s >= 2 ? (cw[pos >> 5] >> (s - 2)) : (cw[pos >> 5] << (2 - s))) & (((1u << PB) - 1u) << 2);
           else
-            idx = funnel(cw[(pos >> 5) + 1], cw[pos >> 5], pos & 31);
-          const u32x2 e = *(const u32x2*)&tab[2 * (idx & ((1u << PB) - 1u))];
-          bhi[kb][c] = e[0];
-          blo[kb][c] = e[1];
+            off = funnel(cw[(pos >> 5) + 1], cw[pos >> 5], s - 2) & (((1u << PB) - 1u) << 2);
+          bhi[kb][c] = *(const uint32_t*)(tb + off);
+          blo[kb][c] = *(const uint32_t*)(tb + Geo::LO_OFF + off);
         }
       }
     }
@@ -215,7 +284,6 @@ decode_kernel(DecodeKArgs a) {
     //      the compiler hoist all of them into registers)
     uint32_t aoff = (uint32_t)lane * 16u;
     asm volatile("" : "+v"(aoff));
-    constexpr int CPT = E;                     // 16-byte chunks per lane per tile (16 outputs)
     f32x16 accp[2];
 #pragma unroll
     for (int t = 0; t < TS; ++t) {
@@ -238,13 +306,14 @@ decode_kernel(DecodeKArgs a) {
         }
       }
       const f32x16 acc = accp[t % 2];
-      // scaled outputs of slice coordinates hh*SC/2 + 16t .. +16 as CPT 16-byte chunks
-      u32x4 ch[CPT];
+      // scaled outputs of slice coordinates hh*SC/2 + 16t .. +16 as CPT 16-byte chunks, staged
+      // at chunk hh*SC/2*E/16 + t*CPT + k of the lane's row
       if constexpr (OUT == TQ_F32) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          ch[q4] = u32x4{__float_as_uint(acc[4 * q4] * ns), __float_as_uint(acc[4 * q4 + 1] * ns),
-                         __float_as_uint(acc[4 * q4 + 2] * ns), __float_as_uint(acc[4 * q4 + 3] * ns)};
+          *(u32x4*)(stg_w + 16 * (t * CPT + q4)) =
+              u32x4{__float_as_uint(acc[4 * q4] * ns), __float_as_uint(acc[4 * q4 + 1] * ns),
+                    __float_as_uint(acc[4 * q4 + 2] * ns), __float_as_uint(acc[4 * q4 + 3] * ns)};
       } else {
         uint32_t w[8];
 #pragma unroll
@@ -252,36 +321,35 @@ decode_kernel(DecodeKArgs a) {
           const float lo = acc[2 * j] * ns, hi = acc[2 * j + 1] * ns;
           w[j] = OUT == TQ_BF16 ? pack_bf16x2(lo, hi) : pack_f16x2(lo, hi);
         }
-        ch[0] = u32x4{w[0], w[1], w[2], w[3]};
-        ch[1] = u32x4{w[4], w[5], w[6], w[7]};
-      }
-      // staged in row-major order (row v = the wave's vector v, Geo::SC coordinates), 16-byte
-      // chunks XOR-swizzled within a row by the row index so that the 32 rows written together
-      // spread over banks
-      constexpr uint32_t RC = Geo::SC * E / 16;            // 16-byte chunks per staged row
-      constexpr uint32_t SW = RC >= 16 ? 15u : RC - 1u;
-      const uint32_t c0 = hh * (Geo::SC / 2 * E / 16) + t * CPT;
-#pragma unroll
-      for (int k = 0; k < CPT; ++k)
-        *(u32x4*)(stg + 16 * (vl * RC + ((c0 + k) ^ (vl & SW)))) = ch[k];
-    }
-    {
-      // the wave's 32 staged rows go out 1 KiB per store instruction: one contiguous block when
-      // a workgroup writes whole rows, else SB-byte pieces of 32 rows (full cache lines)
-      constexpr uint32_t RB = D * E, SB = Geo::SC * E, RC = SB / 16;
-      constexpr uint32_t SW = RC >= 16 ? 15u : RC - 1u;
-      uint8_t* tbase = (uint8_t*)a.out + vbase * RB + q * SB;
-#pragma unroll
-      for (uint32_t j = 0; j < 32 * SB / 1024; ++j) {
-        const uint32_t off = 1024u * j + 16u * lane;
-        const uint32_t rowi = off / SB, c = (off % SB) / 16;
-        const u32x4 qv = *(const u32x4*)(stg + 16 * (rowi * RC + (c ^ (rowi & SW))));
-        uint8_t* dst = vbase + rowi < v_end ? tbase + (size_t)rowi * RB + c * 16 : a.sink + 16 * lane;
-        // non-temporal: the decoded stream is far larger than the caches, and left in them as
-        // dirty lines it is written back during whatever kernel runs next
-        __builtin_nontemporal_store(qv, (u32x4*)dst);
+        *(u32x4*)(stg_w + 16 * (t * CPT)) = u32x4{w[0], w[1], w[2], w[3]};
+        *(u32x4*)(stg_w + 16 * (t * CPT + 1)) = u32x4{w[4], w[5], w[6], w[7]};
       }
     }
+    // the wave's 32 staged rows go out 1 KiB per store instruction (whole rows of the slice,
+    // full cache lines), through a buffer resource over the tile's rows: rows past the end are
+    // dropped by its range check. Non-temporal: the decoded stream is far larger than the
+    // caches, and left in them as dirty lines it is written back during whatever kernel runs next.
+    const uint32_t nv = valid_rows(tl);
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc((uint8_t*)a.out + (nv ? vbase : 0) * RB, nv * RB);
+#pragma unroll
+    for (uint32_t j = 0; j < 32 / ROWS_PER_STORE; ++j) {
+      const u32x4 qv = *(const u32x4*)(stg_r + j * ROWS_PER_STORE * Geo::STG_ROW);
+      __builtin_amdgcn_raw_buffer_store_b128(qv, ro, out_off + j * ROWS_PER_STORE * RB, 0, 2 /* nt */);
+    }
+  };
+
+  // two register sets for the codes, used in turn, so no copy ties a prefetch to its use
+  while (true) {
+    if (tile >= ntile) break;
+    fetch(tile + wstride, sB, cwB, nB);
+    sA = slot_row(tile + 2 * wstride);
+    decode_tile(cwA, nA, tile);
+    tile += wstride;
+    if (tile >= ntile) break;
+    fetch(tile + wstride, sA, cwA, nA);
+    sB = slot_row(tile + 2 * wstride);
+    decode_tile(cwB, nB, tile);
+    tile += wstride;
   }
 }
 
@@ -296,7 +364,6 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
   k.slot = L.slot_mapping;
   k.out = L.out;
   k.zero = L.rot->zero();
-  k.sink = L.rot->sink();
   k.n = L.n;
   k.vpr = L.vectors_per_rot;
   for (int j = 0; j < 8; ++j) {

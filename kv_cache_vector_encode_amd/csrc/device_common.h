@@ -82,6 +82,12 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
 }
 
+// A raw buffer resource over `bytes` bytes at `base`: loads past the end return zero and
+// stores past it are dropped by the hardware's range check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
 // s_waitcnt vmcnt(0): wait for all of this wave's outstanding vector-memory accesses. Issued
 // once after a loop's first prefetch, so that the waits inside the loop are sized for the
 // loop's own accesses rather than for loads still in flight from before it.
