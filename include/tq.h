@@ -96,7 +96,8 @@ tq_rotation_t* tq_rotation_from_gaussian(int d, int n_rot, const float* gaussian
 tq_rotation_t* tq_rotation_from_matrix(int d, int n_rot, const double* pi);
 
 /* Hadamard rotation (Turbo Attention PyPI page, "The codec", Hadamard rotation row: a
- * Walsh-Hadamard transform spreads outlier channels; queries are rotated the same way):
+ * Walsh-Hadamard transform that smears large channels over all coordinates, applied to the
+ * query side as well):
  * Pi_r = H_d diag(s_r) / sqrt(d), H_d Sylvester's +-1 Walsh-Hadamard matrix
  * (H[i][j] = (-1)^popcount(i & j)), s_r = signs[r] (host int8 [n_rot, d], each +1 or -1;
  * NULL = all +1). Uploaded like the other constructors; every kernel takes it unchanged.

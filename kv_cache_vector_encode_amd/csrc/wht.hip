@@ -1,8 +1,9 @@
 // Encode and decode with a Hadamard rotation as an O(d log d) fast Walsh-Hadamard transform.
 //
-// Method: Turbo Attention PyPI page, "The codec", Hadamard rotation row (a Walsh-Hadamard
-// transform with a seeded sign per channel spreads outlier channels before quantization; keys
-// and queries are rotated the same way). With Pi = H_d diag(s) / sqrt(d) (H_d Sylvester's
+// Method: Turbo Attention PyPI page, "The codec", Hadamard rotation row (the rotation is a
+// Walsh-Hadamard transform, here after a seeded sign per channel, so that a few large channels
+// are smeared over all coordinates before quantization; the query side uses the same
+// rotation). With Pi = H_d diag(s) / sqrt(d) (H_d Sylvester's
 // +-1 matrix, H[i][j] = (-1)^popcount(i & j)), the encode of the KV Cache API page
 // (TurboQuantCompressorMSE.compress) becomes y = H (s o x) / (sqrt(d) (n + 1e-8)) and its decode
 // (decompress) x_hat = (n / sqrt(d)) s o (H c[idx]), since H is symmetric. No matrix is read:

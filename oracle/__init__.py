@@ -17,7 +17,7 @@ Sources (pages are cited by title and section; see each function's docstring):
     ~2.7x distance from the information-theoretic bound.
   * aitherkvcache landing page: encode(x) -> (packed uint8, float32 norms), 3.8-7.1x.
   * Turbo Attention (turbo-attn) PyPI page: the 8-key example (3.88x, error 0.10);
-    queries rotated like keys so scores need no un-rotation.
+    its codec table, whose rotation row applies the key rotation to the queries too.
 
 Modules: rotation (Haar rotation by QR), codebook (Lloyd-Max for the sphere-coordinate
 density), codec (norm, rotate, quantize, pack, unpack, decode), attention (scores and
