@@ -965,88 +965,79 @@ static void launch_window(const WinKArgs& w, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((window_kernel<D, WDT, 16>), grid, dim3(kWinChunk), 0, st, w);
 }
 
-// Query heads handled together by qrot_kernel / merge_kernel (a block reads each rotation entry
-// once for all of them); kept small so that there are enough blocks to hide load latency.
-constexpr int kHeadsPerBlock = 2;
-
-// Parts per output coordinate in qrot_kernel / merge_kernel: thread (k, part) covers 1/kParts
-// of a length-D (or length-s_eff) sum, so a thread's chain of dependent loads is kParts times
-// shorter; the parts meet in LDS.
-constexpr int kParts = 4;
-
-// q' = Pi_K q for kHeadsPerBlock query heads of one sequence. Thread (k, part) owns output
-// coordinate k over the rows j of its part, reading Pi_K^T row by row (coalesced across k);
-// the queries sit in LDS.
+// qrot_kernel / merge_kernel: one query head per block, thread (k, part) owning coordinate k
+// over 1/P of a length-D (or length-s_eff) sum, so that its chain of dependent loads is P times
+// shorter; the parts meet in LDS. P = 4 when there are many heads (batched decode), and
+// 1024 / D (a full 1024-thread block) when there are few (one sequence with many splits),
+// where each block's load latency is the whole cost.
+constexpr int kPartsMany = 4;
 template <int D>
-__global__ void __launch_bounds__(D * kParts) qrot_kernel(const void* q, int q_dtype, const float* pikt,
-                                                          int64_t rot_stride, int Hq, int bpr, float* out) {
-  constexpr int HB = kHeadsPerBlock, JP = D / kParts;
-  __shared__ float qs[HB][D];
-  __shared__ float red[kParts][HB][D];
-  const int b = blockIdx.x, h0 = blockIdx.y * HB;
-  const int nh = min(HB, Hq - h0);
+constexpr int parts_few() { return 1024 / D; }
+inline bool few_heads(int B, int Hq) { return (int64_t)B * Hq < 512; }
+
+// q' = Pi_K q for one query head (block (b, h)). Thread (k, part) owns output coordinate k over
+// the rows j of its part, reading Pi_K^T row by row (coalesced across k); the query sits in LDS.
+template <int D, int P>
+__global__ void __launch_bounds__(D * P) qrot_kernel(const void* q, int q_dtype, const float* pikt,
+                                                     int64_t rot_stride, int Hq, int bpr, float* out) {
+  constexpr int JP = D / P;
+  __shared__ float qs[D];
+  __shared__ float red[P][D];
+  const int b = blockIdx.x, h = blockIdx.y;
   const int k = threadIdx.x % D, part = threadIdx.x / D;
-  for (int i = threadIdx.x; i < HB * D; i += blockDim.x) {
-    const int h = i / D, kk = i - h * D;
-    float v = 0.f;
-    if (h < nh) {
-      const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + kk;
-      if (q_dtype == TQ_F32)
-        v = ((const float*)q)[idx];
-      else if (q_dtype == TQ_BF16)
-        v = bf16_bits_to_f32(((const uint16_t*)q)[idx]);
-      else
-        v = f16_bits_to_f32(((const uint16_t*)q)[idx]);
-    }
-    qs[h][kk] = v;
+  const int r = bpr ? b / bpr : 0;
+  // this thread's rows of Pi_K^T first, so that their latency overlaps the query's
+  const float* PT = pikt + r * rot_stride + (int64_t)part * JP * D + k;   // PT[j*D] = Pi[k][part*JP + j]
+  float pv[JP];
+#pragma unroll
+  for (int j = 0; j < JP; ++j) pv[j] = PT[(int64_t)j * D];
+  if (threadIdx.x < D) {
+    const int64_t idx = ((int64_t)b * Hq + h) * D + threadIdx.x;
+    float v;
+    if (q_dtype == TQ_F32)
+      v = ((const float*)q)[idx];
+    else if (q_dtype == TQ_BF16)
+      v = bf16_bits_to_f32(((const uint16_t*)q)[idx]);
+    else
+      v = f16_bits_to_f32(((const uint16_t*)q)[idx]);
+    qs[threadIdx.x] = v;
   }
   __syncthreads();
-  const int r = bpr ? b / bpr : 0;
-  const float* PT = pikt + r * rot_stride + (int64_t)part * JP * D + k;   // PT[j*D] = Pi[k][part*JP + j]
-  float acc[HB];
+  float acc = 0.f;
 #pragma unroll
-  for (int h = 0; h < HB; ++h) acc[h] = 0.f;
-#pragma unroll 16
-  for (int j = 0; j < JP; ++j) {
-    const float pv = PT[(int64_t)j * D];
-#pragma unroll
-    for (int h = 0; h < HB; ++h) acc[h] = fmaf(pv, qs[h][part * JP + j], acc[h]);
-  }
-#pragma unroll
-  for (int h = 0; h < HB; ++h) red[part][h][k] = acc[h];
+  for (int j = 0; j < JP; ++j) acc = fmaf(pv[j], qs[part * JP + j], acc);
+  red[part][k] = acc;
   __syncthreads();
   if (part == 0) {
+    float v = red[0][k];
 #pragma unroll
-    for (int h = 0; h < HB; ++h) {
-      if (h >= nh) continue;
-      float v = red[0][h][k];
-#pragma unroll
-      for (int pp = 1; pp < kParts; ++pp) v += red[pp][h][k];
-      out[((int64_t)b * Hq + h0 + h) * D + k] = v;
-    }
+    for (int pp = 1; pp < P; ++pp) v += red[pp][k];
+    out[((int64_t)b * Hq + h) * D + k] = v;
   }
 }
 
-// Log-sum-exp merge of the token splits for kHeadsPerBlock query heads of one sequence, then
+// Log-sum-exp merge of the token splits of one query head (block (b, h)), then
 // o = Pi_V^T (sum_s acc_s e^(m_s - M)) / L (+ the window's partial, already unrotated).
-// Thread (k, part) owns coordinate k over splits s = part, part + kParts, ... and over the
-// rows of its part in the final product.
-template <int D, int OUT>
-__global__ void __launch_bounds__(D * kParts) merge_kernel(const float* part, int s_eff, int has_window, int B,
-                                                           int Hq, int bpr, const float* piv, int64_t rot_stride,
-                                                           void* out, float* lse) {
-  constexpr int HB = kHeadsPerBlock, NW = D * kParts / 64, JP = D / kParts;
-  __shared__ float orot[HB][D];
-  __shared__ float red[kParts][HB][D];
-  __shared__ float redm[HB][NW];
-  __shared__ float lred[kParts][HB];
-  __shared__ float Ms[HB], Ls[HB];
-  const int b = blockIdx.x, h0 = blockIdx.y * HB;
-  const int nh = min(HB, Hq - h0);
+// Thread (k, part) owns coordinate k over splits s = part, part + P, ... and over the rows of
+// its part in the final product. The split maxima are read once, for M, and kept in LDS, so the
+// sum pass issues its loads without waiting for them.
+template <int D, int OUT, int P>
+__global__ void __launch_bounds__(D * P) merge_kernel(const float* part, int s_eff, int has_window, int B, int Hq,
+                                                      int bpr, const float* piv, int64_t rot_stride, void* out,
+                                                      float* lse) {
+  constexpr int JP = D / P, NT = D * P, NW = NT / 64;
+  constexpr int MS = 2048;                 // split maxima kept in LDS (more are read again)
+  __shared__ float msplit[MS];
+  __shared__ float orot[D];
+  __shared__ float red[P][D];
+  __shared__ float redm[NW];
+  __shared__ float lred[P];
+  __shared__ float Msh, Lsh;
+  const int b = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int k = tid % D, pt = tid / D;
   const int64_t sstride = (int64_t)B * Hq * (D + 2);
-  const float* P0 = part + ((int64_t)b * Hq + h0) * (D + 2);   // split s, head h: + s*sstride + h*(D+2)
+  const float* P0 = part + ((int64_t)b * Hq + h) * (D + 2);   // split s: + s*sstride
   const int ns = s_eff + has_window;
   // this thread's rows of Pi_V for the final product, loaded first so that their latency
   // overlaps the reads of the partials: pvr[j] = Pi[pt*JP + j][k]
@@ -1055,105 +1046,115 @@ __global__ void __launch_bounds__(D * kParts) merge_kernel(const float* part, in
 #pragma unroll
   for (int j = 0; j < JP; ++j) pvr[j] = Pv[(int64_t)j * D];
 
-  // M_h = max over splits (and the window) of m_s
+  // M = max over splits (and the window) of m_s
+  float m = -INFINITY;
+  for (int s = tid; s < ns; s += NT) {
+    const float v = P0[(int64_t)s * sstride];
+    if (s < MS) msplit[s] = v;
+    m = fmaxf(m, v);
+  }
 #pragma unroll
-  for (int h = 0; h < HB; ++h) {
-    float m = -INFINITY;
-    if (h < nh)
-      for (int s = tid; s < ns; s += blockDim.x) m = fmaxf(m, P0[(int64_t)s * sstride + h * (D + 2)]);
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, wave_xor(m, o));
+  if (lane == 0) redm[wv] = m;
+  __syncthreads();
+  if (tid == 0) {
+    float mm = redm[0];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, wave_xor(m, o));
-    if (lane == 0) redm[h][wv] = m;
+    for (int w = 1; w < NW; ++w) mm = fmaxf(mm, redm[w]);
+    Msh = mm;
   }
   __syncthreads();
-  if (tid < HB) {
-    float m = redm[tid][0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) m = fmaxf(m, redm[tid][w]);
-    Ms[tid] = m;
-  }
-  __syncthreads();
+  const float M = Msh;
 
   // this part's splits
-  float acc[HB], lsum[HB];
-#pragma unroll
-  for (int h = 0; h < HB; ++h) {
-    acc[h] = 0.f;
-    lsum[h] = 0.f;
-    const float M = Ms[h];
-    if (h < nh && M > -INFINITY) {
-#pragma unroll 4
-      for (int s = pt; s < s_eff; s += kParts) {
-        const float* Ps = P0 + (int64_t)s * sstride + h * (D + 2);
-        const float ms = Ps[0];
-        const float w = ms > -INFINITY ? __expf(ms - M) : 0.f;
-        lsum[h] = fmaf(w, Ps[1], lsum[h]);
-        acc[h] = fmaf(w, Ps[2 + k], acc[h]);
-      }
+  float acc = 0.f, lsum = 0.f;
+  if (M > -INFINITY) {
+#pragma unroll 8
+    for (int s = pt; s < s_eff; s += P) {
+      const float* Ps = P0 + (int64_t)s * sstride;
+      const float ms = s < MS ? msplit[s] : Ps[0];
+      const float w = ms > -INFINITY ? __expf(ms - M) : 0.f;
+      lsum = fmaf(w, Ps[1], lsum);
+      acc = fmaf(w, Ps[2 + k], acc);
     }
-    red[pt][h][k] = acc[h];
-    if (k == 0) lred[pt][h] = lsum[h];
   }
+  red[pt][k] = acc;
+  if (k == 0) lred[pt] = lsum;
   __syncthreads();
-  if (tid < HB) {
+  if (tid == 0) {
     float l = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < kParts; ++pp) l += lred[pp][tid];
+    for (int pp = 0; pp < P; ++pp) l += lred[pp];
     // the window's partial joins the normalizer here and the output after the rotation back
-    if (has_window && tid < nh && Ms[tid] > -INFINITY) {
-      const float* Pw = P0 + (int64_t)s_eff * sstride + tid * (D + 2);
+    if (has_window && M > -INFINITY) {
+      const float* Pw = P0 + (int64_t)s_eff * sstride;
       const float ms = Pw[0];
-      if (ms > -INFINITY) l = fmaf(__expf(ms - Ms[tid]), Pw[1], l);
+      if (ms > -INFINITY) l = fmaf(__expf(ms - M), Pw[1], l);
     }
-    Ls[tid] = l;
+    Lsh = l;
   }
   __syncthreads();
+  const float L = Lsh;
   if (pt == 0) {
+    float v = red[0][k];
 #pragma unroll
-    for (int h = 0; h < HB; ++h) {
-      float v = red[0][h][k];
-#pragma unroll
-      for (int pp = 1; pp < kParts; ++pp) v += red[pp][h][k];
-      orot[h][k] = Ls[h] > 0.f ? v / Ls[h] : 0.f;
-    }
+    for (int pp = 1; pp < P; ++pp) v += red[pp][k];
+    orot[k] = L > 0.f ? v / L : 0.f;
   }
   __syncthreads();
 
   // o = Pi_V^T orot, this part's rows
-  float o[HB];
+  float o = 0.f;
 #pragma unroll
-  for (int h = 0; h < HB; ++h) o[h] = 0.f;
-#pragma unroll
-  for (int j = 0; j < JP; ++j) {
-#pragma unroll
-    for (int h = 0; h < HB; ++h) o[h] = fmaf(pvr[j], orot[h][pt * JP + j], o[h]);
-  }
-#pragma unroll
-  for (int h = 0; h < HB; ++h) red[pt][h][k] = o[h];
+  for (int j = 0; j < JP; ++j) o = fmaf(pvr[j], orot[pt * JP + j], o);
+  red[pt][k] = o;
   __syncthreads();
   if (pt == 0) {
+    float v = red[0][k];
 #pragma unroll
-    for (int h = 0; h < HB; ++h) {
-      if (h >= nh) continue;
-      float v = red[0][h][k];
-#pragma unroll
-      for (int pp = 1; pp < kParts; ++pp) v += red[pp][h][k];
-      const float L = Ls[h];
-      if (has_window && L > 0.f && Ms[h] > -INFINITY) {
-        const float* Pw = P0 + (int64_t)s_eff * sstride + h * (D + 2);
-        const float ms = Pw[0];
-        if (ms > -INFINITY) v += __expf(ms - Ms[h]) * Pw[2 + k] / L;
-      }
-      const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + k;
-      if constexpr (OUT == TQ_F32)
-        ((float*)out)[idx] = v;
-      else if constexpr (OUT == TQ_BF16)
-        ((uint16_t*)out)[idx] = (uint16_t)f32_to_bf16_bits(v);
-      else
-        ((uint16_t*)out)[idx] = (uint16_t)f32_to_f16_bits(v);
-      if (k == 0 && lse) lse[(int64_t)b * Hq + h0 + h] = L > 0.f ? Ms[h] + logf(L) : -INFINITY;
+    for (int pp = 1; pp < P; ++pp) v += red[pp][k];
+    if (has_window && L > 0.f && M > -INFINITY) {
+      const float* Pw = P0 + (int64_t)s_eff * sstride;
+      const float ms = Pw[0];
+      if (ms > -INFINITY) v += __expf(ms - M) * Pw[2 + k] / L;
     }
+    const int64_t idx = ((int64_t)b * Hq + h) * D + k;
+    if constexpr (OUT == TQ_F32)
+      ((float*)out)[idx] = v;
+    else if constexpr (OUT == TQ_BF16)
+      ((uint16_t*)out)[idx] = (uint16_t)f32_to_bf16_bits(v);
+    else
+      ((uint16_t*)out)[idx] = (uint16_t)f32_to_f16_bits(v);
+    if (k == 0 && lse) lse[(int64_t)b * Hq + h] = L > 0.f ? M + logf(L) : -INFINITY;
   }
+}
+
+template <int D, int P>
+static void launch_qrot(const tq_attn_params* p, const float* pikt, int64_t rs, float* dst, hipStream_t st) {
+  hipLaunchKernelGGL((qrot_kernel<D, P>), dim3(p->batch, p->num_q_heads), dim3(D * P), 0, st, p->q, p->q_dtype, pikt,
+                     rs, p->num_q_heads, p->batch_per_rot, dst);
+}
+template <int D>
+static void launch_qrot_any(const tq_attn_params* p, const float* pikt, int64_t rs, float* dst, hipStream_t st) {
+  if (few_heads(p->batch, p->num_q_heads))
+    launch_qrot<D, parts_few<D>()>(p, pikt, rs, dst, st);
+  else
+    launch_qrot<D, kPartsMany>(p, pikt, rs, dst, st);
+}
+
+template <int D, int OUT, int P>
+static void launch_merge(const tq_attn_params* p, const float* part, int s_eff, int has_win, const float* piv,
+                         int64_t rs, hipStream_t st) {
+  hipLaunchKernelGGL((merge_kernel<D, OUT, P>), dim3(p->batch, p->num_q_heads), dim3(D * P), 0, st, part, s_eff,
+                     has_win, p->batch, p->num_q_heads, p->batch_per_rot, piv, rs, p->out, p->lse);
+}
+template <int D, int OUT>
+static void launch_merge_p(const tq_attn_params* p, const float* part, int s_eff, int has_win, const float* piv,
+                           int64_t rs, hipStream_t st) {
+  if (few_heads(p->batch, p->num_q_heads))
+    launch_merge<D, OUT, parts_few<D>()>(p, part, s_eff, has_win, piv, rs, st);
+  else
+    launch_merge<D, OUT, kPartsMany>(p, part, s_eff, has_win, piv, rs, st);
 }
 
 // Resident waves per CU of the fused-attention kernel instance (registers and LDS as compiled),
@@ -1210,17 +1211,14 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   uint8_t* ws = (uint8_t*)p->workspace;
   float* qrot = (float*)(ws + lay.qrot_off);
   const int Hq = p->num_q_heads, B = p->batch;
-  const unsigned hblocks = (unsigned)((Hq + kHeadsPerBlock - 1) / kHeadsPerBlock);
-  hipLaunchKernelGGL((qrot_kernel<D>), dim3(B, hblocks), dim3(D * kParts), 0, st, p->q, p->q_dtype, rk.f32t(0),
-                     (int64_t)(rk.f32_stride / sizeof(float)), Hq, p->batch_per_rot, qrot);
+  launch_qrot_any<D>(p, rk.f32t(0), (int64_t)(rk.f32_stride / sizeof(float)), qrot, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   float* qsk = (float*)(ws + lay.qsk_off);
   if constexpr (QJL) {
     // S q: the same product with S^T in place of Pi^T
     const Qjl& qj = p->qjl_k->q;
-    hipLaunchKernelGGL((qrot_kernel<D>), dim3(B, hblocks), dim3(D * kParts), 0, st, p->q, p->q_dtype, qj.st(0),
-                       (int64_t)(qj.st_stride / sizeof(float)), Hq, p->batch_per_rot, qsk);
+    launch_qrot_any<D>(p, qj.st(0), (int64_t)(qj.st_stride / sizeof(float)), qsk, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p->max_seq_len == 0 && scores_only) return hipSuccess;
@@ -1301,17 +1299,9 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   }
   const int64_t rs = (int64_t)(rv.f32_stride / sizeof(float));
   switch (p->out_dtype) {
-    case TQ_F32:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_F32>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, lay.splits, has_win, B, Hq,
-                         p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
-      break;
-    case TQ_BF16:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_BF16>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, lay.splits, has_win, B, Hq,
-                         p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
-      break;
-    default:
-      hipLaunchKernelGGL((merge_kernel<D, TQ_F16>), dim3(B, hblocks), dim3(D * kParts), 0, st, a.part, lay.splits, has_win, B, Hq,
-                         p->batch_per_rot, rv.f32(0), rs, p->out, p->lse);
+    case TQ_F32: launch_merge_p<D, TQ_F32>(p, a.part, lay.splits, has_win, rv.f32(0), rs, st); break;
+    case TQ_BF16: launch_merge_p<D, TQ_BF16>(p, a.part, lay.splits, has_win, rv.f32(0), rs, st); break;
+    default: launch_merge_p<D, TQ_F16>(p, a.part, lay.splits, has_win, rv.f32(0), rs, st);
   }
   return hipGetLastError();
 }
