@@ -58,6 +58,9 @@ def parse():
                     help="skip the figures of the rows beside the hot path (window, Hadamard, QJL, group quant)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for scaling HBM byte counters)")
+    ap.add_argument("--attention-32k-only", action="store_true",
+                    help="profiling mode: time only the batch-32 x 32768-token fused decode attention and print "
+                         "its record (not the bench line)")
     return ap.parse_args()
 
 
@@ -635,6 +638,18 @@ def cpu_baseline(n_vec: int = 262144, tokens: int = 16384, max_cores: int = 16):
                                     "%d_cores" % cores: round(full / (vall * 1e9), 1)}}
 
 
+def copy_probe(torch, dev):
+    """A plain 1 GiB device-to-device copy, three times: the reference for scaling the HBM byte
+    counters of a profiling run."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -649,6 +664,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.attention_32k_only:
+        rec = decode_attention_32k(tq, ti, torch, dev, reps=args.steps)
+        if args.copy_probe:
+            copy_probe(torch, dev)
+        rec["source_hash"] = kernel_source_hash()
+        print(json.dumps(rec), flush=True)
+        return
     head = headline_70b(args, tq, ti, torch, dev)
     show = lambda name, rec: print("bench: %s %s" % (name, json.dumps(rec)), file=sys.stderr, flush=True)
     show("headline", {k: head[k] for k in ("value", "ms_per_step", "roofline", "kernels", "mfma_rotation")})
@@ -666,13 +688,7 @@ def main():
             show("hadamard_fast_transform", nxt["hadamard_fast_transform"])
         extra["next_rows"] = nxt
     if args.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        torch.cuda.empty_cache()
+        copy_probe(torch, dev)
     line = {
         "metric": METRIC, "value": head["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
