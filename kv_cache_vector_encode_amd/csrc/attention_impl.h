@@ -965,79 +965,96 @@ static void launch_window(const WinKArgs& w, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((window_kernel<D, WDT, 16>), grid, dim3(kWinChunk), 0, st, w);
 }
 
-// qrot_kernel / merge_kernel: one query head per block, thread (k, part) owning coordinate k
-// over 1/P of a length-D (or length-s_eff) sum, so that its chain of dependent loads is P times
-// shorter; the parts meet in LDS. P = 4 when there are many heads (batched decode), and
-// 1024 / D (a full 1024-thread block) when there are few (one sequence with many splits),
-// where each block's load latency is the whole cost.
-constexpr int kPartsMany = 4;
+// qrot_kernel / merge_kernel: HB query heads of one sequence per block, thread (k, part) owning
+// coordinate k over 1/P of a length-D (or length-s_eff) sum, so that its chain of dependent
+// loads is P times shorter; the parts meet in LDS. Every block reads the whole rotation (64 KiB
+// at d = 128, from L2), so with many heads (batched decode) a block takes HB = 2 heads with
+// P = 4 parts (measured: 1 and 4 heads per block were slower there), and with few (one sequence
+// with many splits) one head with P = 1024 / D parts: there each block's load latency is the
+// whole cost.
+constexpr int kPartsMany = 4, kHeadsMany = 2;
 template <int D>
 constexpr int parts_few() { return 1024 / D; }
 inline bool few_heads(int B, int Hq) { return (int64_t)B * Hq < 512; }
 
-// q' = Pi_K q for one query head (block (b, h)). Thread (k, part) owns output coordinate k over
-// the rows j of its part, reading Pi_K^T row by row (coalesced across k); the query sits in LDS.
-template <int D, int P>
+// q' = Pi_K q for HB query heads of one sequence (block (b, head group)). Thread (k, part) owns
+// output coordinate k over the rows j of its part, reading Pi_K^T row by row (coalesced across
+// k); the queries sit in LDS.
+template <int D, int P, int HB>
 __global__ void __launch_bounds__(D * P) qrot_kernel(const void* q, int q_dtype, const float* pikt,
                                                      int64_t rot_stride, int Hq, int bpr, float* out) {
   constexpr int JP = D / P;
-  __shared__ float qs[D];
-  __shared__ float red[P][D];
-  const int b = blockIdx.x, h = blockIdx.y;
+  __shared__ float qs[HB][D];
+  __shared__ float red[P][HB][D];
+  const int b = blockIdx.x, h0 = blockIdx.y * HB;
+  const int nh = min(HB, Hq - h0);
   const int k = threadIdx.x % D, part = threadIdx.x / D;
   const int r = bpr ? b / bpr : 0;
-  // this thread's rows of Pi_K^T first, so that their latency overlaps the query's
+  // this thread's rows of Pi_K^T first, so that their latency overlaps the queries'
   const float* PT = pikt + r * rot_stride + (int64_t)part * JP * D + k;   // PT[j*D] = Pi[k][part*JP + j]
   float pv[JP];
 #pragma unroll
   for (int j = 0; j < JP; ++j) pv[j] = PT[(int64_t)j * D];
-  if (threadIdx.x < D) {
-    const int64_t idx = ((int64_t)b * Hq + h) * D + threadIdx.x;
-    float v;
-    if (q_dtype == TQ_F32)
-      v = ((const float*)q)[idx];
-    else if (q_dtype == TQ_BF16)
-      v = bf16_bits_to_f32(((const uint16_t*)q)[idx]);
-    else
-      v = f16_bits_to_f32(((const uint16_t*)q)[idx]);
-    qs[threadIdx.x] = v;
+  for (int i = threadIdx.x; i < HB * D; i += D * P) {
+    const int h = i / D, kk = i - h * D;
+    float v = 0.f;
+    if (h < nh) {
+      const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + kk;
+      if (q_dtype == TQ_F32)
+        v = ((const float*)q)[idx];
+      else if (q_dtype == TQ_BF16)
+        v = bf16_bits_to_f32(((const uint16_t*)q)[idx]);
+      else
+        v = f16_bits_to_f32(((const uint16_t*)q)[idx]);
+    }
+    qs[h][kk] = v;
   }
   __syncthreads();
-  float acc = 0.f;
+  float acc[HB];
 #pragma unroll
-  for (int j = 0; j < JP; ++j) acc = fmaf(pv[j], qs[part * JP + j], acc);
-  red[part][k] = acc;
+  for (int h = 0; h < HB; ++h) acc[h] = 0.f;
+#pragma unroll
+  for (int j = 0; j < JP; ++j)
+#pragma unroll
+    for (int h = 0; h < HB; ++h) acc[h] = fmaf(pv[j], qs[h][part * JP + j], acc[h]);
+#pragma unroll
+  for (int h = 0; h < HB; ++h) red[part][h][k] = acc[h];
   __syncthreads();
   if (part == 0) {
-    float v = red[0][k];
 #pragma unroll
-    for (int pp = 1; pp < P; ++pp) v += red[pp][k];
-    out[((int64_t)b * Hq + h) * D + k] = v;
+    for (int h = 0; h < HB; ++h) {
+      if (h >= nh) continue;
+      float v = red[0][h][k];
+#pragma unroll
+      for (int pp = 1; pp < P; ++pp) v += red[pp][h][k];
+      out[((int64_t)b * Hq + h0 + h) * D + k] = v;
+    }
   }
 }
 
-// Log-sum-exp merge of the token splits of one query head (block (b, h)), then
+// Log-sum-exp merge of the token splits for HB query heads of one sequence, then
 // o = Pi_V^T (sum_s acc_s e^(m_s - M)) / L (+ the window's partial, already unrotated).
 // Thread (k, part) owns coordinate k over splits s = part, part + P, ... and over the rows of
-// its part in the final product. The split maxima are read once, for M, and kept in LDS, so the
-// sum pass issues its loads without waiting for them.
-template <int D, int OUT, int P>
+// its part in the final product. The split maxima are read once, for M, and kept in LDS (when
+// they fit), so the sum pass issues its loads without waiting for them.
+template <int D, int OUT, int P, int HB>
 __global__ void __launch_bounds__(D * P) merge_kernel(const float* part, int s_eff, int has_window, int B, int Hq,
                                                       int bpr, const float* piv, int64_t rot_stride, void* out,
                                                       float* lse) {
   constexpr int JP = D / P, NT = D * P, NW = NT / 64;
-  constexpr int MS = 2048;                 // split maxima kept in LDS (more are read again)
-  __shared__ float msplit[MS];
-  __shared__ float orot[D];
-  __shared__ float red[P][D];
-  __shared__ float redm[NW];
-  __shared__ float lred[P];
-  __shared__ float Msh, Lsh;
-  const int b = blockIdx.x, h = blockIdx.y;
+  constexpr int MS = 2048 / HB;              // split maxima kept in LDS per head
+  __shared__ float msplit[HB][MS];
+  __shared__ float orot[HB][D];
+  __shared__ float red[P][HB][D];
+  __shared__ float redm[HB][NW];
+  __shared__ float lred[P][HB];
+  __shared__ float Msh[HB], Lsh[HB];
+  const int b = blockIdx.x, h0 = blockIdx.y * HB;
+  const int nh = min(HB, Hq - h0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int k = tid % D, pt = tid / D;
   const int64_t sstride = (int64_t)B * Hq * (D + 2);
-  const float* P0 = part + ((int64_t)b * Hq + h) * (D + 2);   // split s: + s*sstride
+  const float* P0 = part + ((int64_t)b * Hq + h0) * (D + 2);   // split s, head h: + s*sstride + h*(D+2)
   const int ns = s_eff + has_window;
   // this thread's rows of Pi_V for the final product, loaded first so that their latency
   // overlaps the reads of the partials: pvr[j] = Pi[pt*JP + j][k]
@@ -1046,115 +1063,136 @@ __global__ void __launch_bounds__(D * P) merge_kernel(const float* part, int s_e
 #pragma unroll
   for (int j = 0; j < JP; ++j) pvr[j] = Pv[(int64_t)j * D];
 
-  // M = max over splits (and the window) of m_s
-  float m = -INFINITY;
-  for (int s = tid; s < ns; s += NT) {
-    const float v = P0[(int64_t)s * sstride];
-    if (s < MS) msplit[s] = v;
-    m = fmaxf(m, v);
-  }
+  // M_h = max over splits (and the window) of m_s
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, wave_xor(m, o));
-  if (lane == 0) redm[wv] = m;
-  __syncthreads();
-  if (tid == 0) {
-    float mm = redm[0];
+  for (int h = 0; h < HB; ++h) {
+    float m = -INFINITY;
+    if (h < nh)
+      for (int s = tid; s < ns; s += NT) {
+        const float v = P0[(int64_t)s * sstride + h * (D + 2)];
+        if (s < MS) msplit[h][s] = v;
+        m = fmaxf(m, v);
+      }
 #pragma unroll
-    for (int w = 1; w < NW; ++w) mm = fmaxf(mm, redm[w]);
-    Msh = mm;
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, wave_xor(m, o));
+    if (lane == 0) redm[h][wv] = m;
   }
   __syncthreads();
-  const float M = Msh;
+  if (tid < HB) {
+    float mm = redm[tid][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mm = fmaxf(mm, redm[tid][w]);
+    Msh[tid] = mm;
+  }
+  __syncthreads();
 
   // this part's splits
-  float acc = 0.f, lsum = 0.f;
-  if (M > -INFINITY) {
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    float acc = 0.f, lsum = 0.f;
+    const float M = Msh[h];
+    if (h < nh && M > -INFINITY) {
 #pragma unroll 8
-    for (int s = pt; s < s_eff; s += P) {
-      const float* Ps = P0 + (int64_t)s * sstride;
-      const float ms = s < MS ? msplit[s] : Ps[0];
-      const float w = ms > -INFINITY ? __expf(ms - M) : 0.f;
-      lsum = fmaf(w, Ps[1], lsum);
-      acc = fmaf(w, Ps[2 + k], acc);
+      for (int s = pt; s < s_eff; s += P) {
+        const float* Ps = P0 + (int64_t)s * sstride + h * (D + 2);
+        const float ms = s < MS ? msplit[h][s] : Ps[0];
+        const float w = ms > -INFINITY ? __expf(ms - M) : 0.f;
+        lsum = fmaf(w, Ps[1], lsum);
+        acc = fmaf(w, Ps[2 + k], acc);
+      }
     }
+    red[pt][h][k] = acc;
+    if (k == 0) lred[pt][h] = lsum;
   }
-  red[pt][k] = acc;
-  if (k == 0) lred[pt] = lsum;
   __syncthreads();
-  if (tid == 0) {
+  if (tid < HB) {
     float l = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp) l += lred[pp];
+    for (int pp = 0; pp < P; ++pp) l += lred[pp][tid];
     // the window's partial joins the normalizer here and the output after the rotation back
-    if (has_window && M > -INFINITY) {
-      const float* Pw = P0 + (int64_t)s_eff * sstride;
+    if (has_window && tid < nh && Msh[tid] > -INFINITY) {
+      const float* Pw = P0 + (int64_t)s_eff * sstride + tid * (D + 2);
       const float ms = Pw[0];
-      if (ms > -INFINITY) l = fmaf(__expf(ms - M), Pw[1], l);
+      if (ms > -INFINITY) l = fmaf(__expf(ms - Msh[tid]), Pw[1], l);
     }
-    Lsh = l;
+    Lsh[tid] = l;
   }
   __syncthreads();
-  const float L = Lsh;
   if (pt == 0) {
-    float v = red[0][k];
 #pragma unroll
-    for (int pp = 1; pp < P; ++pp) v += red[pp][k];
-    orot[k] = L > 0.f ? v / L : 0.f;
+    for (int h = 0; h < HB; ++h) {
+      float v = red[0][h][k];
+#pragma unroll
+      for (int pp = 1; pp < P; ++pp) v += red[pp][h][k];
+      orot[h][k] = Lsh[h] > 0.f ? v / Lsh[h] : 0.f;
+    }
   }
   __syncthreads();
 
   // o = Pi_V^T orot, this part's rows
-  float o = 0.f;
+  float o[HB];
 #pragma unroll
-  for (int j = 0; j < JP; ++j) o = fmaf(pvr[j], orot[pt * JP + j], o);
-  red[pt][k] = o;
+  for (int h = 0; h < HB; ++h) o[h] = 0.f;
+#pragma unroll
+  for (int j = 0; j < JP; ++j)
+#pragma unroll
+    for (int h = 0; h < HB; ++h) o[h] = fmaf(pvr[j], orot[h][pt * JP + j], o[h]);
+#pragma unroll
+  for (int h = 0; h < HB; ++h) red[pt][h][k] = o[h];
   __syncthreads();
   if (pt == 0) {
-    float v = red[0][k];
 #pragma unroll
-    for (int pp = 1; pp < P; ++pp) v += red[pp][k];
-    if (has_window && L > 0.f && M > -INFINITY) {
-      const float* Pw = P0 + (int64_t)s_eff * sstride;
-      const float ms = Pw[0];
-      if (ms > -INFINITY) v += __expf(ms - M) * Pw[2 + k] / L;
+    for (int h = 0; h < HB; ++h) {
+      if (h >= nh) continue;
+      float v = red[0][h][k];
+#pragma unroll
+      for (int pp = 1; pp < P; ++pp) v += red[pp][h][k];
+      const float L = Lsh[h], M = Msh[h];
+      if (has_window && L > 0.f && M > -INFINITY) {
+        const float* Pw = P0 + (int64_t)s_eff * sstride + h * (D + 2);
+        const float ms = Pw[0];
+        if (ms > -INFINITY) v += __expf(ms - M) * Pw[2 + k] / L;
+      }
+      const int64_t idx = ((int64_t)b * Hq + h0 + h) * D + k;
+      if constexpr (OUT == TQ_F32)
+        ((float*)out)[idx] = v;
+      else if constexpr (OUT == TQ_BF16)
+        ((uint16_t*)out)[idx] = (uint16_t)f32_to_bf16_bits(v);
+      else
+        ((uint16_t*)out)[idx] = (uint16_t)f32_to_f16_bits(v);
+      if (k == 0 && lse) lse[(int64_t)b * Hq + h0 + h] = L > 0.f ? M + logf(L) : -INFINITY;
     }
-    const int64_t idx = ((int64_t)b * Hq + h) * D + k;
-    if constexpr (OUT == TQ_F32)
-      ((float*)out)[idx] = v;
-    else if constexpr (OUT == TQ_BF16)
-      ((uint16_t*)out)[idx] = (uint16_t)f32_to_bf16_bits(v);
-    else
-      ((uint16_t*)out)[idx] = (uint16_t)f32_to_f16_bits(v);
-    if (k == 0 && lse) lse[(int64_t)b * Hq + h] = L > 0.f ? M + logf(L) : -INFINITY;
   }
 }
 
-template <int D, int P>
+template <int D, int P, int HB>
 static void launch_qrot(const tq_attn_params* p, const float* pikt, int64_t rs, float* dst, hipStream_t st) {
-  hipLaunchKernelGGL((qrot_kernel<D, P>), dim3(p->batch, p->num_q_heads), dim3(D * P), 0, st, p->q, p->q_dtype, pikt,
-                     rs, p->num_q_heads, p->batch_per_rot, dst);
+  const unsigned hb = (unsigned)((p->num_q_heads + HB - 1) / HB);
+  hipLaunchKernelGGL((qrot_kernel<D, P, HB>), dim3(p->batch, hb), dim3(D * P), 0, st, p->q, p->q_dtype, pikt, rs,
+                     p->num_q_heads, p->batch_per_rot, dst);
 }
 template <int D>
 static void launch_qrot_any(const tq_attn_params* p, const float* pikt, int64_t rs, float* dst, hipStream_t st) {
   if (few_heads(p->batch, p->num_q_heads))
-    launch_qrot<D, parts_few<D>()>(p, pikt, rs, dst, st);
+    launch_qrot<D, parts_few<D>(), 1>(p, pikt, rs, dst, st);
   else
-    launch_qrot<D, kPartsMany>(p, pikt, rs, dst, st);
+    launch_qrot<D, kPartsMany, kHeadsMany>(p, pikt, rs, dst, st);
 }
 
-template <int D, int OUT, int P>
+template <int D, int OUT, int P, int HB>
 static void launch_merge(const tq_attn_params* p, const float* part, int s_eff, int has_win, const float* piv,
                          int64_t rs, hipStream_t st) {
-  hipLaunchKernelGGL((merge_kernel<D, OUT, P>), dim3(p->batch, p->num_q_heads), dim3(D * P), 0, st, part, s_eff,
-                     has_win, p->batch, p->num_q_heads, p->batch_per_rot, piv, rs, p->out, p->lse);
+  const unsigned hb = (unsigned)((p->num_q_heads + HB - 1) / HB);
+  hipLaunchKernelGGL((merge_kernel<D, OUT, P, HB>), dim3(p->batch, hb), dim3(D * P), 0, st, part, s_eff, has_win,
+                     p->batch, p->num_q_heads, p->batch_per_rot, piv, rs, p->out, p->lse);
 }
 template <int D, int OUT>
 static void launch_merge_p(const tq_attn_params* p, const float* part, int s_eff, int has_win, const float* piv,
                            int64_t rs, hipStream_t st) {
   if (few_heads(p->batch, p->num_q_heads))
-    launch_merge<D, OUT, parts_few<D>()>(p, part, s_eff, has_win, piv, rs, st);
+    launch_merge<D, OUT, parts_few<D>(), 1>(p, part, s_eff, has_win, piv, rs, st);
   else
-    launch_merge<D, OUT, kPartsMany>(p, part, s_eff, has_win, piv, rs, st);
+    launch_merge<D, OUT, kPartsMany, kHeadsMany>(p, part, s_eff, has_win, piv, rs, st);
 }
 
 // Resident waves per CU of the fused-attention kernel instance (registers and LDS as compiled),
