@@ -6,8 +6,10 @@
 // Layout mirrors the encode: a wave owns 32 vectors; lane (v, hh) reads the packed chunk of
 // rotated coordinates hh*d/2 .. +d/2 of vector v and turns 8 codes at a time into fp16 MFMA B
 // operands; 32x32x16 fp16 MFMAs against prebuilt tiles of Pi^T (resident in LDS) leave 16
-// consecutive output coordinates of one vector in a lane's accumulator, which are scaled by n,
-// staged in LDS and stored with the wave's other rows as whole 16-byte-per-lane blocks.
+// consecutive output coordinates of one vector in a lane's accumulator (tile t, half hh:
+// coordinates 32t + 16hh .. +16 of the slice), which are scaled by n, staged in LDS and stored
+// 128 bytes of each of the wave's 32 rows at a time (a full cache line per row), 1 KiB per
+// store instruction. With that small staging area a CU holds 12 waves at d = 128.
 //
 // Precision. A 16-bit output is the float64 decode rounded to nearest even, so the kernel's
 // unrounded value must sit far closer to the float64 one than a 16-bit ulp: single fp16
@@ -78,25 +80,26 @@ struct DecGeo {
   // the lo table starts LO_OFF bytes after the hi one: further apart than one two-address LDS
   // read reaches and not a multiple of its stride, so each word is read into its own register
   static constexpr int LO_OFF = (TAB_B > 2048 ? TAB_B : 2048) + 8;
-  // Launch shape. The decode is bound by its output stores, and HBM write throughput falls
-  // when many waves keep stores in flight, so every head size runs 8 waves per CU: d = 64 in
-  // two 4-wave workgroups, d = 128 and 256 in one 8-wave workgroup (the tile sets take
-  // 64 KiB); float32 outputs at d = 128 stage twice the bytes, so 4 waves there.
-  static constexpr int WAVES = D == 64 ? 4 : ((D == 128 && OUT == TQ_F32) ? 4 : 8);
+  // Launch shape: d = 64 in two 4-wave workgroups per CU, d = 128 in one 12-wave workgroup
+  // (3 waves per SIMD within 170 registers; the tile sets take 64 KiB of LDS), d = 256 in one
+  // 8-wave workgroup per slice (up to 256 registers).
+  static constexpr int WAVES = D == 64 ? 4 : (D == 128 ? 12 : 8);
   static constexpr int WG_PER_CU = D == 64 ? 2 : 1;
-  // staging: 32 rows of the slice's SB bytes, each padded by 16 bytes so that rows written by
-  // consecutive lanes start in different banks
-  static constexpr int SB = SC * E;
-  static constexpr int STG_ROW = SB + 16;
+  static constexpr int WPE = WAVES * WG_PER_CU / 4;   // waves per SIMD
+  static constexpr int SB = SC * E;                    // output bytes of a row in this slice
+  // Outputs go out in flushes of FT tiles, 128 bytes of each of the wave's 32 rows (tile t holds
+  // slice coordinates 32t .. 32t+31): staged as 32 rows of 128 bytes, each padded by 16 bytes
+  // so that rows written by consecutive lanes start in different banks.
+  static constexpr int FT = 128 / (32 * E);
+  static constexpr int STG_ROW = 128 + 16;
   static constexpr size_t stage_bytes = (size_t)32 * STG_ROW;
   static constexpr size_t lds_bytes = (size_t)FRAG_U4 * 16 + (size_t)WAVES * stage_bytes;
   static_assert(lds_bytes + LO_OFF + TAB_B <= 160 * 1024, "decode LDS budget");
-  static_assert(1024 % SB == 0, "a 1 KiB store covers whole staged rows");
+  static_assert(TS % FT == 0, "whole flushes per slice");
 };
 
-// 8 waves per CU are 2 per SIMD: up to 256 registers per wave
 template <int D, int BITS, int OUT>
-constexpr int dec_wpe() { return 2; }
+constexpr int dec_wpe() { return DecGeo<D, BITS, OUT>::WPE; }
 
 template <int D, int BITS, int OUT, bool SLOT>
 __global__ void __launch_bounds__((DecGeo<D, BITS, OUT>::WAVES * 64))
@@ -233,9 +236,10 @@ decode_kernel(DecodeKArgs a) {
   // per-lane LDS and output offsets (the rest of every address is a constant)
   constexpr int CPT = E;                            // 16-byte chunks per lane per tile (16 outputs)
   constexpr uint32_t RB = D * E;                    // bytes per output row
-  constexpr uint32_t ROWS_PER_STORE = 1024 / Geo::SB;
-  uint8_t* const stg_w = stg + vl * Geo::STG_ROW + 16 * hh * (Geo::SC / 2 * E / 16);
-  const uint32_t lrow = (uint32_t)(16 * lane) / Geo::SB, lchunk = ((uint32_t)(16 * lane) % Geo::SB) / 16;
+  // lane (v, hh) stages tile t's 16 outputs at byte (t % FT) * 32E + 16hh*E of staged row v; a
+  // flush stores 8 rows per instruction, lane l the 16 bytes at 16(l % 8) of row l / 8
+  uint8_t* const stg_w = stg + vl * Geo::STG_ROW + 16 * hh * E;
+  const uint32_t lrow = (uint32_t)lane >> 3, lchunk = (uint32_t)lane & 7u;
   const uint8_t* const stg_r = stg + lrow * Geo::STG_ROW + 16 * lchunk;
   const uint32_t out_off = lrow * RB + (uint32_t)q * Geo::SB + 16 * lchunk;
 
@@ -285,6 +289,8 @@ decode_kernel(DecodeKArgs a) {
     uint32_t aoff = (uint32_t)lane * 16u;
     asm volatile("" : "+v"(aoff));
     f32x16 accp[2];
+    const uint32_t nv = valid_rows(tl);
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc((uint8_t*)a.out + (nv ? vbase : 0) * RB, nv * RB);
 #pragma unroll
     for (int t = 0; t < TS; ++t) {
       if (t % 2 == 0) {
@@ -306,12 +312,12 @@ decode_kernel(DecodeKArgs a) {
         }
       }
       const f32x16 acc = accp[t % 2];
-      // scaled outputs of slice coordinates hh*SC/2 + 16t .. +16 as CPT 16-byte chunks, staged
-      // at chunk hh*SC/2*E/16 + t*CPT + k of the lane's row
+      // scaled outputs of slice coordinates 32t + 16hh .. +16 as CPT 16-byte chunks
+      const int tb = (t % Geo::FT) * 32 * E;
       if constexpr (OUT == TQ_F32) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *(u32x4*)(stg_w + 16 * (t * CPT + q4)) =
+          *(u32x4*)(stg_w + tb + 16 * q4) =
               u32x4{__float_as_uint(acc[4 * q4] * ns), __float_as_uint(acc[4 * q4 + 1] * ns),
                     __float_as_uint(acc[4 * q4 + 2] * ns), __float_as_uint(acc[4 * q4 + 3] * ns)};
       } else {
@@ -321,20 +327,22 @@ decode_kernel(DecodeKArgs a) {
           const float lo = acc[2 * j] * ns, hi = acc[2 * j + 1] * ns;
           w[j] = OUT == TQ_BF16 ? pack_bf16x2(lo, hi) : pack_f16x2(lo, hi);
         }
-        *(u32x4*)(stg_w + 16 * (t * CPT)) = u32x4{w[0], w[1], w[2], w[3]};
-        *(u32x4*)(stg_w + 16 * (t * CPT + 1)) = u32x4{w[4], w[5], w[6], w[7]};
+        *(u32x4*)(stg_w + tb) = u32x4{w[0], w[1], w[2], w[3]};
+        *(u32x4*)(stg_w + tb + 16) = u32x4{w[4], w[5], w[6], w[7]};
       }
-    }
-    // the wave's 32 staged rows go out 1 KiB per store instruction (whole rows of the slice,
-    // full cache lines), through a buffer resource over the tile's rows: rows past the end are
-    // dropped by its range check. Non-temporal: the decoded stream is far larger than the
-    // caches, and left in them as dirty lines it is written back during whatever kernel runs next.
-    const uint32_t nv = valid_rows(tl);
-    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc((uint8_t*)a.out + (nv ? vbase : 0) * RB, nv * RB);
+      if (t % Geo::FT == Geo::FT - 1) {
+        // flush: 128 bytes of each of the 32 rows (a full cache line each), 1 KiB per store
+        // instruction, through a buffer resource over the tile's rows (rows past the end are
+        // dropped by its range check). Non-temporal: the decoded stream is far larger than the
+        // caches, and left in them as dirty lines it is written back during whatever kernel
+        // runs next.
+        const uint32_t fo = (uint32_t)(t / Geo::FT) * 128u;
 #pragma unroll
-    for (uint32_t j = 0; j < 32 / ROWS_PER_STORE; ++j) {
-      const u32x4 qv = *(const u32x4*)(stg_r + j * ROWS_PER_STORE * Geo::STG_ROW);
-      __builtin_amdgcn_raw_buffer_store_b128(qv, ro, out_off + j * ROWS_PER_STORE * RB, 0, 2 /* nt */);
+        for (uint32_t j = 0; j < 4; ++j) {
+          const u32x4 qv = *(const u32x4*)(stg_r + j * 8 * Geo::STG_ROW);
+          __builtin_amdgcn_raw_buffer_store_b128(qv, ro, out_off + fo + j * 8 * RB, 0, 2 /* nt */);
+        }
+      }
     }
   };
 

@@ -365,7 +365,8 @@ static void build_tiles(int d, F value, uint16_t* dst, bool paired = false) {
 // Decode tiles of Pi^T: as build_tiles (column order hh*d/2 + 8 kb, the B operands come from a
 // lane's packed chunk), with the output coordinates cut into qs slices of d/qs: slice q's tiles
 // t' = 0 .. T/qs - 1 come first, and lane (vector v, half hh) ends up holding the slice
-// coordinates q*d/qs + hh*d/(2 qs) + 16 t' + i in accumulator register i. Each slice holds two
+// coordinates q*d/qs + 32 t' + 16 hh + i in accumulator register i (a tile covers 32
+// consecutive coordinates, so pairs of tiles give whole 128-byte pieces of a 16-bit row). Each slice holds two
 // sets, `value(row, col, set)` for set 0 then set 1.
 template <typename F>
 static void build_dec_tiles(int d, int qs, F value, uint16_t* dst) {
@@ -377,7 +378,7 @@ static void build_dec_tiles(int d, int qs, F value, uint16_t* dst) {
         for (int kb = 0; kb < KB; ++kb)
           for (int lane = 0; lane < 64; ++lane) {
             const int m = lane % 32, hh = lane / 32;
-            const int row = q * sc + ((m / 4) % 2) * (sc / 2) + 16 * t + 4 * (m / 8) + m % 4;
+            const int row = q * sc + 32 * t + 16 * ((m / 4) % 2) + 4 * (m / 8) + m % 4;
             for (int e = 0; e < 8; ++e) dst[o++] = value(row, hh * (d / 2) + 8 * kb + e, set);
           }
 }
