@@ -83,7 +83,10 @@ struct DecGeo {
   // Launch shape: d = 64 in two 4-wave workgroups per CU, d = 128 in one 12-wave workgroup
   // (3 waves per SIMD within 170 registers; the tile sets take 64 KiB of LDS), d = 256 in one
   // 8-wave workgroup per slice (up to 256 registers).
-  static constexpr int WAVES = D == 64 ? 4 : (D == 128 ? 12 : 8);
+  // d = 256 (two tiles per slice) looks its operands up one K block at a time, which keeps it
+  // within 128 registers: 16 waves per CU
+  static constexpr bool KB_OUTER = D == 256;
+  static constexpr int WAVES = D == 64 ? 4 : (D == 128 ? 12 : 16);
   static constexpr int WG_PER_CU = D == 64 ? 2 : 1;
   static constexpr int WPE = WAVES * WG_PER_CU / 4;   // waves per SIMD
   static constexpr int SB = SC * E;                    // output bytes of a row in this slice
@@ -250,10 +253,8 @@ decode_kernel(DecodeKArgs a) {
 
     // ---- codes -> fp16 centroids (hi and lo), 8 per K block (the lane's codes 8kb .. 8kb+7),
     //      every word read from its table straight into its operand register
-    u32x4 bhi[KB], blo[KB];
     const char* tb = (const char*)tab;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    auto lookup = [&](int kb, u32x4& bh, u32x4& bl) {
       if constexpr (BITS == 2) {
         // 8 codes = 16 bits = two table bytes, two fp16 words each
 #pragma unroll
@@ -264,8 +265,8 @@ decode_kernel(DecodeKArgs a) {
           const uint32_t off = (s >= 3 ? (w >> (s - 3)) : (w << (3 - s))) & (255u << 3);
           const u32x2 eh = *(const u32x2*)(tb + off);
           const u32x2 el = *(const u32x2*)(tb + Geo::LO_OFF + off);
-          bhi[kb][2 * h] = eh[0]; bhi[kb][2 * h + 1] = eh[1];
-          blo[kb][2 * h] = el[0]; blo[kb][2 * h + 1] = el[1];
+          bh[2 * h] = eh[0]; bh[2 * h + 1] = eh[1];
+          bl[2 * h] = el[0]; bl[2 * h + 1] = el[1];
         }
       } else {
 #pragma unroll
@@ -278,10 +279,15 @@ decode_kernel(DecodeKArgs a) {
             off = (s >= 2 ? (cw[pos >> 5] >> (s - 2)) : (cw[pos >> 5] << (2 - s))) & (((1u << PB) - 1u) << 2);
           else
             off = funnel(cw[(pos >> 5) + 1], cw[pos >> 5], s - 2) & (((1u << PB) - 1u) << 2);
-          bhi[kb][c] = *(const uint32_t*)(tb + off);
-          blo[kb][c] = *(const uint32_t*)(tb + Geo::LO_OFF + off);
+          bh[c] = *(const uint32_t*)(tb + off);
+          bl[c] = *(const uint32_t*)(tb + Geo::LO_OFF + off);
         }
       }
+    };
+    u32x4 bhi[Geo::KB_OUTER ? 1 : KB], blo[Geo::KB_OUTER ? 1 : KB];
+    if constexpr (!Geo::KB_OUTER) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) lookup(kb, bhi[kb], blo[kb]);
     }
 
     // ---- inverse rotation (an opaque offset keeps the Pi^T tiles in LDS instead of letting
@@ -297,18 +303,42 @@ decode_kernel(DecodeKArgs a) {
         // two independent accumulation chains in flight
         accp[0] = f32x16{};
         accp[1] = f32x16{};
+        if constexpr (Geo::KB_OUTER) {
+          // the operands of one K block at a time, looked up one block ahead (two register sets),
+          // so only 16 operand registers are live
+          u32x4 bh[2], bl[2];
+          lookup(0, bh[0], bl[0]);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const char* s0 = (const char*)smem + aoff + (t * KB + kb) * 1024;
-          const char* s1 = (const char*)smem + aoff + ((t + 1) * KB + kb) * 1024;
-          const u32x4 a1_0 = *(const u32x4*)s0, a2_0 = *(const u32x4*)(s0 + Geo::SET_U4 * 16);
-          const u32x4 a1_1 = *(const u32x4*)s1, a2_1 = *(const u32x4*)(s1 + Geo::SET_U4 * 16);
-          accp[0] = mfma32_f16(a1_0, bhi[kb], accp[0]);
-          accp[1] = mfma32_f16(a1_1, bhi[kb], accp[1]);
-          accp[0] = mfma32_f16(a2_0, bhi[kb], accp[0]);
-          accp[1] = mfma32_f16(a2_1, bhi[kb], accp[1]);
-          accp[0] = mfma32_f16(a1_0, blo[kb], accp[0]);
-          accp[1] = mfma32_f16(a1_1, blo[kb], accp[1]);
+          for (int kb = 0; kb < KB; ++kb) {
+            if (kb + 1 < KB) lookup(kb + 1, bh[(kb + 1) & 1], bl[(kb + 1) & 1]);
+            const u32x4 h = bh[kb & 1], l = bl[kb & 1];
+            const char* s0 = (const char*)smem + aoff + (t * KB + kb) * 1024;
+            const char* s1 = (const char*)smem + aoff + ((t + 1) * KB + kb) * 1024;
+            const u32x4 a1_0 = *(const u32x4*)s0, a2_0 = *(const u32x4*)(s0 + Geo::SET_U4 * 16);
+            const u32x4 a1_1 = *(const u32x4*)s1, a2_1 = *(const u32x4*)(s1 + Geo::SET_U4 * 16);
+            accp[0] = mfma32_f16(a1_0, h, accp[0]);
+            accp[1] = mfma32_f16(a1_1, h, accp[1]);
+            accp[0] = mfma32_f16(a2_0, h, accp[0]);
+            accp[1] = mfma32_f16(a2_1, h, accp[1]);
+            accp[0] = mfma32_f16(a1_0, l, accp[0]);
+            accp[1] = mfma32_f16(a1_1, l, accp[1]);
+            // keep the scheduler from pulling every later block's lookups ahead of these MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const char* s0 = (const char*)smem + aoff + (t * KB + kb) * 1024;
+            const char* s1 = (const char*)smem + aoff + ((t + 1) * KB + kb) * 1024;
+            const u32x4 a1_0 = *(const u32x4*)s0, a2_0 = *(const u32x4*)(s0 + Geo::SET_U4 * 16);
+            const u32x4 a1_1 = *(const u32x4*)s1, a2_1 = *(const u32x4*)(s1 + Geo::SET_U4 * 16);
+            accp[0] = mfma32_f16(a1_0, bhi[kb], accp[0]);
+            accp[1] = mfma32_f16(a1_1, bhi[kb], accp[1]);
+            accp[0] = mfma32_f16(a2_0, bhi[kb], accp[0]);
+            accp[1] = mfma32_f16(a2_1, bhi[kb], accp[1]);
+            accp[0] = mfma32_f16(a1_0, blo[kb], accp[0]);
+            accp[1] = mfma32_f16(a1_1, blo[kb], accp[1]);
+          }
         }
       }
       const f32x16 acc = accp[t % 2];
