@@ -259,6 +259,29 @@ def test_paged_any_block_size(dev, block):
                  "paged block %d" % block)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bk", [2, 3, 4])
+@pytest.mark.parametrize("bv", [2, 3, 4])
+def test_paged_ragged_every_width_pair(dev, d, bk, bv):
+    """Every (K, V) width pair of the paged ragged workload, per head size, through the paged
+    path with its head shape (8 KV heads, 32 query heads, pages of 16) on a few ragged
+    sequences: scores and attention against the oracle over every sequence."""
+    S, Hkv, Hq = 5, 8, 32
+    log("case: paged widths d%d K%dV%d" % (d, bk, bv))
+    c = _paged(dev, S, 400, Hkv, Hq, d, bk, bv, seed=40 + 3 * bk + bv, oracle_rows="all")
+    lay = c["lay"]
+    args = dict(seq_lens=lay.seq_lens.to(dev), max_seq_len=int(lay.seq_lens.max()),
+                block_table=lay.block_table.to(dev), block_size=16, num_kv_heads=Hkv)
+    o, lse = tq.attn_decode(c["ck"], c["rk"], c["cv"], c["rv"], c["q"], c["kp"], c["kn"], c["vp"], c["vn"],
+                            out_dtype=torch.float32, return_lse=True, **args)
+    s = tq.scores_compressed(c["ck"], c["rk"], c["q"], c["kp"], c["kn"], **args)
+    torch.cuda.synchronize()
+    _check_paged(c, d, bk, bv, o.cpu().numpy().astype(np.float64), lse.cpu().numpy(), range(S),
+                 "paged widths d%d K%dV%d" % (d, bk, bv))
+    _check_paged_scores(c, d, bk, s.cpu().numpy().astype(np.float64), range(S),
+                        "paged widths d%d K%d scores" % (d, bk))
+
+
 def test_fused_attention_workload_full(dev):
     """Batch 32, 32 query heads over 8 KV heads, context 32768, d=128, K4/V2, bf16 queries, in the
     launch configuration the bench times. The cache is random code bytes with log-normal norms
