@@ -82,9 +82,8 @@ struct DecGeo {
   static constexpr int LO_OFF = (TAB_B > 2048 ? TAB_B : 2048) + 8;
   // Launch shape: d = 64 in two 4-wave workgroups per CU, d = 128 in one 12-wave workgroup
   // (3 waves per SIMD within 170 registers; the tile sets take 64 KiB of LDS), d = 256 in one
-  // 8-wave workgroup per slice (up to 256 registers).
-  // d = 256 (two tiles per slice) looks its operands up one K block at a time, which keeps it
-  // within 128 registers: 16 waves per CU
+  // 16-wave workgroup per CU: with two tiles per slice it looks its operands up one K block at a
+  // time (KB_OUTER), which keeps it within 128 registers.
   static constexpr bool KB_OUTER = D == 256;
   static constexpr int WAVES = D == 64 ? 4 : (D == 128 ? 12 : 16);
   static constexpr int WG_PER_CU = D == 64 ? 2 : 1;
@@ -237,7 +236,6 @@ decode_kernel(DecodeKArgs a) {
   wait_vmem_all();
 
   // per-lane LDS and output offsets (the rest of every address is a constant)
-  constexpr int CPT = E;                            // 16-byte chunks per lane per tile (16 outputs)
   constexpr uint32_t RB = D * E;                    // bytes per output row
   // lane (v, hh) stages tile t's 16 outputs at byte (t % FT) * 32E + 16hh*E of staged row v; a
   // flush stores 8 rows per instruction, lane l the 16 bytes at 16(l % 8) of row l / 8
@@ -342,7 +340,7 @@ decode_kernel(DecodeKArgs a) {
         }
       }
       const f32x16 acc = accp[t % 2];
-      // scaled outputs of slice coordinates 32t + 16hh .. +16 as CPT 16-byte chunks
+      // scaled outputs of slice coordinates 32t + 16hh .. +16 as E 16-byte chunks
       const int tb = (t % Geo::FT) * 32 * E;
       if constexpr (OUT == TQ_F32) {
 #pragma unroll
