@@ -12,15 +12,26 @@
 // store instruction. With that small staging area a CU holds 12 waves at d = 128.
 //
 // Precision. A 16-bit output is the float64 decode rounded to nearest even, so the kernel's
-// unrounded value must sit far closer to the float64 one than a 16-bit ulp: single fp16
+// unrounded value must sit well inside a 16-bit half-ulp of the float64 one; single fp16
 // operands (2^-12 relative each) leave ~3e-4 of the norm, which changes the rounding of many
-// elements. Both operands are therefore split: Pi^T = P_hi + P_lo and c = c_hi + c_lo with
-// every part in fp16, and
-//   2^19 Pi^T c ~ (2^11 P_hi)(2^8 c_hi) + (2^11 P_lo)(2^8 c_hi) + (2^11 P_hi)(2^8 c_lo),
-// three products into one fp32 accumulator (the scalings keep every low part a normal fp16
-// number; P_lo c_lo, ~2^-24 relative, is dropped). Measured in a float emulation: at most
-// ~1.2e-7 of the vector norm per element. The A1 = 2^11 P_hi operand is read once for two
-// products, so LDS reads grow by half a tile set per product, not by two.
+// elements. Pi^T is therefore split, Pi^T = P_hi + P_lo with both parts in fp16 (2^-22
+// relative). The centroid operand takes one of two forms:
+//  * fp16 and float32 outputs, and 4-bit codebooks: c = c_hi + c_lo, and
+//      2^19 Pi^T c ~ (2^11 P_hi)(2^8 c_hi) + (2^11 P_lo)(2^8 c_hi) + (2^11 P_hi)(2^8 c_lo),
+//    three products into one fp32 accumulator (the scalings keep every low part a normal fp16
+//    number; P_lo c_lo, ~2^-24 relative, is dropped): ~1.2e-7 of the vector norm per element
+//    in a float emulation;
+//  * bfloat16 outputs of 2- and 3-bit codebooks: one operand. A codebook has only 2^(bits-1)
+//    centroid magnitudes, and the host picks a scale alpha in [1, 2) under which every
+//    2^8 alpha c_k is within rho <= 2.5e-5 (relative) of an fp16 value c'_k; then
+//      2^19 alpha Pi^T c ~ (2^11 P_hi) c' + (2^11 P_lo) c',
+//    two products, and since every row of Pi^T has unit norm, each element is within
+//    rho ||x|| of the result with exact centroids (Cauchy-Schwarz): a fifth of a bfloat16
+//    half-ulp at a coordinate of typical size ||x|| / sqrt(d) at worst, and as a sum of d
+//    terms of either sign typically ~1/sqrt(d) of that. The 1/alpha goes into the norm
+//    multiplier.
+// The A1 = 2^11 P_hi operand is read once for two products, so LDS reads grow by half a tile
+// set per product, not by two.
 //
 // Instruction budget. On gfx950 the vector ALU and LDS instructions of a SIMD issue largely
 // in series with its MFMAs (a probe that gives each wave independent fp32 FMAs next to its
@@ -52,8 +63,9 @@ struct DecodeKArgs {
   void* out;
   const uint8_t* zero;   // zeros that masked lanes load with a slot gather (>= one packed chunk)
   int64_t n, vpr;
-  uint32_t chi[8];       // 2^8 c_hi as fp16, two per word
-  uint32_t clo[8];       // 2^8 c_lo as fp16, two per word
+  float nscale;          // x_hat = acc * n * nscale
+  uint32_t chi[8];       // 2^8 c_hi (or 2^8 alpha c) as fp16, two per word
+  uint32_t clo[8];       // 2^8 c_lo as fp16, two per word (three-product decodes)
 };
 
 template <int D, int BITS, int OUT>
@@ -67,6 +79,7 @@ struct DecGeo {
   static constexpr int CHUNK_DW = CHUNK / 4;
   static constexpr int G = (CHUNK % 16 == 0 && ROW % 16 == 0) ? 16 : ((CHUNK % 8 == 0 && ROW % 8 == 0) ? 8 : 4);
   static constexpr int E = OUT == TQ_F32 ? 4 : 2;  // output bytes per element
+  static constexpr bool P3 = !decode_one_operand(BITS, OUT);   // c_hi + c_lo: three products
   static constexpr int SET_U4 = TS * KB * 64;       // one tile set of a slice, in u32x4
   static constexpr int FRAG_U4 = 2 * SET_U4;        // A1 and A2
   // Code -> centroid tables, a hi table and a lo table: 2-bit codes go four at a time (one
@@ -217,7 +230,7 @@ decode_kernel(DecodeKArgs a) {
     constexpr int EW = Geo::ENTRY_B / 4;   // words per entry
     for (int j = threadIdx.x; j < Geo::TAB_N; j += blockDim.x) {
 #pragma unroll
-      for (int part = 0; part < 2; ++part) {
+      for (int part = 0; part < (Geo::P3 ? 2 : 1); ++part) {
         const uint32_t* kc = part ? klo : khi;
         uint32_t* t = tab + part * (Geo::LO_OFF / 4) + EW * j;
         if constexpr (Geo::PER_LOOKUP == 4) {
@@ -246,8 +259,8 @@ decode_kernel(DecodeKArgs a) {
 
   auto decode_tile = [&](const uint32_t (&cw)[DW], float nrm, int64_t tl) {
     const int64_t vbase = v_begin + tl * 32;
-    // x_hat = acc * n * 2^-19 (the operand scalings, a power of two)
-    const float ns = nrm * 0x1p-19f;
+    // x_hat = acc * n * 2^-19 (the operand scalings), / alpha with the single-operand table
+    const float ns = nrm * a.nscale;
 
     // ---- codes -> fp16 centroids (hi and lo), 8 per K block (the lane's codes 8kb .. 8kb+7),
     //      every word read from its table straight into its operand register
@@ -262,9 +275,10 @@ decode_kernel(DecodeKArgs a) {
           const int s = p & 31;
           const uint32_t off = (s >= 3 ? (w >> (s - 3)) : (w << (3 - s))) & (255u << 3);
           const u32x2 eh = *(const u32x2*)(tb + off);
-          const u32x2 el = *(const u32x2*)(tb + Geo::LO_OFF + off);
+          u32x2 el{};
+          if constexpr (Geo::P3) el = *(const u32x2*)(tb + Geo::LO_OFF + off);
           bh[2 * h] = eh[0]; bh[2 * h + 1] = eh[1];
-          bl[2 * h] = el[0]; bl[2 * h + 1] = el[1];
+          if constexpr (Geo::P3) { bl[2 * h] = el[0]; bl[2 * h + 1] = el[1]; }
         }
       } else {
 #pragma unroll
@@ -278,11 +292,11 @@ decode_kernel(DecodeKArgs a) {
           else
             off = funnel(cw[(pos >> 5) + 1], cw[pos >> 5], s - 2) & (((1u << PB) - 1u) << 2);
           bh[c] = *(const uint32_t*)(tb + off);
-          bl[c] = *(const uint32_t*)(tb + Geo::LO_OFF + off);
+          if constexpr (Geo::P3) bl[c] = *(const uint32_t*)(tb + Geo::LO_OFF + off);
         }
       }
     };
-    u32x4 bhi[Geo::KB_OUTER ? 1 : KB], blo[Geo::KB_OUTER ? 1 : KB];
+    u32x4 bhi[Geo::KB_OUTER ? 1 : KB], blo[Geo::KB_OUTER ? 1 : KB]{};
     if constexpr (!Geo::KB_OUTER) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) lookup(kb, bhi[kb], blo[kb]);
@@ -304,7 +318,7 @@ decode_kernel(DecodeKArgs a) {
         if constexpr (Geo::KB_OUTER) {
           // the operands of one K block at a time, looked up one block ahead (two register sets),
           // so only 16 operand registers are live
-          u32x4 bh[2], bl[2];
+          u32x4 bh[2], bl[2]{};
           lookup(0, bh[0], bl[0]);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
@@ -318,8 +332,10 @@ decode_kernel(DecodeKArgs a) {
             accp[1] = mfma32_f16(a1_1, h, accp[1]);
             accp[0] = mfma32_f16(a2_0, h, accp[0]);
             accp[1] = mfma32_f16(a2_1, h, accp[1]);
-            accp[0] = mfma32_f16(a1_0, l, accp[0]);
-            accp[1] = mfma32_f16(a1_1, l, accp[1]);
+            if constexpr (Geo::P3) {
+              accp[0] = mfma32_f16(a1_0, l, accp[0]);
+              accp[1] = mfma32_f16(a1_1, l, accp[1]);
+            }
             // keep the scheduler from pulling every later block's lookups ahead of these MFMAs
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -334,8 +350,10 @@ decode_kernel(DecodeKArgs a) {
             accp[1] = mfma32_f16(a1_1, bhi[kb], accp[1]);
             accp[0] = mfma32_f16(a2_0, bhi[kb], accp[0]);
             accp[1] = mfma32_f16(a2_1, bhi[kb], accp[1]);
-            accp[0] = mfma32_f16(a1_0, blo[kb], accp[0]);
-            accp[1] = mfma32_f16(a1_1, blo[kb], accp[1]);
+            if constexpr (Geo::P3) {
+              accp[0] = mfma32_f16(a1_0, blo[kb], accp[0]);
+              accp[1] = mfma32_f16(a1_1, blo[kb], accp[1]);
+            }
           }
         }
       }
@@ -402,10 +420,12 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
   k.zero = L.rot->zero();
   k.n = L.n;
   k.vpr = L.vectors_per_rot;
+  const uint16_t* hi = Geo::P3 ? L.lv.dec_c_hi : L.lv.dec_c_one;
   for (int j = 0; j < 8; ++j) {
-    k.chi[j] = (uint32_t)L.lv.dec_c_hi[2 * j] | ((uint32_t)L.lv.dec_c_hi[2 * j + 1] << 16);
+    k.chi[j] = (uint32_t)hi[2 * j] | ((uint32_t)hi[2 * j + 1] << 16);
     k.clo[j] = (uint32_t)L.lv.dec_c_lo[2 * j] | ((uint32_t)L.lv.dec_c_lo[2 * j + 1] << 16);
   }
+  k.nscale = Geo::P3 ? 0x1p-19f : L.lv.dec_one_nscale;
   const int64_t per_rot = L.vectors_per_rot ? L.vectors_per_rot : L.n;
   const int nrot = L.vectors_per_rot ? (int)((L.n + L.vectors_per_rot - 1) / L.vectors_per_rot) : 1;
   const int64_t tiles = (per_rot + 31) / 32;

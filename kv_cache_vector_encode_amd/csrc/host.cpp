@@ -214,6 +214,50 @@ static double from_f16(uint16_t h) {
   return (h & 0x8000) ? -v : v;
 }
 
+// Relative error of rounding v > 0 (in fp16's normal range) to fp16: 11 significant bits,
+// round to nearest even.
+static double f16_rel_err(double v) {
+  int e;
+  const double x = std::ldexp(std::frexp(v, &e), 11);   // in [1024, 2048)
+  return std::fabs(x - std::nearbyint(x)) / x;
+}
+
+// The decode's single-operand table holds 2^8 alpha c_k in fp16 and scales the result by
+// 1 / alpha. The centroids are +-m_1 .. +-m_h (h = 2^(bits-1) magnitudes), so the table's
+// worst relative error is the largest over the m_j; scanning alpha over 2^20 steps of [1, 2)
+// (a power of two changes no relative error) finds one that leaves every m_j close to an
+// fp16 value: about 1e-6 for two magnitudes, 2e-5 for four, 1e-4 for eight.
+static void choose_decode_scale(Codebook& cb) {
+  const int L = (int)cb.centroids.size(), h = L / 2;
+  std::vector<double> m;
+  for (int k = h; k < L; ++k) m.push_back(256.0 * cb.centroids[k]);
+  // the largest magnitude first: fewest alphas survive it, so the scan stops early for most
+  std::sort(m.begin(), m.end(), [](double a, double b) { return a > b; });
+  double best = INFINITY, best_alpha = 1.0;
+  // only codebooks that can take the table are scanned (alpha = 1 for the others)
+  const int steps = h <= 4 ? 1 << 20 : 1;
+  for (int i = 0; i < steps; ++i) {
+    const double alpha = 1.0 + std::ldexp((double)i, -20);
+    double worst = 0.0;
+    for (double mj : m) {
+      worst = std::max(worst, f16_rel_err(alpha * mj));
+      if (worst >= best) break;
+    }
+    if (worst < best) {
+      best = worst;
+      best_alpha = alpha;
+    }
+  }
+  cb.dec_alpha = best_alpha;
+  // the bound from the table the kernels actually get
+  double rho = 0.0;
+  for (int k = 0; k < L; ++k) {
+    const double v = 256.0 * best_alpha * cb.centroids[k];
+    rho = std::max(rho, std::fabs(from_f16(to_f16(v)) - v) / std::fabs(v));
+  }
+  cb.dec_rho = rho;
+}
+
 LevelArgs make_levels(const Codebook& cb) {
   LevelArgs lv;
   std::memset(&lv, 0, sizeof(lv));
@@ -226,12 +270,15 @@ LevelArgs make_levels(const Codebook& cb) {
     const double chi = from_f16(lv.centroid_f16[k]);
     lv.dec_c_hi[k] = to_f16(256.0 * chi);
     lv.dec_c_lo[k] = to_f16(256.0 * (cb.centroids[k] - chi));
+    lv.dec_c_one[k] = to_f16(256.0 * cb.dec_alpha * cb.centroids[k]);
     lv.centroid_f32[k] = (float)cb.centroids[k];
     lv.centroid_sq[k] = (float)(cb.centroids[k] * cb.centroids[k]);
     const uint16_t hi = to_bf16((float)cb.centroids[k]);
     const uint16_t lo = to_bf16((float)(cb.centroids[k] - (double)from_bf16(hi)));
     lv.centroid_bf16x2[k] = (uint32_t)hi | ((uint32_t)lo << 16);
   }
+  lv.dec_one_nscale = (float)(0x1p-19 / cb.dec_alpha);
+  lv.dec_one_rho = (float)cb.dec_rho;
   // Quantization table: bin width just under the smallest gap between boundaries, so a bin
   // holds at most one boundary; offset = ceil(scale) + 1 so f = y * scale + offset >= 1 for
   // |y| <= 1 (the entry format needs one float exponent per bin).
@@ -552,6 +599,7 @@ tq_codebook_t* tq_codebook_init(int d, int bits) {
   }
   tq_codebook_t* h = new tq_codebook_t;
   solve_lloyd_max(d, bits, h->cb);
+  choose_decode_scale(h->cb);
   set_error("");
   return h;
 }
@@ -891,6 +939,9 @@ int tq_decode(const tq_codebook_t* cb, const tq_rotation_t* rot, int64_t vectors
   if (!aligned(out, 16)) return fail(TQ_ERR_ALIGN, "tq_decode: out must be 16-byte aligned");
   if (slot_mapping && !aligned(slot_mapping, 8)) return fail(TQ_ERR_ALIGN, "tq_decode: slot_mapping must be 8-byte aligned");
   if ((s = check_device(rot->rot, "tq_decode"))) return s;
+  if (!rot->rot.hadamard && decode_one_operand(cb->cb.bits, out_dtype) && cb->cb.dec_rho > kDecOneOperandRho)
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode: no fp16 table of this codebook's centroids is accurate enough "
+                                    "for a bfloat16 decode (relative error " + std::to_string(cb->cb.dec_rho) + ")");
   DecodeLaunch a;
   a.rot = &rot->rot;
   a.lv = make_levels(cb->cb);

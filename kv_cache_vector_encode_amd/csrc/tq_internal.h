@@ -19,7 +19,17 @@ struct Codebook {
   std::vector<double> centroids;   // [2^bits] ascending
   std::vector<double> thresholds;  // [2^bits - 1]
   double mse = 0.0;
+  // Single-fp16 decode table: every 2^8 alpha c_k rounded to fp16 is within dec_rho (relative)
+  // of its exact value; alpha in [1, 2) is chosen to make dec_rho small.
+  double dec_alpha = 1.0, dec_rho = 1.0;
 };
+
+// The largest dec_rho with which a bfloat16 decode takes one fp16 centroid operand (two MFMA
+// products) instead of a hi/lo pair (three).
+constexpr double kDecOneOperandRho = 2.5e-5;
+// Which decodes take the single-operand table: bfloat16 outputs of codebooks with at most four
+// centroid magnitudes (the scan reaches ~2e-5 there; with eight it stops near 1e-4).
+constexpr bool decode_one_operand(int bits, int out_dtype) { return out_dtype == TQ_BF16 && bits <= 3; }
 
 // Rotation stack: float64 host copy and device operand tiles.
 struct Rotation {
@@ -80,6 +90,9 @@ struct LevelArgs {
   uint16_t centroid_f16[kMaxLevels];      // c_k as fp16 bits
   uint16_t dec_c_hi[kMaxLevels];          // decode operands: 2^8 fp16(c_k) and 2^8 (c_k - fp16(c_k)),
   uint16_t dec_c_lo[kMaxLevels];          //   each as fp16 bits
+  uint16_t dec_c_one[kMaxLevels];         // 2^8 alpha c_k as fp16 bits (Codebook::dec_alpha)
+  float dec_one_nscale;                   // 2^-19 / alpha: the norm multiplier that goes with it
+  float dec_one_rho;                      // Codebook::dec_rho
   uint32_t centroid_bf16x2[kMaxLevels];   // c_k = hi + lo as bf16 bits: hi | lo << 16
   float centroid_f32[kMaxLevels];
   float centroid_sq[kMaxLevels];          // c_k^2 (float64 square, rounded once)

@@ -7,13 +7,13 @@ Bars:
     sum of squares (two chains of d/4 fused multiply-adds per lane, two adds, a square root);
   * decode: x_ref = float64 oracle decode of the same codes and norms, cast to the output
     dtype by round-to-nearest-even as the pages' decompress does. Element by element x_gpu
-    must be what the cast gives for some value within DEC_W * ||x_ref|| of x_ref: bit-exact
-    where that interval holds one representable value, either neighbour where the float64
-    value sits that close to a rounding midpoint (a rounding flip, counted like a code flip:
-    a decision both sides take in different precision). Per vector, over the elements the
-    interval determines, ||x_gpu - x_ref_cast|| <= 2e-3 ||x_ref||. DEC_W bounds the kernel's
-    unrounded error; float32 outputs take the same interval plus one float32 rounding and
-    ||x_gpu - x_ref|| <= 2e-3 ||x_ref||;
+    must be what the cast gives for some value within DEC_W[dtype] * ||x_ref|| of x_ref:
+    bit-exact where that interval holds one representable value, either neighbour where the
+    float64 value sits that close to a rounding midpoint (a rounding flip, counted like a code
+    flip: a decision both sides take in different precision). Per vector, over the elements
+    the interval determines, ||x_gpu - x_ref_cast|| <= 2e-3 ||x_ref||. DEC_W bounds the
+    kernel's unrounded error; float32 outputs take the same interval plus one float32 rounding
+    and ||x_gpu - x_ref|| <= 2e-3 ||x_ref||;
   * scores: |s_gpu - s_ref| <= 2e-3 * scale * n_t * ||q|| * ||c[idx_t]|| (Cauchy-Schwarz scale);
   * attention: ||o_gpu - o_ref|| <= 2e-3 * sum_t p_t ||v_hat_t||; |lse_gpu - lse_ref| <= the
     largest score bound of the row.
@@ -35,9 +35,14 @@ from oracle import attention as oatt, codebook as ocb, codec as occ, rotation as
 
 WINDOW = 1e-5
 REL = 2e-3
-# decode: bound on the kernel's unrounded error per element, relative to the vector norm (the
-# fp16 hi/lo operand splits give ~1.2e-7 in a float emulation of the kernel's arithmetic)
-DEC_W = 1e-6
+# decode: bound on the kernel's unrounded error per element, relative to the vector norm, by
+# output dtype. fp16 and float32 outputs: the fp16 hi/lo splits of both operands give ~1.2e-7 in
+# a float emulation of the kernel's arithmetic. bfloat16 outputs: one fp16 operand per centroid
+# (a scaled table within 2.5e-5 relative of the centroids) bounds the error by 2.5e-5 of the norm
+# (Cauchy-Schwarz over a unit row of the rotation), a fifth of a bfloat16 half-ulp at a
+# coordinate of typical size ||x|| / sqrt(d), so the window stays far inside the output's
+# own rounding.
+DEC_W = {torch.bfloat16: 3e-5, torch.float16: 1e-6, torch.float32: 1e-6}
 
 
 def log(*a):
@@ -100,7 +105,7 @@ def decode_bar(got: np.ndarray, ref: np.ndarray, dtype: torch.dtype):
     decode `ref`, both [N, d]. Returns (ok per vector, rounding flips, worst normwise error
     against the cast reference / ||ref||, rounding flips included)."""
     rn = np.linalg.norm(ref, axis=1)
-    w = DEC_W * rn[:, None]
+    w = DEC_W[dtype] * rn[:, None]
     if dtype == torch.float32:
         inside = np.abs(got - ref) <= w + 2.0 ** -24 * np.abs(ref)
         cast, determined, flips = ref, np.ones(ref.shape, bool), 0
@@ -130,8 +135,12 @@ def check_decode(out: torch.Tensor, packed: np.ndarray, norms: np.ndarray, pi: n
         raise AssertionError("%s: %d of %d vectors miss the decode bar (vector %d coord %d: gpu %.9g ref %.12g, "
                              "|ref| %.6g)" % (what, int((~ok).sum()), len(ok), i, j, got[i, j], ref[i, j],
                                               float(np.linalg.norm(ref[i]))))
-    log("%s: decode %s, worst normwise error vs the cast reference %.3g, %d rounding flips"
-        % (what, str(out.dtype)[6:], worst, flips))
+    # against the unrounded float64 decode, the output's error next to the cast's own
+    rn = np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
+    e_gpu = float(np.max(np.linalg.norm(got - ref, axis=1) / rn)) if len(rn) else 0.0
+    e_cast = float(np.max(np.linalg.norm(occ.cast(ref, out.dtype) - ref, axis=1) / rn)) if len(rn) else 0.0
+    log("%s: decode %s, worst normwise error vs the cast reference %.3g, %d rounding flips; "
+        "vs the float64 decode %.3g (the cast itself: %.3g)" % (what, str(out.dtype)[6:], worst, flips, e_gpu, e_cast))
 
 
 def rotation_pair(d: int, seeds):
