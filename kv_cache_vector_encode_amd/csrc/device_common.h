@@ -1,6 +1,8 @@
 // Device helpers for the gfx950 kernels: vector types, MFMA wrappers, conversions.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -57,6 +59,16 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
 // bits [s, s+32) of the 64-bit value hi:lo (0 <= s < 32)
 __device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t s) {
   return __builtin_amdgcn_alignbit(hi, lo, s);
+}
+
+// f(integral_constant<int, B>), ..., f(integral_constant<int, E - 1>) in order: a loop whose
+// index is a constant expression in the body
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 template <typename T>

@@ -20,14 +20,16 @@
 // significant bits, error ~1e-6): bf16 inputs are exact and take 2 passes; float32 and
 // float16 inputs are split too and take 3 (Pi_hi x_hi + Pi_lo x_hi + Pi_hi x_lo).
 //
-// Quantization: one FMA maps the unnormalized Pi x to f = y * s + o (y = Pi x / (n + 1e-8), the
-// per-vector factor s / (n + 1e-8) computed once), and a 128-entry LDS table indexed by
-// floor(f), whose bins each hold at most one decision boundary, gives the code
-// base + (f > boundary) = #{k : t_k < y} as (bits(f) - entry) >> 24: the offset keeps f >= 1,
-// so a bin's floats share one exponent and the compare is an integer subtraction whose carry
-// into bit 24 adds to the base stored above it. With the packing that is 6 VALU instructions
-// per coordinate (fma, convert, shift, subtract, shift, shift-or) where a compare chain over
-// the 2^b - 1 boundaries costs 15-20.
+// Quantization: one FMA maps the unnormalized Pi x to f = y * s + o in [1, 2) (y = Pi x /
+// (n + 1e-8), the per-vector factor s / (n + 1e-8) computed once), and a 128-bin LDS table
+// indexed by the top 7 fraction bits of f, whose bins each hold at most one decision boundary,
+// gives the code base + (f > boundary) = #{k : t_k < y} as byte 3 of bits(f) - entry: all f
+// share one exponent, so the compare is an integer subtraction whose carry into bit 24 adds to
+// the base stored above it. Byte 2 of bits(f) is the exponent's low bit and those 7 fraction
+// bits, so one byte-select shift (SDWA) makes the table address, and another shifts the code
+// (byte 3) to its place in the packed word: with the or that merges it, ~4.5 VALU instructions
+// per coordinate (fma, shift, subtract, shift, half of a three-input or) where a compare chain
+// over the 2^b - 1 boundaries costs 15-20.
 #include "device_common.h"
 #include "tq_internal.h"
 
@@ -94,6 +96,29 @@ __device__ __forceinline__ uint32_t nibble_pair_to_byte(uint32_t word, uint32_t 
   return word;
 }
 
+// (byte 2 of f) * 4: the LDS byte address of its table entry (the table at address 0)
+__device__ __forceinline__ uint32_t lut_addr(uint32_t f) {
+  uint32_t r;
+  asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+      : "=v"(r) : "v"(f));
+  return r;
+}
+// (byte 3 of w) << S and (byte 3 of w) >> S, one SDWA instruction each
+template <int S>
+__device__ __forceinline__ uint32_t byte3_shl(uint32_t w) {
+  uint32_t r;
+  asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+      : "=v"(r) : "I"(S), "v"(w));
+  return r;
+}
+template <int S>
+__device__ __forceinline__ uint32_t byte3_shr(uint32_t w) {
+  uint32_t r;
+  asm("v_lshrrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+      : "=v"(r) : "I"(S), "v"(w));
+  return r;
+}
+
 template <int D, int IN>
 constexpr int enc_waves() { return 8; }
 template <int D, int IN>
@@ -112,7 +137,9 @@ encode_kernel(EncodeKArgs a) {
   constexpr bool SPLIT_X = (IN != TQ_BF16);
   constexpr int WAVES = enc_waves<D, IN>();
   extern __shared__ u32x4 smem[];
-  __shared__ uint32_t lut[kLutBins];
+  // entries at words 128 .. 255 (byte 2 of an f in [1, 2) is 128 + its bin); words 0 .. 127
+  // repeat them for inputs that are not finite
+  __shared__ uint32_t lut[2 * kLutBins];
   __shared__ float csq[kMaxLevels];
 
   const int r = blockIdx.y;
@@ -174,7 +201,7 @@ encode_kernel(EncodeKArgs a) {
     // offset 0): indexing the by-value copy would spill the whole struct to scratch
     const uint32_t* klut = (const uint32_t*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
                                              offsetof(EncodeKArgs, lut));
-    for (int i = threadIdx.x; i < kLutBins; i += blockDim.x) lut[i] = klut[i];
+    for (int i = threadIdx.x; i < 2 * kLutBins; i += blockDim.x) lut[i] = klut[i & (kLutBins - 1)];
     const float* kcsq = (const float*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
                                        offsetof(EncodeKArgs, csq));
     if (threadIdx.x < kMaxLevels) csq[threadIdx.x] = kcsq[threadIdx.x];
@@ -253,8 +280,10 @@ encode_kernel(EncodeKArgs a) {
 #pragma unroll
     for (int w = 0; w < Geo::CHUNK_DW; ++w) pk[w] = 0u;
     uint32_t wprev = 0u;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
+    // tile t and coordinate i as compile-time constants: the packing's shift counts are
+    // instruction immediates
+    static_for<0, T>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
       // a fresh opaque offset per tile: the scheduler cannot pull later tiles' Pi reads ahead
       // (all 4 tiles' operands at once would not fit in registers)
       asm volatile("" : "+v"(aoff));
@@ -269,11 +298,11 @@ encode_kernel(EncodeKArgs a) {
         acc = mfma32_bf16(alo, xh[kb], acc);
         if constexpr (SPLIT_X) acc = mfma32_bf16(ahi, xl[kb], acc);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float f = fmaf(acc[i], fs, foff);
-        const uint32_t w = __float_as_uint(f) - lut[(uint32_t)f];   // the code is byte 3 of w
-        const int pos = (16 * t + i) * BITS;
+      static_for<0, 16>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const uint32_t fb = __float_as_uint(fmaf(acc[i], fs, foff));
+        const uint32_t w = fb - *(const uint32_t*)((const char*)lut + lut_addr(fb));   // code: byte 3
+        constexpr int pos = (16 * t + i) * BITS;
         if constexpr (BITS == 4) {
           // two codes per byte: byte 3 of the odd coordinate's w goes to the high nibble and the
           // even one's to the low nibble, written straight into byte (i % 8) / 2 of the word
@@ -288,19 +317,18 @@ encode_kernel(EncodeKArgs a) {
           }
           wprev = w;
         } else {
-          const uint32_t code = w >> 24;
-          pk[pos >> 5] |= code << (pos & 31);
-          if ((pos & 31) + BITS > 32) pk[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+          pk[pos >> 5] |= byte3_shl<(pos & 31)>(w);
+          if constexpr ((pos & 31) + BITS > 32) pk[(pos >> 5) + 1] |= byte3_shr<32 - (pos & 31)>(w);
         }
         // table reads in groups of 8: all 16 in flight at once would not fit in registers
-        if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-      }
+        if constexpr ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      });
       // finish this tile's packed words here: left alone, the compiler sinks the packing to the
       // store and keeps every table entry of the vector live until then
 #pragma unroll
       for (int w = (16 * t * BITS) >> 5; w <= ((16 * t + 16) * BITS - 1) >> 5; ++w)
         asm volatile("" : "+v"(pk[w]));
-    }
+    });
 
     // ---- norm correction (Turbo Attention page, "The codec", Norms row: the decoded key keeps
     //      the input's length): store n / ||c[idx]||, ||c[idx]||^2 summed over this lane's codes

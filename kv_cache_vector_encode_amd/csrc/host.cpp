@@ -279,36 +279,33 @@ LevelArgs make_levels(const Codebook& cb) {
   }
   lv.dec_one_nscale = (float)(0x1p-19 / cb.dec_alpha);
   lv.dec_one_rho = (float)cb.dec_rho;
-  // Quantization table: bin width just under the smallest gap between boundaries, so a bin
-  // holds at most one boundary; offset = ceil(scale) + 1 so f = y * scale + offset >= 1 for
-  // |y| <= 1 (the entry format needs one float exponent per bin).
-  double gap = INFINITY;
-  for (int k = 0; k + 1 < L - 1; ++k) gap = std::min(gap, cb.thresholds[k + 1] - cb.thresholds[k]);
-  if (!(gap < INFINITY)) gap = 1.0;   // one boundary (1 bit): any width works
-  const double w = gap * (1.0 - 1e-3);
-  lv.lut.scale = (float)(1.0 / w);
-  const float off = std::ceil(lv.lut.scale) + 1.0f;
-  lv.lut.offset = off;
+  // Quantization table: |y| <= 1 (and a little beyond, for rounding) onto f in [1, 2); the bins
+  // are 1/128 wide in f, 0.0156 in y, narrower than the boundary gaps of every codebook the
+  // kernels take (the closest are 0.016 apart, d = 256 at 4 bits); checked below.
+  lv.lut.scale = 0.5f * (1.0f - 0x1p-10f);
+  lv.lut.offset = 1.5f;
+  lv.lut.ok = true;
   float fthr[kMaxLevels];
-  for (int k = 0; k < L - 1; ++k) fthr[k] = (float)(cb.thresholds[k] / w + (double)off);
+  for (int k = 0; k < L - 1; ++k) fthr[k] = (float)(cb.thresholds[k] * (double)lv.lut.scale + 1.5);
   for (int j = 0; j < kLutBins; ++j) {
-    bool has = false;
+    const float lo = 1.0f + (float)j / 128.0f, hi = 1.0f + (float)(j + 1) / 128.0f;
+    int nb = 0;
     float thr = 0.f;
     uint32_t base = 0;
     for (int k = 0; k < L - 1; ++k) {
-      if (fthr[k] < (float)j) ++base;
-      else if (fthr[k] < (float)(j + 1)) {
+      if (fthr[k] < lo) ++base;
+      else if (fthr[k] < hi) {
         thr = fthr[k];
-        has = true;
+        ++nb;
       }
     }
+    if (nb > 1) lv.lut.ok = false;
     uint32_t e;
-    if (has) {
+    if (nb) {
       std::memcpy(&e, &thr, 4);
       e = e + 1u - (1u << 24) - (base << 24);
     } else {
-      const float lowest = j == 0 ? 0.5f : (float)j;
-      std::memcpy(&e, &lowest, 4);
+      std::memcpy(&e, &lo, 4);
       e -= base << 24;
     }
     lv.lut.entry[j] = e;
@@ -316,10 +313,6 @@ LevelArgs make_levels(const Codebook& cb) {
   return lv;
 }
 
-bool lut_covers_unit_range(const LevelArgs& lv) {
-  // |y| <= 1 must land inside the table, at f >= 1
-  return lv.lut.scale + lv.lut.offset + 1.0f < (float)kLutBins && lv.lut.offset - lv.lut.scale >= 1.0f;
-}
 
 // ------------------------------------------------------------------------------------
 // Householder QR of a d x d matrix (row-major) in float64; Q returned row-major.

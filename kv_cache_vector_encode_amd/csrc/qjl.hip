@@ -74,7 +74,7 @@ qjl_encode_kernel(QjlKArgs a) {
   constexpr int T = Geo::T, KB = Geo::KB, HALF = Geo::HALF;
   constexpr bool SPLIT_X = (IN != TQ_BF16);
   extern __shared__ u32x4 smem[];
-  __shared__ uint32_t lut[kLutBins];
+  __shared__ uint32_t lut[2 * kLutBins];   // entries at 128 + bin, repeated below
   __shared__ float cf[kMaxLevels];
 
   const int r = blockIdx.y;
@@ -90,7 +90,7 @@ qjl_encode_kernel(QjlKArgs a) {
     // tables straight from the kernel-argument segment (`a` is the only argument)
     const char* ka = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
     const uint32_t* klut = (const uint32_t*)(ka + offsetof(QjlKArgs, lut));
-    for (int i = threadIdx.x; i < kLutBins; i += blockDim.x) lut[i] = klut[i];
+    for (int i = threadIdx.x; i < 2 * kLutBins; i += blockDim.x) lut[i] = klut[i & (kLutBins - 1)];
     const float* kcf = (const float*)(ka + offsetof(QjlKArgs, cf));
     if (threadIdx.x < kMaxLevels) cf[threadIdx.x] = kcf[threadIdx.x];
   }
@@ -225,7 +225,7 @@ qjl_encode_kernel(QjlKArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float f = fmaf(acc[i], fs, foff);
-        const uint32_t code = (__float_as_uint(f) - lut[(uint32_t)f]) >> 24;
+        const uint32_t code = (__float_as_uint(f) - lut[(__float_as_uint(f) >> 16) & 255u]) >> 24;
         const int pos = (16 * t + i) * BITS;
         pk[pos >> 5] |= code << (pos & 31);
         if ((pos & 31) + BITS > 32) pk[(pos >> 5) + 1] |= code >> (32 - (pos & 31));

@@ -70,17 +70,20 @@ struct Qjl {
   const float* st(int r) const { return (const float*)((const uint8_t*)dev + st_off + (size_t)r * st_stride); }
 };
 
-// Quantization table for the encode. With f = y * scale + offset (y the rotated, normalized
-// coordinate), bin = floor(f) holds at most one decision boundary: code = base[bin] + (f > thr[bin]),
-// which equals #{k : t_k < y}. The offset keeps f >= 1 for |y| <= 1 (up to rounding: bin 0 takes
-// f in [0.5, 1)), so all f of one bin share a float exponent and their bit patterns differ by
-// less than 2^23. An entry e is chosen so that (bits(f) - e) >> 24 is the code:
+// Quantization table for the encode. f = y * scale + offset (y the rotated, normalized
+// coordinate) maps |y| < 1.0009 into [1, 2), one float binade, cut into 128 bins of width 1/128;
+// bin j is byte 2 of bits(f) minus 128 (the exponent's low bit, then the top 7 fraction bits),
+// so a kernel's table index is one byte select. Each bin holds at most one decision boundary,
+// and the code base + (f > thr) = #{k : t_k < y} is (bits(f) - e) >> 24 for the bin's entry e:
 //   bin with boundary thr:  e = bits(thr) + 1 - 2^24 - (base << 24)   (f > thr <=> bits(f) > bits(thr))
 //   bin without boundary:   e = bits(lowest f of the bin) - (base << 24)
-// The boundary is kept exactly as a float.
+// (all f of the binade share one exponent, so their bit patterns differ by less than 2^23). The
+// boundary is kept exactly as a float. Kernels hold the entries at LDS word 128 + j (byte 2 of
+// bits(f) times 4), with a second copy below for inputs that are not finite.
 constexpr int kLutBins = 128;
 struct QuantLut {
   float scale, offset;
+  bool ok;                  // every bin holds at most one boundary
   uint32_t entry[kLutBins];
 };
 
@@ -100,7 +103,7 @@ struct LevelArgs {
 };
 
 LevelArgs make_levels(const Codebook& cb);
-bool lut_covers_unit_range(const LevelArgs& lv);
+inline bool lut_covers_unit_range(const LevelArgs& lv) { return lv.lut.ok; }
 
 void set_error(const std::string& msg);
 

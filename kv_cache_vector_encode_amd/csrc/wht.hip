@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(kWhtWaves * 64) encode_wht_kernel(WhtEncArgs a
   constexpr int ELEM = IN == TQ_F32 ? 4 : 2;
   constexpr int NRAW = 32 * ELEM / 16;          // 16-byte loads per lane
   constexpr int ROW = D * BITS / 8;             // packed bytes per vector
-  __shared__ uint32_t lut[kLutBins];
+  __shared__ uint32_t lut[2 * kLutBins];   // entries at 128 + bin, repeated below
   __shared__ float csq[kMaxLevels];
 
   const int r = blockIdx.y;
@@ -154,7 +154,7 @@ __global__ void __launch_bounds__(kWhtWaves * 64) encode_wht_kernel(WhtEncArgs a
     const char* ka = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
     const uint32_t* klut = (const uint32_t*)(ka + offsetof(WhtEncArgs, lut));
     const float* kcsq = (const float*)(ka + offsetof(WhtEncArgs, csq));
-    for (int i = threadIdx.x; i < kLutBins; i += blockDim.x) lut[i] = klut[i];
+    for (int i = threadIdx.x; i < 2 * kLutBins; i += blockDim.x) lut[i] = klut[i & (kLutBins - 1)];
     if (threadIdx.x < kMaxLevels) csq[threadIdx.x] = kcsq[threadIdx.x];
   }
   const uint32_t smask = sign_mask(a.pi + r * a.pi_stride + 32 * j);
@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(kWhtWaves * 64) encode_wht_kernel(WhtEncArgs a
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const float f = fmaf(v[e], fs, foff);
-      const uint32_t code = (__float_as_uint(f) - lut[(uint32_t)f]) >> 24;
+      const uint32_t code = (__float_as_uint(f) - lut[(__float_as_uint(f) >> 16) & 255u]) >> 24;
       const int pos = e * BITS;
       pk[pos >> 5] |= code << (pos & 31);
       if ((pos & 31) + BITS > 32) pk[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
