@@ -198,7 +198,7 @@ constexpr int attn_wpe(int d, int bk, int bv, bool qjl, bool paged) {
                                                       : 3;
 }
 
-template <int D, int BK, int BV, bool SCORES, int PAGE, bool QJL>
+template <int D, int BK, int BV, bool SCORES, int PAGE, bool QJL, bool MQ>
 __global__ void __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(attn_wpe(D, BK, BV, QJL, PAGE != kDense))))
 attn_kernel(AttnKArgs a) {
   constexpr int KB = D / 32;            // K blocks of the score MFMA
@@ -291,6 +291,57 @@ attn_kernel(AttnKArgs a) {
           }
         }
     }
+  };
+  // With G <= 8 (MQ) the score MFMA's 16 columns hold (head, part): column n16 is head n16 % 8's
+  // query, its bf16 hi part for n16 < 8 and its lo part for n16 >= 8, so ONE product per K
+  // block takes both parts (the 2/3-bit keys' c_lo q_lo term comes along) and a row rotation by
+  // 8 lanes adds the two halves. Then lane n16 and lane n16 + 8 both hold head n16 % 8's score;
+  // only lanes n16 < G are heads. With G > 8 every column is a head and the parts take
+  // separate products.
+  constexpr bool merged = MQ;
+  auto query_operands_m = [&](const float* src, u32x4* dst, float f, auto dup) {
+    constexpr bool DUP = decltype(dup)::value;
+    const int hm = n16 & 7;
+    const bool ok = hm < a.G, lo = n16 >= 8;
+    float qv[D / 4];
+    const float* qp = src + ((int64_t)b * a.Hq + kvh * a.G + (ok ? hm : 0)) * D + q4 * (D / 4);
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) qv[i] = ok ? qp[i] : 0.f;
+    auto part = [&](float v) -> uint32_t {
+      const uint32_t hb = f32_to_bf16_bits(v);
+      return lo ? f32_to_bf16_bits(v - bf16_bits_to_f32(hb)) : hb;
+    };
+    if constexpr (DUP) {
+#pragma unroll
+      for (int kb = 0; kb < KB1; ++kb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t w = part(qv[4 * kb + c] * f);
+          if (wave == 0) ((uint32_t*)&dst[kb * 64 + lane])[c] = w | (w << 16);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t w0 = part(qv[8 * kb + 2 * c] * f), w1 = part(qv[8 * kb + 2 * c + 1] * f);
+          if (wave == 0) ((uint32_t*)&dst[kb * 64 + lane])[c] = w0 | (w1 << 16);
+        }
+    }
+  };
+  // head n16 % 8's score from the two halves (lanes n16 and n16 + 8 of each row of 16): one
+  // v_add_f32 with a row rotation by 8 on its first source per value. Written as asm because
+  // this compiler merged separate row-rotation builtins on the elements of one vector into a
+  // single rotation of element 0. The inputs come from ordinary VALU instructions (not straight
+  // from an MFMA), and DPP needs two wait states after a VALU write of its source: s_nop 1.
+  auto add_halves = [](float (&v)[4]) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_add_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_add_f32_dpp %2, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_add_f32_dpp %3, %3, %3 row_ror:8 row_mask:0xf bank_mask:0xf"
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
   };
   float m_run = -INFINITY, l_run = 0.f, n_run = 0.f, n_eff = 1.0f, m_eff = -INFINITY;
   f32x4 acc[TV];
@@ -454,8 +505,13 @@ attn_kernel(AttnKArgs a) {
     // the softmax runs in base 2 (v_exp_f32 is 2^x): fused-attention scores are kept in units
     // of log2(e) and the running max is converted back when the partial is written
     constexpr float kSU = SCORES ? 1.0f : 1.4426950408889634f;
-    query_operands(a.qrot, sq, a.scale * kSU, std::integral_constant<bool, K1>{});
-    if constexpr (QJL) query_operands(a.qsk, ssq, a.scale * a.qjl_c * kSU, std::false_type{});
+    if constexpr (merged) {
+      query_operands_m(a.qrot, sq, a.scale * kSU, std::integral_constant<bool, K1>{});
+      if constexpr (QJL) query_operands_m(a.qsk, ssq, a.scale * a.qjl_c * kSU, std::false_type{});
+    } else {
+      query_operands(a.qrot, sq, a.scale * kSU, std::integral_constant<bool, K1>{});
+      if constexpr (QJL) query_operands(a.qsk, ssq, a.scale * a.qjl_c * kSU, std::false_type{});
+    }
     __syncthreads();
   }
 
@@ -464,9 +520,11 @@ attn_kernel(AttnKArgs a) {
   // arrive before its first use. The two sets alternate by unrolling the walk by two; copying a
   // prefetch buffer instead would make the wave wait for every load in flight.
   if (start < end) {
-    // lanes of heads past the group's G read lane 63's operand, which is zero when G < 16:
-    // the reads of those lanes then share one address, which costs LDS almost nothing
-    uint32_t qoff = (uint32_t)(head_ok ? lane : 63) * 16u;
+    // lanes of heads past the group's G read lane 63's operand, which is zero when G < 16 (and,
+    // with merged columns, when G < 8): the reads of those lanes then share one address, which
+    // costs LDS almost nothing
+    const bool col_ok = merged ? (n16 & 7) < a.G : head_ok;
+    uint32_t qoff = (uint32_t)(col_ok ? lane : 63) * 16u;
     auto block = [&](int t0, const KBlk& cur, const VBlk& vb, const float (&nr)[NR], KBlk& kN, VBlk& vN,
                      float (&nN)[NR]) {
       // past the wave's range a dense fetch would read the next wave's rows: the last block
@@ -514,19 +572,31 @@ attn_kernel(AttnKArgs a) {
       f32x4 St[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       if constexpr (K1) {
         // codes 4kb .. 4kb+3 of the lane's chunk are bytes 2(kb%2), 2(kb%2)+1 of word kb/2
-#pragma unroll
-        for (int kb = 0; kb < KB1; ++kb) {
-          const u32x4 qh = *(const u32x4*)(qbase + kb * 1024);
-          const u32x4 ql = *(const u32x4*)(qbase + (KB1 + kb) * 1024);
+        auto key_operand = [&](int kb, int tile) -> u32x4 {
           const int sh = 16 * (kb & 1);
+          const uint32_t w = cur.kc[tile][kb >> 1];
+          const u32x2 p0 = *(const u32x2*)((const char*)tkh + 8u * ((w >> sh) & 0xffu));
+          const u32x2 p1 = *(const u32x2*)((const char*)tkh + 8u * ((w >> (sh + 8)) & 0xffu));
+          return u32x4{p0[0], p0[1], p1[0], p1[1]};
+        };
+        if constexpr (merged) {
 #pragma unroll
-          for (int tile = 0; tile < 2; ++tile) {
-            const uint32_t w = cur.kc[tile][kb >> 1];
-            const u32x2 p0 = *(const u32x2*)((const char*)tkh + 8u * ((w >> sh) & 0xffu));
-            const u32x2 p1 = *(const u32x2*)((const char*)tkh + 8u * ((w >> (sh + 8)) & 0xffu));
-            const u32x4 ak = {p0[0], p0[1], p1[0], p1[1]};
-            St[tile] = mfma16_bf16(ak, qh, St[tile]);
-            St[tile] = mfma16_bf16(ak, ql, St[tile]);
+          for (int kb = 0; kb < KB1; ++kb) {
+            const u32x4 q = *(const u32x4*)(qbase + kb * 1024);
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile) St[tile] = mfma16_bf16(key_operand(kb, tile), q, St[tile]);
+          }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < KB1; ++kb) {
+            const u32x4 qh = *(const u32x4*)(qbase + kb * 1024);
+            const u32x4 ql = *(const u32x4*)(qbase + (KB1 + kb) * 1024);
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile) {
+              const u32x4 ak = key_operand(kb, tile);
+              St[tile] = mfma16_bf16(ak, qh, St[tile]);
+              St[tile] = mfma16_bf16(ak, ql, St[tile]);
+            }
           }
         }
       }
@@ -544,10 +614,12 @@ attn_kernel(AttnKArgs a) {
               akl[c] = tkl[idx];
             }
             const u32x4 qh = *(const u32x4*)(qbase + kb * 1024);
-            const u32x4 ql = *(const u32x4*)(qbase + (KB + kb) * 1024);
             S = mfma16_bf16(akh, qh, S);
             S = mfma16_bf16(akl, qh, S);
-            S = mfma16_bf16(akh, ql, S);
+            if constexpr (!merged) {
+              const u32x4 ql = *(const u32x4*)(qbase + (KB + kb) * 1024);
+              S = mfma16_bf16(akh, ql, S);
+            }
           }
         }
         // QJL term: <S q, signs> with the signs as exact bf16 +-1 (bit 1 -> +1) against S q hi + lo
@@ -563,16 +635,25 @@ attn_kernel(AttnKArgs a) {
               as[c] = 0xBF80BF80u ^ ((w & 1u) << 15) ^ ((w & 2u) << 30);
             }
             const u32x4 sh = *(const u32x4*)(sbase + kb * 1024);
-            const u32x4 sl = *(const u32x4*)(sbase + (KB + kb) * 1024);
             S2 = mfma16_bf16(as, sh, S2);
-            S2 = mfma16_bf16(as, sl, S2);
+            if constexpr (!merged) {
+              const u32x4 sl = *(const u32x4*)(sbase + (KB + kb) * 1024);
+              S2 = mfma16_bf16(as, sl, S2);
+            }
           }
         }
         // D layout: lane (head n16, q4) register r = token t0 + 16*tile + 4*q4 + r = tok(4*tile + r)
+        float vt[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = S[r] * kn[4 * tile + r];
-          if constexpr (QJL) v = fmaf(S2[r], rn[4 * tile + r], v);
+          vt[r] = S[r] * kn[4 * tile + r];
+          if constexpr (QJL) vt[r] = fmaf(S2[r], rn[4 * tile + r], vt[r]);
+        }
+        // merged columns: the two halves of a head's (token-scaled) score, both rows of one token
+        if constexpr (merged) add_halves(vt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = vt[r];
           if constexpr (SCORES) {
             const int tt = t0 + 16 * tile + 4 * q4 + r;
             const bool ok = tt < end;
@@ -1198,14 +1279,14 @@ static void launch_merge_p(const tq_attn_params* p, const float* part, int s_eff
 // Resident waves per CU of the fused-attention kernel instance (registers and LDS as compiled),
 // from the runtime's occupancy calculator, once per (instance, device). The split count sizes the
 // grid to one round of them.
-template <int D, int BK, int BV, int PAGE, bool QJL>
+template <int D, int BK, int BV, int PAGE, bool QJL, bool MQ>
 static int attn_resident_waves_t(int device) {
   static std::mutex mu;
   static int cached[64] = {0};
   std::lock_guard<std::mutex> lk(mu);
   if (device >= 0 && device < 64 && cached[device]) return cached[device];
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, (const void*)attn_kernel<D, BK, BV, false, PAGE, QJL>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, (const void*)attn_kernel<D, BK, BV, false, PAGE, QJL, MQ>,
                                                    kAttnWaves * 64, 0) != hipSuccess ||
       blocks <= 0)
     blocks = attn_wpe(D, BK, BV, QJL, PAGE != kDense);   // the build's target: wpe waves per SIMD
@@ -1216,10 +1297,17 @@ static int attn_resident_waves_t(int device) {
 
 template <int D, int BK, int BV, bool QJL>
 static int attn_resident_p(const tq_attn_params* p, int device) {
-  if (!p->block_table) return attn_resident_waves_t<D, BK, BV, kDense, QJL>(device);
+  // query parts in the score MFMA's columns (MQ) when a KV head serves at most 8 query heads
+  if (p->num_q_heads <= 8 * p->num_kv_heads) {
+    if (!p->block_table) return attn_resident_waves_t<D, BK, BV, kDense, QJL, true>(device);
+    const int bs = p->block_size;
+    if (bs >= 16 && (bs & (bs - 1)) == 0) return attn_resident_waves_t<D, BK, BV, kPagedPow2, QJL, true>(device);
+    return attn_resident_waves_t<D, BK, BV, kPagedAny, QJL, true>(device);
+  }
+  if (!p->block_table) return attn_resident_waves_t<D, BK, BV, kDense, QJL, false>(device);
   const int bs = p->block_size;
-  if (bs >= 16 && (bs & (bs - 1)) == 0) return attn_resident_waves_t<D, BK, BV, kPagedPow2, QJL>(device);
-  return attn_resident_waves_t<D, BK, BV, kPagedAny, QJL>(device);
+  if (bs >= 16 && (bs & (bs - 1)) == 0) return attn_resident_waves_t<D, BK, BV, kPagedPow2, QJL, false>(device);
+  return attn_resident_waves_t<D, BK, BV, kPagedAny, QJL, false>(device);
 }
 
 template <int D, bool QJL>
@@ -1289,7 +1377,9 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   a.window = p->window;
   {
     const int64_t waves = (int64_t)lay.splits * kAttnWaves * p->num_kv_heads * B;
-    const int64_t resident = (int64_t)attn_resident_waves_t<D, BK, BV, PAGE, QJL>(rk.device) * device_cu_count(rk.device);
+    const int rw = a.G <= 8 ? attn_resident_waves_t<D, BK, BV, PAGE, QJL, true>(rk.device)
+                            : attn_resident_waves_t<D, BK, BV, PAGE, QJL, false>(rk.device);
+    const int64_t resident = (int64_t)rw * device_cu_count(rk.device);
     a.one_round = waves <= resident ? 1 : 0;
   }
   a.scale = p->scale;
@@ -1302,11 +1392,18 @@ static hipError_t launch_attn_p(const tq_attn_params* p, const Codebook& ck, con
   a.qsk = qsk;
   a.qjl_c = (float)(std::sqrt(M_PI / 2.0) / D);
   dim3 grid((unsigned)lay.splits, (unsigned)p->num_kv_heads, (unsigned)B);
+  auto launch = [&](auto sc) {
+    constexpr bool SC = decltype(sc)::value;
+    if (a.G <= 8)
+      hipLaunchKernelGGL((attn_kernel<D, BK, BV, SC, PAGE, QJL, true>), grid, dim3(kAttnWaves * 64), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<D, BK, BV, SC, PAGE, QJL, false>), grid, dim3(kAttnWaves * 64), 0, st, a);
+  };
   if (scores_only) {
-    hipLaunchKernelGGL((attn_kernel<D, BK, BV, true, PAGE, QJL>), grid, dim3(kAttnWaves * 64), 0, st, a);
+    launch(std::true_type{});
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((attn_kernel<D, BK, BV, false, PAGE, QJL>), grid, dim3(kAttnWaves * 64), 0, st, a);
+  launch(std::false_type{});
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int has_win = p->window > 0 ? 1 : 0;
   if (has_win) {
