@@ -66,10 +66,11 @@ struct EncGeo {
   static constexpr int SET_U4 = TS * KB * 64;      // one slice's tiles of one pass, u32x4 per lane
   static constexpr int FRAG_U4 = 2 * SET_U4;       // hi and lo tiles of the slice
   static constexpr bool LDS = (D <= 128) || QS > 1;
-  // Occupancy plan: at d <= 128, two 8-wave workgroups per CU (2 x 64 KiB of Pi tiles in LDS),
-  // i.e. 4 waves per SIMD within 128 VGPRs; d=256 needs up to 256 VGPRs, so one 8-wave
-  // workgroup (2 waves per SIMD), holding half of Pi's output rows (128 KiB) when split in two
-  // slices, else reading Pi from L2.
+  // Occupancy plan: at d <= 128, two workgroups per CU (2 x 64 KiB of Pi tiles in LDS): bf16
+  // inputs at d = 128 in 12-wave workgroups without an input prefetch (6 waves per SIMD within
+  // 80 VGPRs); d = 64, and float32 / fp16 inputs, which are split in registers, in 8-wave ones
+  // (4 per SIMD within 128; at d = 64 the prefetch measured 7% faster than more waves); d=256 needs up to 256 VGPRs, so one 8-wave workgroup (2 waves per SIMD), holding half of
+  // Pi's output rows (128 KiB) when split in two slices, else reading Pi from L2.
   static constexpr int WG_PER_CU = D == 256 ? 1 : 2;
 };
 // Byte B of `word` = (byte 3 of lo) | (byte 3 of hi) << 4; for B > 0 the other bytes are kept,
@@ -119,10 +120,13 @@ __device__ __forceinline__ uint32_t byte3_shr(uint32_t w) {
   return r;
 }
 
+// bf16 inputs at d = 128 take more waves instead of a prefetch (see the occupancy plan)
 template <int D, int IN>
-constexpr int enc_waves() { return 8; }
+constexpr bool enc_many_waves() { return D == 128 && IN == TQ_BF16; }
 template <int D, int IN>
-constexpr int enc_wpe() { return D == 256 ? 2 : 4; }
+constexpr int enc_waves() { return enc_many_waves<D, IN>() ? 12 : 8; }
+template <int D, int IN>
+constexpr int enc_wpe() { return D == 256 ? 2 : (enc_many_waves<D, IN>() ? 6 : 4); }
 
 // QS > 1 (d = 256): QS workgroups share each group of vectors, each computing the output tiles of
 // one slice of the coordinates with that slice's rows of Pi in LDS (the dense Pi, 256 KiB as hi +
@@ -158,15 +162,17 @@ encode_kernel(EncodeKArgs a) {
   const int vl = lane & 31, hh = lane >> 5;
 
   // Raw inputs of one tile: lane (v, hh) reads elements 16kb + 8hh .. +7 with 16-byte loads.
-  // bf16 inputs are the MFMA B operands as loaded and are prefetched one tile ahead, so every
-  // wave keeps a tile of loads in flight while it rotates and quantizes the previous one.
+  // bf16 inputs are the MFMA B operands as loaded. At d = 64 and 256 they are prefetched one
+  // tile ahead, so every wave keeps a tile of loads in flight while it rotates and quantizes the
+  // previous one; at d = 128 the 32 registers of a prefetch buy more: without it a SIMD holds
+  // 6 waves instead of 4, which hides the load latency better (measured ~8% faster).
   // Every load and store is issued unconditionally (masked lanes read row v_begin and write
   // the sink): the memory counter is in order, and a branch around an access would make the
   // wait for a prefetched load also wait for the stores issued after it.
   constexpr int ELEM = IN == TQ_F32 ? 4 : 2;
   constexpr int NRAW = HALF * ELEM / 16;
   constexpr int PER = ELEM / 2;          // 16-byte loads per K block
-  constexpr bool PREFETCH = (IN == TQ_BF16);
+  constexpr bool PREFETCH = IN == TQ_BF16 && !enc_many_waves<D, IN>();
   const int64_t wstride = (int64_t)nslots * WAVES;
   // loads tile tl's inputs and returns the packed row its codes go to (-1: none)
   auto fetch = [&](int64_t tl, u32x4 (&raw)[NRAW]) -> int64_t {
@@ -222,6 +228,10 @@ encode_kernel(EncodeKArgs a) {
       rown = fetch(tile + wstride, xr);   // past the end this reads row v_begin, unused
     } else {
       row = fetch(tile, xr);
+      if constexpr (IN == TQ_BF16) {
+#pragma unroll
+        for (int k = 0; k < NRAW; ++k) xh[k] = xr[k];
+      }
     }
 
     // ---- norm, and the MFMA B operands (bf16 hi, and lo for split inputs)
