@@ -9,7 +9,7 @@
 // consecutive output coordinates of one vector in a lane's accumulator (tile t, half hh:
 // coordinates 32t + 16hh .. +16 of the slice), which are scaled by n, staged in LDS and stored
 // 128 bytes of each of the wave's 32 rows at a time (a full cache line per row), 1 KiB per
-// store instruction. With that small staging area a CU holds 12 waves at d = 128.
+// store instruction. With that small staging area a CU holds 12 or 16 waves at d = 128.
 //
 // Precision. A 16-bit output is the float64 decode rounded to nearest even, so the kernel's
 // unrounded value must sit well inside a 16-bit half-ulp of the float64 one; single fp16
@@ -93,12 +93,13 @@ struct DecGeo {
   // the lo table starts LO_OFF bytes after the hi one: further apart than one two-address LDS
   // read reaches and not a multiple of its stride, so each word is read into its own register
   static constexpr int LO_OFF = (TAB_B > 2048 ? TAB_B : 2048) + 8;
-  // Launch shape: d = 64 in two 4-wave workgroups per CU, d = 128 in one 12-wave workgroup
-  // (3 waves per SIMD within 170 registers; the tile sets take 64 KiB of LDS), d = 256 in one
-  // 16-wave workgroup per CU: with two tiles per slice it looks its operands up one K block at a
-  // time (KB_OUTER), which keeps it within 128 registers.
+  // Launch shape: d = 64 in two 4-wave workgroups per CU; d = 128 in one workgroup per CU (the
+  // tile sets take 64 KiB of LDS) of 16 waves with the single-operand centroid table (4 per SIMD
+  // within 128 registers: 5% faster than 12) and of 12 with the hi/lo one (3 per SIMD within
+  // 170); d = 256 in one 16-wave workgroup per CU: with two tiles per slice it looks its operands
+  // up one K block at a time (KB_OUTER), which keeps it within 128 registers.
   static constexpr bool KB_OUTER = D == 256;
-  static constexpr int WAVES = D == 64 ? 4 : (D == 128 ? 12 : 16);
+  static constexpr int WAVES = D == 64 ? 4 : (D == 128 ? (decode_one_operand(BITS, OUT) ? 16 : 12) : 16);
   static constexpr int WG_PER_CU = D == 64 ? 2 : 1;
   static constexpr int WPE = WAVES * WG_PER_CU / 4;   // waves per SIMD
   static constexpr int SB = SC * E;                    // output bytes of a row in this slice
