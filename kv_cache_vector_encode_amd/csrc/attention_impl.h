@@ -679,11 +679,13 @@ attn_kernel(AttnKArgs a) {
         //      in the norms): until then the weights stay below 2^12 in fp16 and a block needs no
         //      cross-lane reduction and no rescale. 1/N rides in the exponent: p_t / N =
         //      2^(s_t - m_e) with m_e = m + log2 N, and l gains N * sum 2^(s_t - m_e).
+        // NaN-propagating maxima (v_maximum3_f32): fmaxf would first quiet every input that the
+        // compiler cannot prove canonical (loaded norms, asm results), one instruction each
         float mb = s[0], nb = vn[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) {
-          mb = fmaxf(mb, s[e]);
-          nb = fmaxf(nb, vn[e]);
+          mb = __builtin_elementwise_maximum(mb, s[e]);
+          nb = __builtin_elementwise_maximum(nb, vn[e]);
         }
         if (__any(mb > m_run + 8.0f || nb > 16.0f * n_run)) {
           mb = fmaxf(mb, wave_xor(mb, 16));
