@@ -218,7 +218,7 @@ attn_kernel(AttnKArgs a) {
   //     bf16 hi | lo << 16, and the score MFMA's K dimension runs over (coordinate, hi / lo)
   //     with the query duplicated, so one product takes (c_hi + c_lo) q_hi and a second one
   //     (c_hi + c_lo) q_lo;
-  //   2/3-bit keys: a pair of codes (at most 64 entries) -> two bf16 hi (tkh) / lo (tkl)
+  //   2/3-bit keys: a pair of codes (at most 64 entries) -> two bf16 hi / lo (both in tkh)
   //     halves, three products per K block (c_hi q_hi + c_lo q_hi + c_hi q_lo);
   //   values: a pair of V codes (one coordinate of two tokens) -> one fp16 pair; 2-bit codes
   //     are first interleaved so that each nibble is such a pair (16 entries).
@@ -226,7 +226,12 @@ attn_kernel(AttnKArgs a) {
   constexpr int KB1 = D / 16;           // score MFMAs per pass with one code per operand word
   constexpr int KTAB = K1 ? 512 : 1 << PK;
   constexpr int VTAB = 1 << (2 * BV);
-  __shared__ uint32_t tkh[KTAB], tkl[K1 ? 1 : KTAB];
+  // 2/3-bit keys: the lo halves start KLO bytes after the hi halves, further apart than one
+  // two-address LDS read reaches and not a multiple of its 256-byte stride, so the compiler
+  // cannot merge a pair's two reads into one two-register read that would then need moves:
+  // each word goes straight into its MFMA operand register
+  constexpr int KLO = K1 ? 0 : (4 * KTAB > 1024 ? 4 * KTAB : 1024) + 8;
+  __shared__ __attribute__((aligned(16))) uint32_t tkh[K1 ? KTAB : (KLO + 4 * KTAB) / 4];
   __shared__ uint32_t tv[SCORES ? 1 : VTAB];
   constexpr int NQB = K1 ? KB1 : KB;    // query operand words per pass and lane
   __shared__ u32x4 sq[2 * NQB * 64];   // query B operands [hi, lo][kb][lane], shared by the waves
@@ -494,7 +499,7 @@ attn_kernel(AttnKArgs a) {
         } else {
           const uint32_t c0 = kk[j & MK], c1 = kk[j >> BK];
           tkh[j] = (c0 & 0xffffu) | (c1 << 16);
-          tkl[j] = (c0 >> 16) | (c1 & 0xffff0000u);
+          tkh[KLO / 4 + j] = (c0 >> 16) | (c1 & 0xffff0000u);
         }
       }
       if constexpr (!SCORES) {
@@ -609,9 +614,16 @@ attn_kernel(AttnKArgs a) {
             u32x4 akh, akl;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const uint32_t idx = bits_at<PK>(cur.kc[tile], (4 * kb + c) * PK);
-              akh[c] = tkh[idx];
-              akl[c] = tkl[idx];
+              // byte offset of the code pair's entry: its PK bits shifted to bit 2, one mask
+              const int pos = (4 * kb + c) * PK, sb = pos & 31;
+              const uint32_t* w = cur.kc[tile];
+              uint32_t off;
+              if (sb + PK <= 32)
+                off = (sb >= 2 ? (w[pos >> 5] >> (sb - 2)) : (w[pos >> 5] << (2 - sb))) & (((1u << PK) - 1u) << 2);
+              else
+                off = funnel(w[(pos >> 5) + 1], w[pos >> 5], sb - 2) & (((1u << PK) - 1u) << 2);
+              akh[c] = lds_word(tkh, off);
+              akl[c] = lds_word(tkh, off + KLO);
             }
             const u32x4 qh = *(const u32x4*)(qbase + kb * 1024);
             S = mfma16_bf16(akh, qh, S);

@@ -212,7 +212,9 @@ decode_kernel(DecodeKArgs a) {
     }
   };
 
-  int64_t tile = (int64_t)slot_id * WAVES + wave;
+  // tiles go to waves wave-major (as in the encode): an uneven last round is spread over every
+  // workgroup instead of falling to a subset of them
+  int64_t tile = (int64_t)wave * nslots + slot_id;
   uint32_t cwA[DW], cwB[DW];
   float nA, nB;
   int64_t sA = slot_row(tile), sB = 0;

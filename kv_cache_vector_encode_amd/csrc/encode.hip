@@ -23,13 +23,14 @@
 // Quantization: one FMA maps the unnormalized Pi x to f = y * s + o in [1, 2) (y = Pi x /
 // (n + 1e-8), the per-vector factor s / (n + 1e-8) computed once), and a 128-bin LDS table
 // indexed by the top 7 fraction bits of f, whose bins each hold at most one decision boundary,
-// gives the code base + (f > boundary) = #{k : t_k < y} as byte 3 of bits(f) - entry: all f
-// share one exponent, so the compare is an integer subtraction whose carry into bit 24 adds to
-// the base stored above it. Byte 2 of bits(f) is the exponent's low bit and those 7 fraction
-// bits, so one byte-select shift (SDWA) makes the table address, and another shifts the code
-// (byte 3) to its place in the packed word: with the or that merges it, ~4.5 VALU instructions
-// per coordinate (fma, shift, subtract, shift, half of a three-input or) where a compare chain
-// over the 2^b - 1 boundaries costs 15-20.
+// gives the code base + (f > boundary) = #{k : t_k < y} as the top bits of bits(f) - entry:
+// all f share one exponent, so the compare is an integer subtraction whose carry adds to the
+// base stored above it. Byte 2 of bits(f) is the exponent's low bit and those 7 fraction bits,
+// so one byte-select shift (SDWA) makes the table address. 2- and 3-bit codes sit in the top b
+// bits and one funnel shift appends each to the packed word (4 VALU instructions per
+// coordinate: fma, shift, subtract, funnel shift); 4-bit codes sit in byte 3 and a pair goes
+// into its byte with two byte-select instructions. A compare chain over the 2^b - 1 boundaries
+// costs 15-20.
 #include "device_common.h"
 #include "tq_internal.h"
 
@@ -104,22 +105,6 @@ __device__ __forceinline__ uint32_t lut_addr(uint32_t f) {
       : "=v"(r) : "v"(f));
   return r;
 }
-// (byte 3 of w) << S and (byte 3 of w) >> S, one SDWA instruction each
-template <int S>
-__device__ __forceinline__ uint32_t byte3_shl(uint32_t w) {
-  uint32_t r;
-  asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
-      : "=v"(r) : "I"(S), "v"(w));
-  return r;
-}
-template <int S>
-__device__ __forceinline__ uint32_t byte3_shr(uint32_t w) {
-  uint32_t r;
-  asm("v_lshrrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
-      : "=v"(r) : "I"(S), "v"(w));
-  return r;
-}
-
 // bf16 inputs at d = 128 take more waves instead of a prefetch (see the occupancy plan)
 template <int D, int IN>
 constexpr bool enc_many_waves() { return D == 128 && IN == TQ_BF16; }
@@ -189,7 +174,10 @@ encode_kernel(EncodeKArgs a) {
       return ok ? v : -1;
     }
   };
-  int64_t tile = (int64_t)slot_id * WAVES + wave;
+  // Tiles go to waves wave-major (tile = wave * nslots + slot, then every wstride): when the
+  // tiles do not divide evenly, the waves with one more are the low-numbered waves of every
+  // workgroup, so the last round keeps every CU and SIMD busy rather than a subset of workgroups
+  int64_t tile = (int64_t)wave * nslots + slot_id;
   u32x4 xr[NRAW];
   int64_t rown = -1;
   // the first tile's loads are issued before the table copies below, so the two latencies overlap
@@ -290,10 +278,18 @@ encode_kernel(EncodeKArgs a) {
 #pragma unroll
     for (int w = 0; w < Geo::CHUNK_DW; ++w) pk[w] = 0u;
     uint32_t wprev = 0u;
+    // 2- and 3-bit codes (table entries with the code in the top BITS bits): the lane's codes are
+    // taken from its last coordinate down to its first and each is appended to `chain` by one
+    // funnel shift, chain = (chain << BITS) | code; after code j, chain holds stream bits
+    // [BITS*j, BITS*j + 32). A word whose first bit is code j's first bit is the chain itself; a
+    // word that begins inside code j is (chain << r) | (the top r bits of code j) taken before
+    // code j goes in (r = the code's bits in that word): one more funnel shift.
+    constexpr bool CHAIN = BITS < 4;
+    uint32_t chain = 0u;
     // tile t and coordinate i as compile-time constants: the packing's shift counts are
     // instruction immediates
     static_for<0, T>([&](auto tc) {
-      constexpr int t = decltype(tc)::value;
+      constexpr int t = CHAIN ? T - 1 - decltype(tc)::value : decltype(tc)::value;
       // a fresh opaque offset per tile: the scheduler cannot pull later tiles' Pi reads ahead
       // (all 4 tiles' operands at once would not fit in registers)
       asm volatile("" : "+v"(aoff));
@@ -309,11 +305,19 @@ encode_kernel(EncodeKArgs a) {
         if constexpr (SPLIT_X) acc = mfma32_bf16(ahi, xl[kb], acc);
       }
       static_for<0, 16>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
+        constexpr int i = CHAIN ? 15 - decltype(ic)::value : decltype(ic)::value;
         const uint32_t fb = __float_as_uint(fmaf(acc[i], fs, foff));
-        const uint32_t w = fb - *(const uint32_t*)((const char*)lut + lut_addr(fb));   // code: byte 3
+        // code: byte 3 (4 bits), the top BITS bits (2 and 3 bits)
+        const uint32_t w = fb - *(const uint32_t*)((const char*)lut + lut_addr(fb));
         constexpr int pos = (16 * t + i) * BITS;
-        if constexpr (BITS == 4) {
+        if constexpr (CHAIN) {
+          if constexpr ((pos & 31) + BITS > 32) {
+            constexpr int r = (pos & 31) + BITS - 32;
+            pk[(pos >> 5) + 1] = __builtin_amdgcn_alignbit(chain, w, 32 - r);
+          }
+          chain = __builtin_amdgcn_alignbit(chain, w, 32 - BITS);
+          if constexpr ((pos & 31) == 0) pk[pos >> 5] = chain;
+        } else if constexpr (BITS == 4) {
           // two codes per byte: byte 3 of the odd coordinate's w goes to the high nibble and the
           // even one's to the low nibble, written straight into byte (i % 8) / 2 of the word
           if (i & 1) {
@@ -326,18 +330,16 @@ encode_kernel(EncodeKArgs a) {
             }
           }
           wprev = w;
-        } else {
-          pk[pos >> 5] |= byte3_shl<(pos & 31)>(w);
-          if constexpr ((pos & 31) + BITS > 32) pk[(pos >> 5) + 1] |= byte3_shr<32 - (pos & 31)>(w);
         }
         // table reads in groups of 8: all 16 in flight at once would not fit in registers
-        if constexpr ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        if constexpr ((decltype(ic)::value & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       });
       // finish this tile's packed words here: left alone, the compiler sinks the packing to the
       // store and keeps every table entry of the vector live until then
 #pragma unroll
       for (int w = (16 * t * BITS) >> 5; w <= ((16 * t + 16) * BITS - 1) >> 5; ++w)
         asm volatile("" : "+v"(pk[w]));
+      if constexpr (CHAIN) asm volatile("" : "+v"(chain));
     });
 
     // ---- norm correction (Turbo Attention page, "The codec", Norms row: the decoded key keeps
@@ -403,7 +405,8 @@ static hipError_t launch_encode_t(const EncodeLaunch& L) {
   k.lut_off = L.lv.lut.offset;
   k.norm_correct = L.norm_correct ? 1 : 0;
   for (int j = 0; j < kMaxLevels; ++j) k.csq[j] = L.lv.centroid_sq[j];
-  for (int j = 0; j < kLutBins; ++j) k.lut[j] = L.lv.lut.entry[j];
+  // 2- and 3-bit codes are packed by funnel shifts from the top bits of the difference
+  for (int j = 0; j < kLutBins; ++j) k.lut[j] = BITS < 4 ? L.lv.lut.entry_top[j] : L.lv.lut.entry[j];
   const int64_t per_rot = L.vectors_per_rot ? L.vectors_per_rot : L.n;
   const int nrot = L.vectors_per_rot ? (int)((L.n + L.vectors_per_rot - 1) / L.vectors_per_rot) : 1;
   const int64_t tiles = (per_rot + 31) / 32;

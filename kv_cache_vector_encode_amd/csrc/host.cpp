@@ -300,15 +300,19 @@ LevelArgs make_levels(const Codebook& cb) {
       }
     }
     if (nb > 1) lv.lut.ok = false;
-    uint32_t e;
+    const int top = 32 - cb.bits;   // carry position of entry_top (bits <= 8, so top >= 24)
+    uint32_t e, et;
     if (nb) {
       std::memcpy(&e, &thr, 4);
+      et = e + 1u - (1u << top) - (base << top);
       e = e + 1u - (1u << 24) - (base << 24);
     } else {
       std::memcpy(&e, &lo, 4);
+      et = e - (base << top);
       e -= base << 24;
     }
     lv.lut.entry[j] = e;
+    lv.lut.entry_top[j] = et;
   }
   return lv;
 }

@@ -128,7 +128,9 @@ qjl_encode_kernel(QjlKArgs a) {
       return ok ? v : -1;
     }
   };
-  int64_t tile = (int64_t)blockIdx.x * WAVES + wave;
+  // tiles go to waves wave-major (as in the encode): an uneven last round is spread over every
+  // workgroup instead of falling to a subset of them
+  int64_t tile = (int64_t)wave * gridDim.x + blockIdx.x;
   u32x4 xr[NRAW];
   int64_t rown = -1;
   if (PREFETCH) {

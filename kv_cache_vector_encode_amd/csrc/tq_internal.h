@@ -80,11 +80,16 @@ struct Qjl {
 // (all f of the binade share one exponent, so their bit patterns differ by less than 2^23). The
 // boundary is kept exactly as a float. Kernels hold the entries at LDS word 128 + j (byte 2 of
 // bits(f) times 4), with a second copy below for inputs that are not finite.
+// entry_top is the same table with the carry moved from bit 24 to bit 32 - b (2^24 and base << 24
+// become 2^(32-b) and base << (32-b)): the code is then the top b bits of bits(f) - e, which a
+// funnel shift appends to a packed word in one instruction. The f's of one binade differ by less
+// than 2^23 < 2^(32-b), so the carry analysis is unchanged.
 constexpr int kLutBins = 128;
 struct QuantLut {
   float scale, offset;
   bool ok;                  // every bin holds at most one boundary
   uint32_t entry[kLutBins];
+  uint32_t entry_top[kLutBins];
 };
 
 // Levels passed to kernels by value.
