@@ -374,15 +374,15 @@ encode_kernel(EncodeKArgs a) {
       if constexpr (Geo::G == 16) {
 #pragma unroll
         for (int w = 0; w < Geo::CHUNK_DW; w += 4)
-          *(u32x4*)(dst + 4 * w) = u32x4{pk[w], pk[w + 1], pk[w + 2], pk[w + 3]};
+          __builtin_nontemporal_store(u32x4{pk[w], pk[w + 1], pk[w + 2], pk[w + 3]}, (u32x4*)(dst + 4 * w));
       } else if constexpr (Geo::G == 8) {
 #pragma unroll
-        for (int w = 0; w < Geo::CHUNK_DW; w += 2) *(u32x2*)(dst + 4 * w) = u32x2{pk[w], pk[w + 1]};
+        for (int w = 0; w < Geo::CHUNK_DW; w += 2) __builtin_nontemporal_store(u32x2{pk[w], pk[w + 1]}, (u32x2*)(dst + 4 * w));
       } else {
 #pragma unroll
-        for (int w = 0; w < Geo::CHUNK_DW; ++w) *(uint32_t*)(dst + 4 * w) = pk[w];
+        for (int w = 0; w < Geo::CHUNK_DW; ++w) __builtin_nontemporal_store(pk[w], (uint32_t*)(dst + 4 * w));
       }
-      *np = nst;
+      __builtin_nontemporal_store(nst, np);
     }
   }
 }
