@@ -650,6 +650,30 @@ def copy_probe(torch, dev):
     torch.cuda.empty_cache()
 
 
+def copy_bandwidth(torch, dev, reps: int = 10):
+    """Measured HBM rate of a plain 1 GiB device-to-device copy (read + write bytes per copy /
+    median event time): what streaming reaches on this machine, beside the 8 TB/s peak."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    ms = sorted(ts)[len(ts) // 2]
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    return {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "ms": round(ms, 4),
+            "note": "1 GiB device-to-device copy, read + write bytes, median of %d" % reps}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -683,6 +707,8 @@ def main():
         extra["paged_ragged"] = paged_ragged(tq, ti, torch, dev)
         show("paged_ragged", extra["paged_ragged"])
         extra["codec_check_4096"] = codec_check_latency(tq, ti, torch, dev)
+        extra["hbm_copy"] = copy_bandwidth(torch, dev)
+        show("hbm_copy", extra["hbm_copy"])
         if nxt is not None:
             nxt["hadamard_fast_transform"] = hadamard_fast_transform(tq, ti, torch, dev)
             show("hadamard_fast_transform", nxt["hadamard_fast_transform"])
