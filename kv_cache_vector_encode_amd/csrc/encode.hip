@@ -366,7 +366,16 @@ encode_kernel(EncodeKArgs a) {
       }
     }
 
-    // ---- store
+    // ---- store: dense rows non-temporally (a wave's 32 rows are one contiguous run); slot-mapped
+    //      rows with ordinary stores: a paged pool puts the KV heads of one token in different
+    //      pages, so each row stands alone in its cache line until the cache combines it with
+    //      the neighbouring tokens' rows
+    auto put = [&](auto v, auto* p) {
+      if constexpr (SLOT)
+        *p = v;
+      else
+        __builtin_nontemporal_store(v, p);
+    };
     {
       const bool ok = row >= 0;
       uint8_t* dst = ok ? a.packed + row * Geo::ROW + hh * Geo::CHUNK + q * Geo::CHUNK_S : a.sink + 64 * lane;
@@ -374,15 +383,15 @@ encode_kernel(EncodeKArgs a) {
       if constexpr (Geo::G == 16) {
 #pragma unroll
         for (int w = 0; w < Geo::CHUNK_DW; w += 4)
-          __builtin_nontemporal_store(u32x4{pk[w], pk[w + 1], pk[w + 2], pk[w + 3]}, (u32x4*)(dst + 4 * w));
+          put(u32x4{pk[w], pk[w + 1], pk[w + 2], pk[w + 3]}, (u32x4*)(dst + 4 * w));
       } else if constexpr (Geo::G == 8) {
 #pragma unroll
-        for (int w = 0; w < Geo::CHUNK_DW; w += 2) __builtin_nontemporal_store(u32x2{pk[w], pk[w + 1]}, (u32x2*)(dst + 4 * w));
+        for (int w = 0; w < Geo::CHUNK_DW; w += 2) put(u32x2{pk[w], pk[w + 1]}, (u32x2*)(dst + 4 * w));
       } else {
 #pragma unroll
-        for (int w = 0; w < Geo::CHUNK_DW; ++w) __builtin_nontemporal_store(pk[w], (uint32_t*)(dst + 4 * w));
+        for (int w = 0; w < Geo::CHUNK_DW; ++w) put(pk[w], (uint32_t*)(dst + 4 * w));
       }
-      __builtin_nontemporal_store(nst, np);
+      put(nst, np);
     }
   }
 }
