@@ -366,12 +366,13 @@ encode_kernel(EncodeKArgs a) {
       }
     }
 
-    // ---- store: dense rows non-temporally (a wave's 32 rows are one contiguous run); slot-mapped
-    //      rows with ordinary stores: a paged pool puts the KV heads of one token in different
-    //      pages, so each row stands alone in its cache line until the cache combines it with
-    //      the neighbouring tokens' rows
+    // ---- store: dense rows of one slice non-temporally (a wave's 32 rows are one contiguous
+    //      run); slot-mapped rows, and the half rows of the d = 256 slices, with ordinary stores:
+    //      a paged pool puts the KV heads of one token in different pages, and a slice writes
+    //      every other half row, so those pieces stand alone in their cache lines until the
+    //      cache combines them with their neighbours
     auto put = [&](auto v, auto* p) {
-      if constexpr (SLOT)
+      if constexpr (SLOT || QS > 1)
         *p = v;
       else
         __builtin_nontemporal_store(v, p);
